@@ -1,0 +1,84 @@
+"""Seeded synthetic inputs for the five workloads (shapes and distributions
+only; none of the quantization method's arithmetic lives here). Shared by the
+tests, the smoke check and the benchmark, and by both the GPU path and the
+oracle: every generator is deterministic for a given (seed, device).
+
+Workloads (LLM-shaped, synthetic; no dataset or trained weights are used):
+  worked_example  4096 fp32 values ~N(0,1), every 512th multiplied by 20
+                  (the glossary page's "Como funciona FP4" example).
+  w4a4_linear     weight [4096, 4096] ~N(0, 0.02) as [out, in]; activations
+                  [2048, 4096] ~N(0, 1) with 1% of the columns (41) x30
+                  (outlier channels); bf16.
+  moe_mxfp4       32 experts: weight [2880, 5760] ~N(0, 0.02) per expert as
+                  [K, N] (quantized transposed); tokens [512, 2880] ~N(0, 1)
+                  per expert; bf16.
+  training        weight [8192, 8192] ~N(0, 0.02); gradient [8192, 8192]
+                  ~Laplace(0, 1e-3) by inverse CDF of a uniform; bf16.
+  rht_activation  activations [16384, 4096] ~N(0, 1) with 0.5% of entries
+                  replaced by Student-t (df = 2) draws; random 16-bit sign
+                  mask; weight [4096, 12288] ~N(0, 0.02) as [K, N]; bf16.
+Every size is a parameter so the tests can draw smaller instances from the
+same recipe.
+"""
+from __future__ import annotations
+
+import torch
+
+
+def _gen(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def worked_example(seed: int = 0) -> torch.Tensor:
+    g = _gen(seed, "cpu")
+    x = torch.randn(4096, generator=g)
+    x[::512] *= 20
+    return x
+
+
+def w4a4_linear(m: int = 2048, n: int = 4096, k: int = 4096, seed: int = 2, device="cpu") -> dict:
+    g = _gen(seed, device)
+    w = (0.02 * torch.randn(n, k, generator=g, device=device)).to(torch.bfloat16)
+    a = torch.randn(m, k, generator=g, device=device)
+    n_out = max(1, round(0.01 * k))
+    cols = torch.randperm(k, generator=g, device=device)[:n_out]
+    a[:, cols] *= 30
+    return {"w": w, "a": a.to(torch.bfloat16), "outlier_cols": cols}
+
+
+def moe_mxfp4(experts: int = 32, tokens: int = 512, k: int = 2880, n: int = 5760, seed: int = 3, device="cpu") -> dict:
+    g = _gen(seed, device)
+    w = torch.empty(experts, k, n, dtype=torch.bfloat16, device=device)
+    for e in range(experts):  # per expert, to bound fp32 temporaries
+        w[e] = (0.02 * torch.randn(k, n, generator=g, device=device)).to(torch.bfloat16)
+    x = torch.randn(experts, tokens, k, generator=g, device=device).to(torch.bfloat16)
+    return {"w": w, "x": x}
+
+
+def training(n: int = 8192, seed: int = 4, device="cpu") -> dict:
+    g = _gen(seed, device)
+    w = (0.02 * torch.randn(n, n, generator=g, device=device)).to(torch.bfloat16)
+    u = torch.rand(n, n, generator=g, device=device) - 0.5
+    grad = -1e-3 * torch.sign(u) * torch.log1p(-2.0 * u.abs())
+    return {"w": w, "grad": grad.to(torch.bfloat16), "sr_seed": seed, "sr_offset": 0}
+
+
+def rht_activation(m: int = 16384, k: int = 4096, n: int = 12288, seed: int = 5, device="cpu") -> dict:
+    g = _gen(seed, device)
+    x = torch.randn(m, k, generator=g, device=device)
+    mask = torch.rand(m, k, generator=g, device=device) < 0.005
+    z = torch.randn(m, k, generator=g, device=device)
+    u = torch.rand(m, k, generator=g, device=device).clamp_min(1e-12)
+    t2 = z / torch.sqrt(-torch.log(u))  # Student-t with 2 degrees of freedom
+    x = torch.where(mask, t2, x)
+    bits = torch.randint(0, 2, (16,), generator=g, device=device).cpu()
+    signs = int(sum(int(b) << i for i, b in enumerate(bits.tolist())))
+    w = (0.02 * torch.randn(k, n, generator=g, device=device)).to(torch.bfloat16)
+    return {"x": x.to(torch.bfloat16), "w": w, "signs": signs}
+
+
+def bf16_bits(t: torch.Tensor):
+    """numpy uint16 view of a bf16 CPU tensor (the oracle's bf16 input form)."""
+    return t.contiguous().cpu().view(torch.int16).numpy().view("uint16")
