@@ -1,0 +1,271 @@
+// fp4_api.cpp -- the C ABI declared in include/fp4.h: host-side argument
+// validation (no HIP call happens before it passes), the gfx950 device check,
+// and dispatch to the kernels.
+#include "fp4.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "launch.h"
+
+using namespace fp4impl;
+
+namespace {
+
+constexpr uint32_t kKnownFlags = FP4_FOUR_OVER_SIX | FP4_BLOCK2D | FP4_TRANSPOSE | FP4_STOCHASTIC | FP4_HADAMARD;
+constexpr int64_t kMaxGridYZ = 65535;
+constexpr int64_t kMaxGridX = 2147483647;
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+// Per-device cache of "is gfx950": 0 unknown, 1 yes, 2 no.
+std::atomic<int> g_device_ok[64];
+
+fp4_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return FP4_ERR_DEVICE;
+  }
+  if (dev < 64) {
+    int c = g_device_ok[dev].load(std::memory_order_relaxed);
+    if (c == 1) return FP4_OK;
+    if (c == 2) return FP4_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return FP4_ERR_DEVICE;
+  }
+  bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) g_device_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? FP4_OK : FP4_ERR_DEVICE;
+}
+
+struct QuantPlan {
+  int64_t R = 0, C = 0;
+  int blk = 0;
+  int nparts = 0;
+  size_t ws = 0;
+};
+
+// Validation shared by fp4_quantize_workspace and fp4_quantize that only
+// depends on sizes and options.
+fp4_status plan_quantize(int64_t batch, int64_t rows, int64_t cols, const fp4_quant_opts* o, QuantPlan* p) {
+  if (!o || o->size != sizeof(fp4_quant_opts)) return FP4_ERR_INVALID;
+  if (o->format != FP4_MXFP4 && o->format != FP4_NVFP4) return FP4_ERR_INVALID;
+  if (o->flags & ~kKnownFlags) return FP4_ERR_INVALID;
+  if (batch < 0 || rows < 0 || cols < 0) return FP4_ERR_INVALID;
+  const bool nv = o->format == FP4_NVFP4;
+  if (!nv && (o->flags & (FP4_FOUR_OVER_SIX | FP4_BLOCK2D))) return FP4_ERR_UNSUPPORTED;
+  if ((o->flags & FP4_BLOCK2D) && (o->flags & FP4_HADAMARD) && (o->flags & FP4_TRANSPOSE)) return FP4_ERR_UNSUPPORTED;
+  const bool tr = o->flags & FP4_TRANSPOSE;
+  p->blk = nv ? 16 : 32;
+  p->R = tr ? cols : rows;
+  p->C = tr ? rows : cols;
+  if (p->C % p->blk != 0) return FP4_ERR_INVALID;
+  if (tr && (p->R % 8 != 0)) return FP4_ERR_INVALID;
+  if ((o->flags & FP4_BLOCK2D) && (p->R % 16 != 0)) return FP4_ERR_INVALID;
+  if (batch > kMaxGridYZ) return FP4_ERR_UNSUPPORTED;
+  if (tr) {
+    if ((rows + 127) / 128 > kMaxGridYZ || (cols + 255) / 256 > kMaxGridX) return FP4_ERR_UNSUPPORTED;
+  } else if (o->flags & FP4_BLOCK2D) {
+    if (p->R / 16 > kMaxGridYZ || ((p->C / 16) + 15) / 16 > kMaxGridX) return FP4_ERR_UNSUPPORTED;
+  } else {
+    if (p->R > 0 && ((p->R * (p->C / 16)) + 255) / 256 > kMaxGridX) return FP4_ERR_UNSUPPORTED;
+  }
+  if (nv && !o->amax_in && batch > 0 && rows > 0 && cols > 0) {
+    p->nparts = amax_partials(rows, cols, o->flags);
+    p->ws = (size_t)batch * (size_t)p->nparts * sizeof(float);
+  }
+  return FP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fp4_status_str(int32_t s) {
+  switch (s) {
+    case FP4_OK: return "FP4_OK";
+    case FP4_ERR_INVALID: return "FP4_ERR_INVALID: invalid argument";
+    case FP4_ERR_UNSUPPORTED: return "FP4_ERR_UNSUPPORTED: unsupported option or shape combination";
+    case FP4_ERR_ALIGN: return "FP4_ERR_ALIGN: misaligned pointer or stride";
+    case FP4_ERR_DEVICE: return "FP4_ERR_DEVICE: current HIP device is not gfx950";
+    case FP4_ERR_WORKSPACE: return "FP4_ERR_WORKSPACE: workspace missing or too small";
+    case FP4_ERR_HIP: return "FP4_ERR_HIP: HIP runtime error";
+    default: return "unknown fp4 status";
+  }
+}
+
+size_t fp4_quantize_workspace(int64_t batch, int64_t rows, int64_t cols, const fp4_quant_opts* opts) {
+  QuantPlan p;
+  if (plan_quantize(batch, rows, cols, opts, &p) != FP4_OK) return 0;
+  return p.ws;
+}
+
+fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t batch, int64_t rows, int64_t cols,
+                        int64_t ld_x, int64_t batch_stride_x, const fp4_quant_opts* opts,
+                        uint8_t* codes, int64_t ld_codes, int64_t batch_stride_codes,
+                        uint8_t* scales, int64_t ld_scales, int64_t batch_stride_scales,
+                        float* tensor_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  QuantPlan p;
+  fp4_status st = plan_quantize(batch, rows, cols, opts, &p);
+  if (st != FP4_OK) return st;
+  if (x_dtype != FP4_F32 && x_dtype != FP4_BF16) return FP4_ERR_INVALID;
+  if (batch == 0 || rows == 0 || cols == 0) return FP4_OK;
+  const bool nv = opts->format == FP4_NVFP4;
+  if (!x || !codes || !scales || (nv && !tensor_scale)) return FP4_ERR_INVALID;
+  if (ld_x < cols || ld_codes < p.C / 2 || ld_scales < p.C / p.blk) return FP4_ERR_INVALID;
+  if (batch > 1) {
+    if (batch_stride_x < 0) return FP4_ERR_INVALID;
+    if (batch_stride_codes < (p.R - 1) * ld_codes + p.C / 2) return FP4_ERR_INVALID;
+    if (batch_stride_scales < (p.R - 1) * ld_scales + p.C / p.blk) return FP4_ERR_INVALID;
+  }
+  const int64_t esize = x_dtype == FP4_BF16 ? 2 : 4;
+  if (!aligned(x, 16) || (ld_x * esize) % 16 != 0 || (batch > 1 && (batch_stride_x * esize) % 16 != 0))
+    return FP4_ERR_ALIGN;
+  if (!aligned(codes, 8) || ld_codes % 8 != 0 || (batch > 1 && batch_stride_codes % 8 != 0)) return FP4_ERR_ALIGN;
+  if (nv && !aligned(tensor_scale, 4)) return FP4_ERR_ALIGN;
+  if (nv && opts->amax_in && !aligned(opts->amax_in, 4)) return FP4_ERR_ALIGN;
+  if (p.ws > 0) {
+    if (!workspace || workspace_bytes < p.ws) return FP4_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return FP4_ERR_ALIGN;
+  }
+  st = check_device();
+  if (st != FP4_OK) return st;
+
+  QuantArgs a;
+  a.x = x;
+  a.x_bf16 = x_dtype == FP4_BF16;
+  a.batch = batch;
+  a.src_rows = rows;
+  a.src_cols = cols;
+  a.ld_x = ld_x;
+  a.bs_x = batch > 1 ? batch_stride_x : 0;
+  a.R = p.R;
+  a.C = p.C;
+  a.nvfp4 = nv;
+  a.flags = opts->flags;
+  a.signs = opts->rht_signs & 0xffffu;
+  a.seed = opts->seed;
+  a.offset = opts->offset;
+  a.amax_in = opts->amax_in;
+  a.codes = codes;
+  a.ld_c = ld_codes;
+  a.bs_c = batch > 1 ? batch_stride_codes : 0;
+  a.scales = scales;
+  a.ld_s = ld_scales;
+  a.bs_s = batch > 1 ? batch_stride_scales : 0;
+  a.tensor_scale = tensor_scale;
+  a.partials = static_cast<float*>(workspace);
+  a.nparts = p.nparts;
+  (void)hipGetLastError();
+  return launch_quantize(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FP4_OK : FP4_ERR_HIP;
+}
+
+fp4_status fp4_dequantize(int32_t format, int64_t batch, int64_t rows, int64_t cols,
+                          const uint8_t* codes, int64_t ld_codes, int64_t batch_stride_codes,
+                          const uint8_t* scales, int64_t ld_scales, int64_t batch_stride_scales,
+                          const float* tensor_scale, void* y, int32_t y_dtype, int64_t ld_y,
+                          int64_t batch_stride_y, void* stream) {
+  if (format != FP4_MXFP4 && format != FP4_NVFP4) return FP4_ERR_INVALID;
+  if (y_dtype != FP4_F32 && y_dtype != FP4_BF16) return FP4_ERR_INVALID;
+  if (batch < 0 || rows < 0 || cols < 0) return FP4_ERR_INVALID;
+  const bool nv = format == FP4_NVFP4;
+  const int64_t blk = nv ? 16 : 32;
+  if (cols % blk != 0) return FP4_ERR_INVALID;
+  if (batch > kMaxGridYZ) return FP4_ERR_UNSUPPORTED;
+  if (rows > 0 && ((rows * (cols / 16)) + 255) / 256 > kMaxGridX) return FP4_ERR_UNSUPPORTED;
+  if (batch == 0 || rows == 0 || cols == 0) return FP4_OK;
+  if (!codes || !scales || !y || (nv && !tensor_scale)) return FP4_ERR_INVALID;
+  if (ld_codes < cols / 2 || ld_scales < cols / blk || ld_y < cols) return FP4_ERR_INVALID;
+  if (batch > 1 && (batch_stride_codes < 0 || batch_stride_scales < 0 ||
+                    batch_stride_y < (rows - 1) * ld_y + cols))
+    return FP4_ERR_INVALID;
+  const int64_t esize = y_dtype == FP4_BF16 ? 2 : 4;
+  if (!aligned(codes, 8) || ld_codes % 8 != 0 || (batch > 1 && batch_stride_codes % 8 != 0)) return FP4_ERR_ALIGN;
+  if (!aligned(y, 16) || (ld_y * esize) % 16 != 0 || (batch > 1 && (batch_stride_y * esize) % 16 != 0))
+    return FP4_ERR_ALIGN;
+  if (nv && !aligned(tensor_scale, 4)) return FP4_ERR_ALIGN;
+  fp4_status st = check_device();
+  if (st != FP4_OK) return st;
+  DequantArgs a;
+  a.nvfp4 = nv;
+  a.batch = batch;
+  a.rows = rows;
+  a.cols = cols;
+  a.codes = codes;
+  a.ld_c = ld_codes;
+  a.bs_c = batch > 1 ? batch_stride_codes : 0;
+  a.scales = scales;
+  a.ld_s = ld_scales;
+  a.bs_s = batch > 1 ? batch_stride_scales : 0;
+  a.tensor_scale = tensor_scale;
+  a.y = y;
+  a.y_bf16 = y_dtype == FP4_BF16;
+  a.ld_y = ld_y;
+  a.bs_y = batch > 1 ? batch_stride_y : 0;
+  (void)hipGetLastError();
+  return launch_dequantize(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FP4_OK : FP4_ERR_HIP;
+}
+
+fp4_status fp4_gemm(int32_t format, int64_t groups, int64_t M, int64_t N, int64_t K,
+                    const uint8_t* a_codes, int64_t lda, int64_t a_group_stride,
+                    const uint8_t* a_scales, int64_t lda_scales, int64_t a_scales_group_stride,
+                    const float* a_tensor_scale,
+                    const uint8_t* b_codes, int64_t ldb, int64_t b_group_stride,
+                    const uint8_t* b_scales, int64_t ldb_scales, int64_t b_scales_group_stride,
+                    const float* b_tensor_scale,
+                    void* c, int32_t c_dtype, int64_t ldc, int64_t c_group_stride, void* stream) {
+  if (format != FP4_MXFP4 && format != FP4_NVFP4) return FP4_ERR_INVALID;
+  if (c_dtype != FP4_F32 && c_dtype != FP4_BF16) return FP4_ERR_INVALID;
+  if (groups < 0 || M < 0 || N < 0 || K < 0) return FP4_ERR_INVALID;
+  if (K % 64 != 0) return FP4_ERR_INVALID;
+  if (groups > kMaxGridYZ || (M + 127) / 128 > kMaxGridYZ || (N + 127) / 128 > kMaxGridX) return FP4_ERR_UNSUPPORTED;
+  if (groups == 0 || M == 0 || N == 0) return FP4_OK;
+  const bool nv = format == FP4_NVFP4;
+  const int64_t blk = nv ? 16 : 32;
+  if (!a_codes || !a_scales || !b_codes || !b_scales || !c) return FP4_ERR_INVALID;
+  if (nv && (!a_tensor_scale || !b_tensor_scale)) return FP4_ERR_INVALID;
+  if (lda < K / 2 || ldb < K / 2 || lda_scales < K / blk || ldb_scales < K / blk || ldc < N) return FP4_ERR_INVALID;
+  if (groups > 1 && (a_group_stride < 0 || b_group_stride < 0 || a_scales_group_stride < 0 ||
+                     b_scales_group_stride < 0 || c_group_stride < (M - 1) * ldc + N))
+    return FP4_ERR_INVALID;
+  if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || lda % 16 != 0 || ldb % 16 != 0) return FP4_ERR_ALIGN;
+  if (groups > 1 && (a_group_stride % 16 != 0 || b_group_stride % 16 != 0)) return FP4_ERR_ALIGN;
+  if (!aligned(c, c_dtype == FP4_BF16 ? 2 : 4)) return FP4_ERR_ALIGN;
+  if (nv && (!aligned(a_tensor_scale, 4) || !aligned(b_tensor_scale, 4))) return FP4_ERR_ALIGN;
+  fp4_status st = check_device();
+  if (st != FP4_OK) return st;
+  GemmArgs g;
+  g.nvfp4 = nv;
+  g.groups = groups;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.a = a_codes;
+  g.lda = lda;
+  g.a_gs = groups > 1 ? a_group_stride : 0;
+  g.as = a_scales;
+  g.lda_s = lda_scales;
+  g.as_gs = groups > 1 ? a_scales_group_stride : 0;
+  g.a_ts = a_tensor_scale;
+  g.b = b_codes;
+  g.ldb = ldb;
+  g.b_gs = groups > 1 ? b_group_stride : 0;
+  g.bs = b_scales;
+  g.ldb_s = ldb_scales;
+  g.bs_gs = groups > 1 ? b_scales_group_stride : 0;
+  g.b_ts = b_tensor_scale;
+  g.c = c;
+  g.c_bf16 = c_dtype == FP4_BF16;
+  g.ldc = ldc;
+  g.c_gs = groups > 1 ? c_group_stride : 0;
+  (void)hipGetLastError();
+  return launch_gemm(g, static_cast<hipStream_t>(stream)) == hipSuccess ? FP4_OK : FP4_ERR_HIP;
+}
+
+}  // extern "C"

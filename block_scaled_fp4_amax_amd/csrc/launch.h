@@ -1,0 +1,79 @@
+// launch.h -- internal launch interface between the C ABI (fp4_api.cpp) and
+// the HIP kernels. Arguments here are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4impl {
+
+enum Flags : uint32_t {
+  kFourOverSix = 1u,
+  kBlock2D = 2u,
+  kTranspose = 4u,
+  kStochastic = 8u,
+  kHadamard = 16u,
+};
+
+struct QuantArgs {
+  const void* x;
+  bool x_bf16;
+  int64_t batch, src_rows, src_cols;  // source matrix per batch item
+  int64_t ld_x, bs_x;                 // elements
+  int64_t R, C;                       // output matrix (C is the block direction)
+  bool nvfp4;
+  uint32_t flags;
+  uint32_t signs;
+  uint64_t seed, offset;
+  const float* amax_in;   // [batch] or null
+  uint8_t* codes;
+  int64_t ld_c, bs_c;
+  uint8_t* scales;
+  int64_t ld_s, bs_s;
+  float* tensor_scale;    // [batch] (NVFP4)
+  float* partials;        // workspace [batch][nparts] (NVFP4 without amax_in)
+  int nparts;
+};
+
+// Number of per-workgroup partial maxima the NVFP4 amax pre-pass writes for
+// one batch item (also fixes its grid).
+int amax_partials(int64_t src_rows, int64_t src_cols, uint32_t flags);
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
+
+struct DequantArgs {
+  bool nvfp4;
+  int64_t batch, rows, cols;
+  const uint8_t* codes;
+  int64_t ld_c, bs_c;
+  const uint8_t* scales;
+  int64_t ld_s, bs_s;
+  const float* tensor_scale;
+  void* y;
+  bool y_bf16;
+  int64_t ld_y, bs_y;
+};
+
+hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream);
+
+struct GemmArgs {
+  bool nvfp4;
+  int64_t groups, M, N, K;
+  const uint8_t* a;
+  int64_t lda, a_gs;
+  const uint8_t* as;
+  int64_t lda_s, as_gs;
+  const float* a_ts;
+  const uint8_t* b;
+  int64_t ldb, b_gs;
+  const uint8_t* bs;
+  int64_t ldb_s, bs_gs;
+  const float* b_ts;
+  void* c;
+  bool c_bf16;
+  int64_t ldc, c_gs;
+};
+
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream);
+
+}  // namespace fp4impl

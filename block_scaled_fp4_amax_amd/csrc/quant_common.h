@@ -1,0 +1,149 @@
+// quant_common.h -- per-block quantization steps shared by the row-major and
+// the transposed quantize kernels.
+//
+// Method (Ultralytics glossary "FP4", section "Como funciona FP4"; Hugging
+// Face transformers "Four Over Six", introduction):
+//   MXFP4  block of 32 along the row, scale 2^e with e = floor(log2 amax) - 2
+//          (E8M0), element code = nearest E2M1 of x / 2^e.
+//   NVFP4  block of 16, E4M3 scale of amax / (M * S_t) with M = 6, element
+//          code = nearest E2M1 of x * (1 / (E4M3 * S_t)).
+//   4/6    also try M = 4 and keep the candidate with the smaller squared
+//          error; the error of a 16-slice is eff^2 * (FMA chain over elements
+//          0..7 of (val - q)^2 + FMA chain over elements 8..15).
+#pragma once
+
+#include "fp4_device.h"
+#include "launch.h"
+
+namespace fp4impl {
+using namespace fp4dev;
+
+constexpr float kInf = __builtin_huge_valf();
+
+// One NVFP4 scale candidate: effective block scale eff = E4M3(code) * S_t and
+// its correctly rounded reciprocal. eff below the smallest normal makes the
+// block a zero block (r = 0, so every code keeps only its sign).
+struct NvCand {
+  float eff, r;
+  uint32_t code;
+  bool zero;
+};
+
+__device__ __forceinline__ NvCand nv_candidate(float amax, float k, float St) {
+  NvCand c;
+  float s = amax * k;
+  s = s > kE4M3Max ? kE4M3Max : s;
+  c.code = e4m3_encode(s);
+  c.eff = e4m3_decode(c.code) * St;
+  c.zero = !(c.eff >= kFltMin);
+  c.r = c.zero ? 0.0f : 1.0f / c.eff;
+  return c;
+}
+
+// Nearest-even E2M1 codes of 16 scaled values, packed 2 per byte.
+__device__ __forceinline__ void pack16(const float q[16], uint32_t& w0, uint32_t& w1) {
+  w0 = e2m1_pack2<0>(0u, q[0], q[1]);
+  w0 = e2m1_pack2<1>(w0, q[2], q[3]);
+  w0 = e2m1_pack2<2>(w0, q[4], q[5]);
+  w0 = e2m1_pack2<3>(w0, q[6], q[7]);
+  w1 = e2m1_pack2<0>(0u, q[8], q[9]);
+  w1 = e2m1_pack2<1>(w1, q[10], q[11]);
+  w1 = e2m1_pack2<2>(w1, q[12], q[13]);
+  w1 = e2m1_pack2<3>(w1, q[14], q[15]);
+}
+
+// FMA chain of (val(code) - q)^2 over 8 elements whose codes are packed in w.
+__device__ __forceinline__ float sq_chain8(const float q[8], uint32_t w) {
+  f32x2 d0 = e2m1_unpack2<0>(w), d1 = e2m1_unpack2<1>(w), d2 = e2m1_unpack2<2>(w), d3 = e2m1_unpack2<3>(w);
+  float acc = 0.0f, e;
+  e = d0.x - q[0]; acc = __builtin_fmaf(e, e, acc);
+  e = d0.y - q[1]; acc = __builtin_fmaf(e, e, acc);
+  e = d1.x - q[2]; acc = __builtin_fmaf(e, e, acc);
+  e = d1.y - q[3]; acc = __builtin_fmaf(e, e, acc);
+  e = d2.x - q[4]; acc = __builtin_fmaf(e, e, acc);
+  e = d2.y - q[5]; acc = __builtin_fmaf(e, e, acc);
+  e = d3.x - q[6]; acc = __builtin_fmaf(e, e, acc);
+  e = d3.y - q[7]; acc = __builtin_fmaf(e, e, acc);
+  return acc;
+}
+
+__device__ __forceinline__ float sq_sum16(const float q[16], uint32_t w0, uint32_t w1) {
+  return sq_chain8(q, w0) + sq_chain8(q + 8, w1);
+}
+
+// Candidate error eff^2 * partial sum; a zero block never wins.
+__device__ __forceinline__ float cand_error(const NvCand& c, float sum) {
+  return c.zero ? kInf : (c.eff * c.eff) * sum;
+}
+
+// Stochastic rounding of 16 scaled values whose first element has linear
+// output index L0 (a multiple of 16): Philox4x32-10 with counter
+// (L/8, offset) and key seed gives 128 bits per 8 elements, 16 bits each
+// (element L uses word (L/2) % 4, low half when L is even).
+__device__ __forceinline__ void sr16(const float q[16], uint64_t L0, uint64_t seed, uint64_t offset,
+                                     uint32_t& w0, uint32_t& w1) {
+  uint64_t n = L0 >> 3;
+  uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  uint32_t o0 = (uint32_t)offset, o1 = (uint32_t)(offset >> 32);
+  u32x4 ra = philox4x32_10(u32x4{(uint32_t)n, (uint32_t)(n >> 32), o0, o1}, k0, k1);
+  n += 1;
+  u32x4 rb = philox4x32_10(u32x4{(uint32_t)n, (uint32_t)(n >> 32), o0, o1}, k0, k1);
+  w0 = 0u;
+  w1 = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    uint32_t wa = ra[(i >> 1) & 3], wb = rb[(i >> 1) & 3];
+    uint32_t r16a = (i & 1) ? (wa >> 16) : (wa & 0xffffu);
+    uint32_t r16b = (i & 1) ? (wb >> 16) : (wb & 0xffffu);
+    w0 |= e2m1_sr(q[i], r16a) << (4 * i);
+    w1 |= e2m1_sr(q[8 + i], r16b) << (4 * i);
+  }
+}
+
+// NVFP4 tensor scale for batch item b, computed identically by every
+// workgroup: T from amax_in or the max of the pre-pass partials; S_t = T / D
+// with D = 6 * 448 (4 * 448 under 4/6), replaced by 1 when zero, denormal or
+// not finite. Workgroup (0, 0) of the item stores S_t.
+template <bool FOS>
+__device__ __forceinline__ float tensor_scale_prologue(const QuantArgs& a, int64_t b) {
+  __shared__ float red[4];
+  float T;
+  if (a.amax_in) {
+    T = a.amax_in[b];
+  } else {
+    float m = 0.0f;
+    const float* p = a.partials + b * a.nparts;
+    for (int i = threadIdx.x; i < a.nparts; i += blockDim.x) m = __builtin_fmaxf(m, p[i]);
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, s, 64));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    T = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+  }
+  float St = T / (FOS ? 1792.0f : 2688.0f);
+  if (!(St >= kFltMin && St <= 3.40282347e38f)) St = 1.0f;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.tensor_scale[b] = St;
+  return St;
+}
+
+template <typename TIn>
+__device__ __forceinline__ void load8(const TIn* p, float v[8]);
+
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float v[8]) {
+  uint4 w = *reinterpret_cast<const uint4*>(p);
+  v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
+  v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+  v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
+  v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+}
+
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float v[8]) {
+  float4 a = reinterpret_cast<const float4*>(p)[0];
+  float4 b = reinterpret_cast<const float4*>(p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+}  // namespace fp4impl

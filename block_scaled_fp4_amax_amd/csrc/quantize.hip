@@ -1,0 +1,393 @@
+// quantize.hip -- block-scaled FP4 quantization kernels for gfx950.
+//
+//   amax_kernel        NVFP4 tensor-amax pre-pass (after the Hadamard
+//                      transform when on): per-workgroup partial maxima.
+//   quant_rows_kernel  blocks along contiguous rows. One lane owns one
+//                      16-value slice (two 16-byte loads of bf16): an NVFP4
+//                      block, half an MXFP4 block (lane pair), or one row of a
+//                      16x16 tile (16 lanes).
+//   quant_cols_kernel  transposed input: blocks run down the columns of X.
+//                      One lane owns a 16-row x 8-column patch (sixteen
+//                      16-byte row loads, so a wave reads 32 rows x 256
+//                      columns with 1 KiB-contiguous accesses) = eight blocks,
+//                      one per source column; an MXFP4 block is a vertical
+//                      lane pair, a 16x16 tile a horizontal one.
+//
+// The method is stated in quant_common.h.
+#include "quant_common.h"
+
+namespace fp4impl {
+
+// ------------------------------------------------------------------------
+// amax pre-pass
+// ------------------------------------------------------------------------
+enum AmaxMode { kAmaxPlain = 0, kAmaxRhtRows = 1, kAmaxRhtCols = 2 };
+
+int amax_partials(int64_t src_rows, int64_t src_cols, uint32_t flags) {
+  int64_t units;
+  if (!(flags & kHadamard)) units = src_rows * (src_cols / 8);
+  else if (flags & kTranspose) units = (src_rows / 16) * (src_cols / 8);
+  else units = src_rows * (src_cols / 16);
+  int64_t p = (units + 4 * 256 - 1) / (4 * 256);
+  if (p < 1) p = 1;
+  if (p > 1024) p = 1024;
+  return (int)p;
+}
+
+template <typename TIn, int MODE>
+__global__ __launch_bounds__(256) void amax_kernel(QuantArgs a) {
+  const int64_t b = blockIdx.y;
+  const TIn* x = reinterpret_cast<const TIn*>(a.x) + b * a.bs_x;
+  const int64_t rows = a.src_rows, cols = a.src_cols;
+  int64_t per_row, units;
+  if (MODE == kAmaxPlain) { per_row = cols / 8; units = rows * per_row; }
+  else if (MODE == kAmaxRhtRows) { per_row = cols / 16; units = rows * per_row; }
+  else { per_row = cols / 8; units = (rows / 16) * per_row; }
+  float m = 0.0f;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < units; u += stride) {
+    int64_t r = u / per_row, c = u - r * per_row;
+    if (MODE == kAmaxPlain) {
+      float v[8];
+      load8<TIn>(x + r * a.ld_x + c * 8, v);
+#pragma unroll
+      for (int i = 0; i < 8; i++) m = __builtin_fmaxf(m, __builtin_fabsf(v[i]));
+    } else if (MODE == kAmaxRhtRows) {
+      float v[16];
+      load8<TIn>(x + r * a.ld_x + c * 16, v);
+      load8<TIn>(x + r * a.ld_x + c * 16 + 8, v + 8);
+      rht16(v, a.signs);
+      m = __builtin_fmaxf(m, max_abs16(v));
+    } else {
+      float t[16][8];
+#pragma unroll
+      for (int i = 0; i < 16; i++) load8<TIn>(x + (r * 16 + i) * a.ld_x + c * 8, t[i]);
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; i++) v[i] = t[i][j];
+        rht16(v, a.signs);
+        m = __builtin_fmaxf(m, max_abs16(v));
+      }
+    }
+  }
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, s, 64));
+  __shared__ float red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    a.partials[b * a.nparts + blockIdx.x] =
+        __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+}
+
+// ------------------------------------------------------------------------
+// Row-major quantization
+// ------------------------------------------------------------------------
+template <typename TIn, bool NV, bool FOS, bool B2D, bool SR, bool RHT>
+__global__ __launch_bounds__(256) void quant_rows_kernel(QuantArgs a) {
+  const int64_t b = blockIdx.z;
+  float St = 1.0f, k6 = 0.0f, k4 = 0.0f;
+  if constexpr (NV) {
+    St = tensor_scale_prologue<FOS>(a, b);
+    k6 = 1.0f / (6.0f * St);
+    k4 = 1.0f / (4.0f * St);
+  }
+  const int64_t upr = a.C >> 4;  // 16-value units per row
+  int64_t row, cu;
+  if constexpr (B2D) {
+    row = (int64_t)blockIdx.y * 16 + (threadIdx.x & 15);
+    cu = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  } else {
+    int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    row = u / upr;
+    cu = u - row * upr;
+  }
+  // validity is uniform across every group of lanes that exchanges data
+  if (row >= a.R || cu >= upr) return;
+
+  const TIn* xp = reinterpret_cast<const TIn*>(a.x) + b * a.bs_x + row * a.ld_x + cu * 16;
+  float v[16];
+  load8<TIn>(xp, v);
+  load8<TIn>(xp + 8, v + 8);
+  if constexpr (RHT) rht16(v, a.signs);
+
+  float amax = max_abs16(v);
+  uint32_t w0, w1, sbyte;
+  const uint64_t L0 = ((uint64_t)b * (uint64_t)a.R + (uint64_t)row) * (uint64_t)a.C + (uint64_t)cu * 16;
+
+  if constexpr (!NV) {
+    amax = __builtin_fmaxf(amax, xor_shfl<1>(amax));
+    sbyte = e8m0_from_amax(amax);
+    if constexpr (SR) {
+      float q[16];
+#pragma unroll
+      for (int i = 0; i < 16; i++) q[i] = __builtin_ldexpf(v[i], 127 - (int)sbyte);
+      sr16(q, L0, a.seed, a.offset, w0, w1);
+    } else {
+      float sc = e8m0_scale_operand(sbyte);
+      w0 = e2m1_pack2_scaled<0>(0u, v[0], v[1], sc);
+      w0 = e2m1_pack2_scaled<1>(w0, v[2], v[3], sc);
+      w0 = e2m1_pack2_scaled<2>(w0, v[4], v[5], sc);
+      w0 = e2m1_pack2_scaled<3>(w0, v[6], v[7], sc);
+      w1 = e2m1_pack2_scaled<0>(0u, v[8], v[9], sc);
+      w1 = e2m1_pack2_scaled<1>(w1, v[10], v[11], sc);
+      w1 = e2m1_pack2_scaled<2>(w1, v[12], v[13], sc);
+      w1 = e2m1_pack2_scaled<3>(w1, v[14], v[15], sc);
+    }
+  } else {
+    if constexpr (B2D) {
+      amax = __builtin_fmaxf(amax, xor_shfl<1>(amax));
+      amax = __builtin_fmaxf(amax, xor_shfl<2>(amax));
+      amax = __builtin_fmaxf(amax, xor_shfl<4>(amax));
+      amax = __builtin_fmaxf(amax, xor_shfl<8>(amax));
+    }
+    NvCand c = nv_candidate(amax, k6, St);
+    float q[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) q[i] = v[i] * c.r;
+    pack16(q, w0, w1);
+    if constexpr (FOS) {
+      NvCand c4 = nv_candidate(amax, k4, St);
+      float q4[16];
+#pragma unroll
+      for (int i = 0; i < 16; i++) q4[i] = v[i] * c4.r;
+      uint32_t x0, x1;
+      pack16(q4, x0, x1);
+      float s6 = sq_sum16(q, w0, w1), s4 = sq_sum16(q4, x0, x1);
+      if constexpr (B2D) {
+        // pairwise tree over the tile's 16 rows (lanes), adjacent rows first
+        s6 = s6 + xor_shfl<1>(s6); s4 = s4 + xor_shfl<1>(s4);
+        s6 = s6 + xor_shfl<2>(s6); s4 = s4 + xor_shfl<2>(s4);
+        s6 = s6 + xor_shfl<4>(s6); s4 = s4 + xor_shfl<4>(s4);
+        s6 = s6 + xor_shfl<8>(s6); s4 = s4 + xor_shfl<8>(s4);
+      }
+      if (cand_error(c4, s4) < cand_error(c, s6)) {
+        c = c4;
+        w0 = x0;
+        w1 = x1;
+#pragma unroll
+        for (int i = 0; i < 16; i++) q[i] = q4[i];
+      }
+    }
+    if constexpr (SR) sr16(q, L0, a.seed, a.offset, w0, w1);
+    sbyte = c.code;
+  }
+
+  uint8_t* cp = a.codes + b * a.bs_c + row * a.ld_c + cu * 8;
+  *reinterpret_cast<uint2*>(cp) = make_uint2(w0, w1);
+  if constexpr (NV) {
+    a.scales[b * a.bs_s + row * a.ld_s + cu] = (uint8_t)sbyte;
+  } else {
+    if ((cu & 1) == 0) a.scales[b * a.bs_s + row * a.ld_s + (cu >> 1)] = (uint8_t)sbyte;
+  }
+}
+
+// ------------------------------------------------------------------------
+// Transposed quantization (output = Q(X^T))
+// ------------------------------------------------------------------------
+template <typename TIn, bool NV, bool FOS, bool B2D, bool SR, bool RHT>
+__global__ __launch_bounds__(256) void quant_cols_kernel(QuantArgs a) {
+  const int64_t b = blockIdx.z;
+  float St = 1.0f, k6 = 0.0f, k4 = 0.0f;
+  if constexpr (NV) {
+    St = tensor_scale_prologue<FOS>(a, b);
+    k6 = 1.0f / (6.0f * St);
+    k4 = 1.0f / (4.0f * St);
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane & 1, g = lane >> 1;
+  const int64_t n0 = (int64_t)blockIdx.x * 256 + g * 8;                 // source columns n0..n0+7
+  const int64_t k0 = (int64_t)blockIdx.y * 128 + wave * 32 + h * 16;    // source rows k0..k0+15
+  if (n0 >= a.src_cols || k0 >= a.src_rows) return;
+
+  const TIn* xp = reinterpret_cast<const TIn*>(a.x) + b * a.bs_x + k0 * a.ld_x + n0;
+  float t[16][8];
+#pragma unroll
+  for (int i = 0; i < 16; i++) load8<TIn>(xp + i * a.ld_x, t[i]);
+
+  uint8_t* cbase = a.codes + b * a.bs_c + (k0 >> 1);
+  uint8_t* sbase = a.scales + b * a.bs_s;
+  const uint64_t Lrow = (uint64_t)b * (uint64_t)a.R;
+
+  if constexpr (NV && B2D) {
+    // one 16x16 tile per horizontal lane pair (lanes g and g^1)
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i++)
+#pragma unroll
+      for (int j = 0; j < 8; j++) amax = __builtin_fmaxf(amax, __builtin_fabsf(t[i][j]));
+    amax = __builtin_fmaxf(amax, xor_shfl<2>(amax));
+    NvCand c = nv_candidate(amax, k6, St);
+    if constexpr (FOS) {
+      NvCand c4 = nv_candidate(amax, k4, St);
+      // per source row: FMA chain over this lane's 8 columns, plus the
+      // partner's chain over the other 8 columns; then a pairwise tree over
+      // the 16 source rows
+      float p6[16], p4[16];
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        float q6[8], q4[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) { q6[j] = t[i][j] * c.r; q4[j] = t[i][j] * c4.r; }
+        uint32_t w6 = e2m1_pack2<0>(0u, q6[0], q6[1]);
+        w6 = e2m1_pack2<1>(w6, q6[2], q6[3]);
+        w6 = e2m1_pack2<2>(w6, q6[4], q6[5]);
+        w6 = e2m1_pack2<3>(w6, q6[6], q6[7]);
+        uint32_t w4 = e2m1_pack2<0>(0u, q4[0], q4[1]);
+        w4 = e2m1_pack2<1>(w4, q4[2], q4[3]);
+        w4 = e2m1_pack2<2>(w4, q4[4], q4[5]);
+        w4 = e2m1_pack2<3>(w4, q4[6], q4[7]);
+        p6[i] = sq_chain8(q6, w6);
+        p4[i] = sq_chain8(q4, w4);
+        p6[i] = p6[i] + xor_shfl<2>(p6[i]);
+        p4[i] = p4[i] + xor_shfl<2>(p4[i]);
+      }
+#pragma unroll
+      for (int width = 1; width < 16; width <<= 1)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2 * width) {
+          p6[i] = p6[i] + p6[i + width];
+          p4[i] = p4[i] + p4[i + width];
+        }
+      if (cand_error(c4, p4[0]) < cand_error(c, p6[0])) c = c4;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const int64_t n = n0 + j;
+      float q[16];
+#pragma unroll
+      for (int i = 0; i < 16; i++) q[i] = t[i][j] * c.r;
+      uint32_t w0, w1;
+      if constexpr (SR) sr16(q, (Lrow + (uint64_t)n) * (uint64_t)a.C + (uint64_t)k0, a.seed, a.offset, w0, w1);
+      else pack16(q, w0, w1);
+      *reinterpret_cast<uint2*>(cbase + n * a.ld_c) = make_uint2(w0, w1);
+      sbase[n * a.ld_s + (k0 >> 4)] = (uint8_t)c.code;
+    }
+    return;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const int64_t n = n0 + j;
+      float v[16];
+#pragma unroll
+      for (int i = 0; i < 16; i++) v[i] = t[i][j];
+      if constexpr (RHT) rht16(v, a.signs);
+      float amax = max_abs16(v);
+      const uint64_t L0 = (Lrow + (uint64_t)n) * (uint64_t)a.C + (uint64_t)k0;
+      uint32_t w0, w1, sbyte;
+      if constexpr (!NV) {
+        amax = __builtin_fmaxf(amax, xor_shfl<1>(amax));  // vertical lane pair = 32 rows
+        sbyte = e8m0_from_amax(amax);
+        if constexpr (SR) {
+          float q[16];
+#pragma unroll
+          for (int i = 0; i < 16; i++) q[i] = __builtin_ldexpf(v[i], 127 - (int)sbyte);
+          sr16(q, L0, a.seed, a.offset, w0, w1);
+        } else {
+          float sc = e8m0_scale_operand(sbyte);
+          w0 = e2m1_pack2_scaled<0>(0u, v[0], v[1], sc);
+          w0 = e2m1_pack2_scaled<1>(w0, v[2], v[3], sc);
+          w0 = e2m1_pack2_scaled<2>(w0, v[4], v[5], sc);
+          w0 = e2m1_pack2_scaled<3>(w0, v[6], v[7], sc);
+          w1 = e2m1_pack2_scaled<0>(0u, v[8], v[9], sc);
+          w1 = e2m1_pack2_scaled<1>(w1, v[10], v[11], sc);
+          w1 = e2m1_pack2_scaled<2>(w1, v[12], v[13], sc);
+          w1 = e2m1_pack2_scaled<3>(w1, v[14], v[15], sc);
+        }
+        if (h == 0) sbase[n * a.ld_s + (k0 >> 5)] = (uint8_t)sbyte;
+      } else {
+        NvCand c = nv_candidate(amax, k6, St);
+        float q[16];
+#pragma unroll
+        for (int i = 0; i < 16; i++) q[i] = v[i] * c.r;
+        pack16(q, w0, w1);
+        if constexpr (FOS) {
+          NvCand c4 = nv_candidate(amax, k4, St);
+          float q4[16];
+#pragma unroll
+          for (int i = 0; i < 16; i++) q4[i] = v[i] * c4.r;
+          uint32_t x0, x1;
+          pack16(q4, x0, x1);
+          if (cand_error(c4, sq_sum16(q4, x0, x1)) < cand_error(c, sq_sum16(q, w0, w1))) {
+            c = c4;
+            w0 = x0;
+            w1 = x1;
+#pragma unroll
+            for (int i = 0; i < 16; i++) q[i] = q4[i];
+          }
+        }
+        if constexpr (SR) sr16(q, L0, a.seed, a.offset, w0, w1);
+        sbyte = c.code;
+        sbase[n * a.ld_s + (k0 >> 4)] = (uint8_t)sbyte;
+      }
+      *reinterpret_cast<uint2*>(cbase + n * a.ld_c) = make_uint2(w0, w1);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
+// dispatch
+// ------------------------------------------------------------------------
+template <typename TIn, bool NV, bool FOS, bool B2D, bool SR, bool RHT>
+static void launch_one(const QuantArgs& a, hipStream_t s) {
+  if (a.flags & kTranspose) {
+    if constexpr (B2D && RHT) {
+      return;  // rejected by the API
+    } else {
+      dim3 grid((unsigned)((a.src_cols + 255) / 256), (unsigned)((a.src_rows + 127) / 128), (unsigned)a.batch);
+      hipLaunchKernelGGL((quant_cols_kernel<TIn, NV, FOS, B2D, SR, RHT>), grid, dim3(256), 0, s, a);
+    }
+  } else if (B2D) {
+    dim3 grid((unsigned)(((a.C >> 4) + 15) / 16), (unsigned)(a.R / 16), (unsigned)a.batch);
+    hipLaunchKernelGGL((quant_rows_kernel<TIn, NV, FOS, B2D, SR, RHT>), grid, dim3(256), 0, s, a);
+  } else {
+    int64_t units = a.R * (a.C >> 4);
+    dim3 grid((unsigned)((units + 255) / 256), 1, (unsigned)a.batch);
+    hipLaunchKernelGGL((quant_rows_kernel<TIn, NV, FOS, B2D, SR, RHT>), grid, dim3(256), 0, s, a);
+  }
+}
+
+template <typename TIn, bool NV, bool FOS, bool B2D>
+static void launch_sr_rht(const QuantArgs& a, hipStream_t s) {
+  const bool sr = a.flags & kStochastic, rht = a.flags & kHadamard;
+  if (sr) {
+    if (rht) launch_one<TIn, NV, FOS, B2D, true, true>(a, s);
+    else launch_one<TIn, NV, FOS, B2D, true, false>(a, s);
+  } else {
+    if (rht) launch_one<TIn, NV, FOS, B2D, false, true>(a, s);
+    else launch_one<TIn, NV, FOS, B2D, false, false>(a, s);
+  }
+}
+
+template <typename TIn>
+static void launch_typed(const QuantArgs& a, hipStream_t s) {
+  if (!a.nvfp4) {
+    launch_sr_rht<TIn, false, false, false>(a, s);
+    return;
+  }
+  if (!a.amax_in) {
+    int mode = !(a.flags & kHadamard) ? kAmaxPlain : ((a.flags & kTranspose) ? kAmaxRhtCols : kAmaxRhtRows);
+    dim3 grid((unsigned)a.nparts, (unsigned)a.batch);
+    if (mode == kAmaxPlain) hipLaunchKernelGGL((amax_kernel<TIn, kAmaxPlain>), grid, dim3(256), 0, s, a);
+    else if (mode == kAmaxRhtRows) hipLaunchKernelGGL((amax_kernel<TIn, kAmaxRhtRows>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((amax_kernel<TIn, kAmaxRhtCols>), grid, dim3(256), 0, s, a);
+  }
+  const bool fos = a.flags & kFourOverSix, b2d = a.flags & kBlock2D;
+  if (fos) {
+    if (b2d) launch_sr_rht<TIn, true, true, true>(a, s);
+    else launch_sr_rht<TIn, true, true, false>(a, s);
+  } else {
+    if (b2d) launch_sr_rht<TIn, true, false, true>(a, s);
+    else launch_sr_rht<TIn, true, false, false>(a, s);
+  }
+}
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
+  if (a.x_bf16) launch_typed<uint16_t>(a, s);
+  else launch_typed<float>(a, s);
+  return hipGetLastError();
+}
+
+}  // namespace fp4impl

@@ -1,0 +1,149 @@
+"""GPU parity of fp4_gemm against the oracle's reference, the pages' FP32
+fallback: dequantize both operands, then matmul (here in float64). The GEMM's
+operands are the oracle's own codes and scales, uploaded, so nothing on the
+reference side comes from the HIP path.
+
+Tolerance (fp32 output): relative Frobenius error <= 1e-3, and element-wise
+|C - C_ref| <= (2K + 4) * 2^-24 * (|A| |B|^T) (fp32 accumulation over K plus
+the epilogue scaling). bf16 output: the same plus one bf16 rounding,
+2^-8 * |C_ref|."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp4_amax_amd as F
+from block_scaled_fp4_amax_amd import inputs
+from gpu_util import flag_str, oracle_input
+
+pytestmark = pytest.mark.gpu
+
+MX, NV = 0, 1
+FOS, B2D, TR, SR, RHT = 1, 2, 4, 8, 16
+
+
+def oracle_operand(O, x, fmt, flags, signs=0, rows=None):
+    """Oracle-quantize x ([G, r, c] CPU). Returns the uploaded Quantized and the
+    oracle's dequantized values [G, R, C] (float32), optionally only for the
+    output rows `rows`."""
+    x3 = x.unsqueeze(0) if x.dim() == 2 else x
+    codes, scales, ts, deq = [], [], [], []
+    for b in range(x3.shape[0]):
+        r = O.quantize(oracle_input(x3[b]), fmt, flags=flags, rht_signs=signs)
+        codes.append(r["codes"])
+        scales.append(r["scales"])
+        ts.append(r["tensor_scale"] or 0.0)
+        c, s = (r["codes"], r["scales"]) if rows is None else (r["codes"][rows], r["scales"][rows])
+        deq.append(O.dequantize(fmt, c, s, r["tensor_scale"]))
+    q = F.Quantized(fmt, torch.from_numpy(np.stack(codes)).cuda(), torch.from_numpy(np.stack(scales)).cuda(),
+                    torch.tensor(ts, dtype=torch.float32).cuda() if fmt == NV else None)
+    return q, np.stack(deq)
+
+
+def check_close(c_gpu, ref, absab, K, out_dtype, what):
+    c = c_gpu.double().cpu().numpy()
+    bound = (2 * K + 4) * 2.0 ** -24 * absab
+    if out_dtype == torch.bfloat16:
+        bound = bound + 2.0 ** -8 * np.abs(ref)
+    err = np.abs(c - ref)
+    worst = np.argmax(err - bound)
+    assert (err <= bound + 1e-30).all(), f"{what}: element bound exceeded at {np.unravel_index(worst, err.shape)}"
+    if out_dtype == torch.float32:
+        rel = np.linalg.norm(c - ref) / max(np.linalg.norm(ref), 1e-300)
+        assert rel <= 1e-3, f"{what}: relative Frobenius error {rel}"
+
+
+def run_case(O, a, b, fmt, fa, fb, out_dtype, signs=0, what=""):
+    print(f"[gemm] {what} fmt={fmt} A{tuple(a.shape)} {flag_str(fa)} B{tuple(b.shape)} {flag_str(fb)} -> {out_dtype}",
+          flush=True)
+    qa, da = oracle_operand(O, a, fmt, fa, signs)
+    qb, db = oracle_operand(O, b, fmt, fb, signs)
+    c = F.gemm(qa, qb, out_dtype)
+    torch.cuda.synchronize()
+    c3 = c if c.dim() == 3 else c.unsqueeze(0)
+    for g in range(da.shape[0]):
+        ref = O.gemm_reference(da[g], db[g])
+        absab = np.abs(da[g]).astype(np.float64) @ np.abs(db[g]).astype(np.float64).T
+        check_close(c3[g], ref, absab, da.shape[-1], out_dtype, f"{what} group {g}")
+
+
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_mxfp4_dense_ragged(oracle, out):
+    a = inputs.w4a4_linear(m=70, n=200, k=320)
+    run_case(oracle, a["a"], a["w"], MX, 0, 0, out, what="mx-dense")
+
+
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_mxfp4_grouped_moe_recipe(oracle, out):
+    d = inputs.moe_mxfp4(experts=3, tokens=40, k=2880, n=96)
+    run_case(oracle, d["x"], d["w"], MX, 0, TR, out, what="mx-grouped")
+
+
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("flags", [0, FOS])
+def test_nvfp4_dense_ragged(oracle, out, flags):
+    d = inputs.w4a4_linear(m=200, n=272, k=320)
+    run_case(oracle, d["a"], d["w"], NV, flags, flags, out, what="nv-dense")
+
+
+def test_nvfp4_grouped(oracle):
+    a = torch.stack([inputs.w4a4_linear(m=33, n=64, k=128, seed=s)["a"] for s in range(3)])
+    b = torch.stack([inputs.w4a4_linear(m=33, n=64, k=128, seed=s)["w"] for s in range(3)])
+    run_case(oracle, a, b, NV, FOS, FOS, torch.float32, what="nv-grouped")
+
+
+def test_nvfp4_rht_recipe(oracle):
+    d = inputs.rht_activation(m=100, k=256, n=160)
+    run_case(oracle, d["x"], d["w"], NV, FOS | RHT, FOS | RHT | TR, torch.float32, signs=d["signs"], what="nv-rht")
+
+
+def test_rht_cancels_in_the_product(oracle):
+    """Same sign mask on both operands: the rotated FP4 product approximates
+    the unrotated bf16 product about as well as plain FP4 does."""
+    d = inputs.rht_activation(m=128, k=512, n=256)
+    exact = d["x"].double() @ d["w"].double()
+    qa, _ = oracle_operand(oracle, d["x"], NV, FOS | RHT, d["signs"])
+    qb, _ = oracle_operand(oracle, d["w"], NV, FOS | RHT | TR, d["signs"])
+    c = F.gemm(qa, qb, torch.float32).double().cpu()[0]
+    rel = (c - exact).norm() / exact.norm()
+    assert rel < 0.2, rel
+
+
+# ---------------------------------------------------------------------------
+# full sizes (the benchmark's launch configurations), sampled outputs
+# ---------------------------------------------------------------------------
+def full_case(O, a, b, fmt, fa, fb, out_dtype, signs=0, what=""):
+    print(f"[gemm-full] {what} A{tuple(a.shape)} B{tuple(b.shape)}", flush=True)
+    a3 = a.unsqueeze(0) if a.dim() == 2 else a
+    b3 = b.unsqueeze(0) if b.dim() == 2 else b
+    G = a3.shape[0]
+    M = a3.shape[1]
+    N = b3.shape[2] if fb & TR else b3.shape[1]
+    rng = np.random.default_rng(1)
+    rows = np.sort(rng.choice(M, size=min(M, 48), replace=False))
+    cols = np.sort(rng.choice(N, size=min(N, 48), replace=False))
+    qa, da = oracle_operand(O, a3.cpu(), fmt, fa, signs, rows=rows)
+    qb, db = oracle_operand(O, b3.cpu(), fmt, fb, signs, rows=cols)
+    c = F.gemm(qa, qb, out_dtype)
+    torch.cuda.synchronize()
+    c3 = c if c.dim() == 3 else c.unsqueeze(0)
+    for g in sorted(set(rng.integers(0, G, 3).tolist())):
+        ref = O.gemm_reference(da[g], db[g])
+        absab = np.abs(da[g]).astype(np.float64) @ np.abs(db[g]).astype(np.float64).T
+        got = c3[g][torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()]
+        check_close(got, ref, absab, da.shape[-1], out_dtype, f"{what} group {g}")
+
+
+def test_full_w4a4_linear(oracle):
+    d = inputs.w4a4_linear(device="cuda")
+    full_case(oracle, d["a"], d["w"], NV, FOS, FOS, torch.bfloat16, what="2048x4096x4096 nvfp4")
+
+
+def test_full_moe_grouped(oracle):
+    d = inputs.moe_mxfp4(device="cuda")
+    full_case(oracle, d["x"], d["w"], MX, 0, TR, torch.bfloat16, what="32x512x5760x2880 mxfp4")
+
+
+def test_full_rht_gemm(oracle):
+    d = inputs.rht_activation(device="cuda")
+    full_case(oracle, d["x"], d["w"], NV, FOS | RHT, FOS | RHT | TR, torch.bfloat16, signs=d["signs"],
+              what="16384x12288x4096 nvfp4 rht")

@@ -1,0 +1,192 @@
+"""GPU parity of fp4_quantize / fp4_dequantize against the CPU oracle:
+codes, scale bytes and tensor scales bit-exact, on every option combination,
+on shapes that span several workgroups with ragged tails, on the workloads'
+recipes at reduced and at full size (sampled), and on edge cases."""
+import numpy as np
+import pytest
+import torch
+
+from block_scaled_fp4_amax_amd import inputs
+from gpu_util import (assert_codes_equal, flag_str, gpu_quantize, mixed_matrix, oracle_input, oracle_quantize)
+
+pytestmark = pytest.mark.gpu
+
+MX, NV = 0, 1
+FOS, B2D, TR, SR, RHT = 1, 2, 4, 8, 16
+
+
+def valid_combos():
+    out = []
+    for f in range(32):
+        if f & (FOS | B2D) == 0:
+            out.append((MX, f))
+        if not (f & B2D and f & RHT and f & TR):
+            out.append((NV, f))
+    return out
+
+
+def check(F, O, x_cpu, fmt, flags, signs=0x5A3C, seed=1234, offset=5, amax=None, what=""):
+    xd = x_cpu.cuda()
+    print(f"[quantize] {what} fmt={fmt} flags={flag_str(flags)} shape={tuple(x_cpu.shape)} {x_cpu.dtype}",
+          flush=True)
+    q, gc, gs, gt = gpu_quantize(F, xd, fmt, flags, signs, seed, offset, amax=amax)
+    oc, os_, ot = oracle_quantize(O, x_cpu, fmt, flags, signs, seed, offset, amax=amax)
+    assert_codes_equal(gc, oc, f"codes {what} {flag_str(flags)}")
+    assert_codes_equal(gs, os_, f"scales {what} {flag_str(flags)}")
+    if fmt == NV:
+        np.testing.assert_array_equal(gt.view(np.uint32), ot.view(np.uint32))
+    return q
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("fmt,flags", valid_combos(), ids=lambda v: str(v))
+def test_every_option_combination(fp4, oracle, dtype, fmt, flags):
+    x = mixed_matrix(288, 544, seed=flags * 2 + fmt, dtype=dtype)
+    check(fp4, oracle, x, fmt, flags, what="combo")
+
+
+@pytest.mark.parametrize("fmt,flags", [(MX, 0), (MX, TR | SR), (NV, FOS), (NV, FOS | TR | RHT), (NV, B2D | FOS | TR),
+                                       (NV, SR | FOS)])
+def test_batched(fp4, oracle, fmt, flags):
+    x = torch.stack([mixed_matrix(96, 160, seed=s) for s in range(3)])
+    x[1] *= 1000.0
+    check(fp4, oracle, x, fmt, flags, what="batch3")
+
+
+def test_worked_example_all_modes(fp4, oracle):
+    x = inputs.worked_example().reshape(1, 4096)
+    for fmt, flags in [(MX, 0), (NV, 0), (NV, FOS)]:
+        q = check(fp4, oracle, x, fmt, flags, what="worked-example")
+        deq = fp4.dequantize(q).cpu().numpy()
+        r = oracle.quantize(x.numpy(), fmt, flags=flags)
+        want = oracle.dequantize(fmt, r["codes"], r["scales"], r["tensor_scale"])
+        np.testing.assert_array_equal(deq.view(np.uint32), want.view(np.uint32))
+
+
+def test_w4a4_recipe_small(fp4, oracle):
+    d = inputs.w4a4_linear(m=200, n=272, k=320)
+    check(fp4, oracle, d["a"], NV, FOS, what="w4a4-A")
+    check(fp4, oracle, d["w"], NV, FOS, what="w4a4-W")
+
+
+def test_moe_recipe_small(fp4, oracle):
+    d = inputs.moe_mxfp4(experts=3, tokens=40, k=2880, n=96)
+    check(fp4, oracle, d["w"], MX, TR, what="moe-W")
+    check(fp4, oracle, d["x"], MX, 0, what="moe-X")
+
+
+def test_training_recipe_small(fp4, oracle):
+    d = inputs.training(n=256)
+    check(fp4, oracle, d["w"], NV, FOS | B2D, what="train-W")
+    check(fp4, oracle, d["w"], NV, FOS | B2D | TR, what="train-WT")
+    check(fp4, oracle, d["grad"], NV, FOS | SR, seed=d["sr_seed"], offset=d["sr_offset"], what="train-G")
+
+
+def test_rht_recipe_small(fp4, oracle):
+    d = inputs.rht_activation(m=100, k=256, n=160)
+    check(fp4, oracle, d["x"], NV, FOS | RHT, signs=d["signs"], what="rht-X")
+    check(fp4, oracle, d["w"], NV, FOS | RHT | TR, signs=d["signs"], what="rht-WT")
+
+
+def test_supplied_amax_matches_computed(fp4, oracle):
+    x = mixed_matrix(64, 256, seed=77)
+    T = oracle.tensor_amax(oracle_input(x), 0)
+    check(fp4, oracle, x, NV, FOS, amax=[T], what="amax_in")
+    T2 = 3.0 * T  # a stale (delayed-scaling) amax is honoured as given
+    check(fp4, oracle, x, NV, FOS, amax=[T2], what="amax_in-stale")
+
+
+@pytest.mark.parametrize("kind", ["zeros", "tiny", "huge", "single"])
+def test_edge_values(fp4, oracle, kind):
+    x = torch.zeros(32, 128)
+    if kind == "tiny":
+        x = torch.randn(32, 128) * 1e-36  # tensor scale would underflow: S_t = 1
+    elif kind == "huge":
+        x = torch.randn(32, 128) * 1e37
+        x[0, 0] = 3.0e38
+    elif kind == "single":
+        x[5, 77] = -3.0
+    for fmt, flags in [(MX, 0), (NV, 0), (NV, FOS), (NV, FOS | B2D), (NV, TR | FOS)]:
+        check(fp4, oracle, x, fmt, flags, what=kind)
+
+
+def test_empty_is_noop(fp4):
+    x = torch.zeros(0, 64, dtype=torch.bfloat16, device="cuda")
+    q = fp4.quantize(x, "nvfp4")
+    assert q.codes.shape == (0, 32)
+
+
+def test_deterministic(fp4):
+    d = inputs.training(n=512, device="cuda")
+    a = fp4.quantize(d["grad"], "nvfp4", four_over_six=True, stochastic=True, seed=4)
+    b = fp4.quantize(d["grad"], "nvfp4", four_over_six=True, stochastic=True, seed=4)
+    assert torch.equal(a.codes, b.codes) and torch.equal(a.scales, b.scales)
+    c = fp4.quantize(d["grad"], "nvfp4", four_over_six=True, stochastic=True, seed=5)
+    assert not torch.equal(a.codes, c.codes)
+
+
+@pytest.mark.parametrize("fmt,flags", [(MX, 0), (NV, 0), (NV, FOS), (NV, FOS | RHT)])
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_dequantize_parity(fp4, oracle, fmt, flags, out):
+    x = mixed_matrix(130, 320, seed=9)
+    q = fp4.quantize(x.cuda(), fmt, four_over_six=bool(flags & FOS), hadamard=bool(flags & RHT), rht_signs=0xBEEF)
+    y = fp4.dequantize(q, out).cpu()
+    r = oracle.quantize(oracle_input(x), fmt, flags=flags, rht_signs=0xBEEF)
+    want = torch.from_numpy(oracle.dequantize(fmt, r["codes"], r["scales"], r["tensor_scale"]))
+    want = want.to(out)
+    assert torch.equal(y.view(torch.int16 if out == torch.bfloat16 else torch.int32),
+                       want.view(torch.int16 if out == torch.bfloat16 else torch.int32))
+
+
+# ---------------------------------------------------------------------------
+# full sizes, in the benchmark's launch configurations, on sampled outputs
+# ---------------------------------------------------------------------------
+def sampled_rows(F, O, x_dev, fmt, flags, signs=0, seed=0, offset=0, n=6, what=""):
+    """Quantize the whole tensor on the GPU; recompute a sample of output rows
+    (16-row tiles under 2D) with the oracle, using the full tensor's amax."""
+    print(f"[full] {what} {tuple(x_dev.shape)} flags={flag_str(flags)}", flush=True)
+    q, gc, gs, gt = gpu_quantize(F, x_dev, fmt, flags, signs, seed, offset)
+    x_cpu = x_dev.cpu()
+    x3 = x_cpu.unsqueeze(0) if x_cpu.dim() == 2 else x_cpu
+    B, rows, cols = x3.shape
+    R, C = (cols, rows) if flags & TR else (rows, cols)
+    rng = np.random.default_rng(0)
+    for b in sorted(set(rng.integers(0, B, 2).tolist())):
+        T = None
+        if fmt == NV:
+            T = O.tensor_amax(oracle_input(x3[b]), flags & (TR | RHT), signs)
+            assert gt[b] == np.float32(O.nvfp4_tensor_scale(T, bool(flags & FOS)))
+        step = 16
+        starts = sorted(set((rng.integers(0, R // step, n) * step).tolist())) + [R - step]
+        for r0 in starts:
+            r1 = r0 + step
+            part = x3[b][:, r0:r1] if flags & TR else x3[b][r0:r1]
+            sub = O.quantize(oracle_input(part.contiguous()), fmt, flags=flags, rht_signs=signs, seed=seed, offset=offset, amax=T,
+                             L0=(b * R + r0) * C)
+            assert_codes_equal(gc[b, r0:r1], sub["codes"], f"{what} rows {r0}:{r1}")
+            assert_codes_equal(gs[b, r0:r1], sub["scales"], f"{what} scales rows {r0}:{r1}")
+
+
+def test_full_w4a4(fp4, oracle):
+    d = inputs.w4a4_linear(device="cuda")
+    sampled_rows(fp4, oracle, d["a"], NV, FOS, what="A 2048x4096")
+    sampled_rows(fp4, oracle, d["w"], NV, FOS, what="W 4096x4096")
+
+
+def test_full_moe(fp4, oracle):
+    d = inputs.moe_mxfp4(device="cuda")
+    sampled_rows(fp4, oracle, d["w"], MX, TR, what="W 32x2880x5760^T")
+    sampled_rows(fp4, oracle, d["x"], MX, 0, what="X 32x512x2880")
+
+
+def test_full_training(fp4, oracle):
+    d = inputs.training(device="cuda")
+    sampled_rows(fp4, oracle, d["w"], NV, FOS | B2D, what="W 8192^2 2D")
+    sampled_rows(fp4, oracle, d["w"], NV, FOS | B2D | TR, what="W^T 8192^2 2D")
+    sampled_rows(fp4, oracle, d["grad"], NV, FOS | SR, seed=d["sr_seed"], offset=d["sr_offset"], what="G 8192^2 SR")
+
+
+def test_full_rht(fp4, oracle):
+    d = inputs.rht_activation(device="cuda")
+    sampled_rows(fp4, oracle, d["x"], NV, FOS | RHT, signs=d["signs"], what="X 16384x4096 RHT")
+    sampled_rows(fp4, oracle, d["w"], NV, FOS | RHT | TR, signs=d["signs"], what="W^T 12288x4096 RHT")
