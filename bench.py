@@ -1,0 +1,350 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-scaled FP4 hot path on one MI355X.
+
+A step is one pass of the workload's whole path over one batch of seeded
+synthetic input already resident in HBM. The default workload is the W4A4
+linear layer: NVFP4 four-over-six quantization of the activations
+[2048, 4096] and of the weight [4096, 4096] (each with its tensor-amax
+pre-pass), then the NVFP4 GEMM to a [2048, 4096] bf16 output.
+
+Timing: W untimed warm-up steps, then K steps between two device
+synchronisations, with HIP events (torch.cuda.Event on the stream the kernels
+run on) around the whole region and around every op inside it. Inputs rotate
+over enough copies (>= 600 MB) that the 256 MB Infinity Cache cannot serve
+them from one step to the next.
+
+Output: one JSON line. `value` is the step's roofline time (sum over its ops
+of algorithmic bytes / 8 TB/s for codec scans, flops / dense matrix peak for
+the GEMM) as a percentage of the measured step time. `roofline` describes the
+op that takes most of the step; `kernels` lists every op. `cpu_baseline`
+times the CPU oracle on a bounded sample of the same workload (single
+thread), scaled to the full step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME|all]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+import torch
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "FP4 quantize GB/s + W4A4 GEMM TFLOPS, each as % of MI355X roofline"
+PEAK_HBM_GBS = 8000.0                       # MI355X HBM3E
+PEAK_TFLOPS = {"bf16": 2500.0, "fp4": 10100.0}  # dense matrix-core peaks
+ROTATE_BYTES = 600 << 20
+
+
+class Op:
+    """One library call in the step: `launch(i)` enqueues it for input set i."""
+
+    def __init__(self, name, kernel, bound, work, peak, launch, unit):
+        self.name, self.kernel, self.bound, self.work, self.peak = name, kernel, bound, work, peak
+        self.launch, self.unit = launch, unit
+        self.durations = []
+
+    def roofline_seconds(self):
+        return self.work / (self.peak * 1e9 if self.unit == "GB/s" else self.peak * 1e12)
+
+
+def quant_bytes(elems_in, in_bytes, blk, nv, batch=1):
+    return elems_in * in_bytes + elems_in // 2 + elems_in // blk + (4 * batch if nv else 0)
+
+
+class QuantCall:
+    """Preallocated fp4_quantize call over `sets` input copies."""
+
+    def __init__(self, F, xs, fmt, flags=0, signs=0, seed=0, offset=0):
+        self.F, self.xs = F, xs
+        x = xs[0]
+        x3 = x if x.dim() == 3 else x.unsqueeze(0)
+        self.batch, self.rows, self.cols = x3.shape
+        tr = bool(flags & F.FP4_TRANSPOSE)
+        R, C = (self.cols, self.rows) if tr else (self.rows, self.cols)
+        self.R, self.C = R, C
+        self.blk = 16 if fmt == F.FP4_NVFP4 else 32
+        dev = x.device
+        self.opts = F.make_opts(fmt, flags, signs, seed, offset)
+        self.codes = torch.empty((self.batch, R, C // 2), dtype=torch.uint8, device=dev)
+        self.scales = torch.empty((self.batch, R, C // self.blk), dtype=torch.uint8, device=dev)
+        self.ts = torch.empty((self.batch,), dtype=torch.float32, device=dev)
+        self.ws_bytes = F.fp4_quantize_workspace(self.batch, self.rows, self.cols, self.opts)
+        self.ws = torch.empty((max(self.ws_bytes, 16),), dtype=torch.uint8, device=dev)
+        self.dt = F.FP4_BF16 if x.dtype == torch.bfloat16 else F.FP4_F32
+        self.nv = fmt == F.FP4_NVFP4
+        self.fmt = fmt
+        self.stream = torch.cuda.current_stream().cuda_stream
+        self.lib = F.lib()
+        self.opts_ref = ctypes.byref(self.opts)
+
+    def __call__(self, i):
+        x = self.xs[i % len(self.xs)]
+        st = self.lib.fp4_quantize(x.data_ptr(), self.dt, self.batch, self.rows, self.cols, self.cols,
+                                   self.rows * self.cols, self.opts_ref, self.codes.data_ptr(), self.C // 2,
+                                   self.R * (self.C // 2), self.scales.data_ptr(), self.C // self.blk,
+                                   self.R * (self.C // self.blk), self.ts.data_ptr(), self.ws.data_ptr(),
+                                   self.ws_bytes, self.stream)
+        if st != 0:
+            raise RuntimeError(f"fp4_quantize: {self.F.fp4_status_str(st)}")
+
+    def bytes(self):
+        return quant_bytes(self.batch * self.rows * self.cols, 2 if self.dt == self.F.FP4_BF16 else 4, self.blk,
+                           self.nv, self.batch)
+
+    def quantized(self):
+        return self.F.Quantized(self.fmt, self.codes, self.scales, self.ts if self.nv else None)
+
+
+class GemmCall:
+    def __init__(self, F, qa, qb, out_dtype=torch.bfloat16):
+        self.F, self.lib = F, F.lib()
+        self.a, self.b = qa.quantized(), qb.quantized()
+        self.G, self.M, half = self.a.codes.shape
+        self.N = self.b.codes.shape[1]
+        self.K = half * 2
+        self.c = torch.empty((self.G, self.M, self.N), dtype=out_dtype, device=self.a.codes.device)
+        self.ct = F.FP4_BF16 if out_dtype == torch.bfloat16 else F.FP4_F32
+        self.stream = torch.cuda.current_stream().cuda_stream
+        a, b = self.a, self.b
+        self.args = (a.fmt, self.G, self.M, self.N, self.K, a.codes.data_ptr(), half, self.M * half,
+                     a.scales.data_ptr(), a.scales.shape[-1], self.M * a.scales.shape[-1],
+                     a.tensor_scale.data_ptr() if a.tensor_scale is not None else None,
+                     b.codes.data_ptr(), half, self.N * half, b.scales.data_ptr(), b.scales.shape[-1],
+                     self.N * b.scales.shape[-1], b.tensor_scale.data_ptr() if b.tensor_scale is not None else None,
+                     self.c.data_ptr(), self.ct, self.N, self.M * self.N, self.stream)
+
+    def __call__(self, i):
+        st = self.lib.fp4_gemm(*self.args)
+        if st != 0:
+            raise RuntimeError(f"fp4_gemm: {self.F.fp4_status_str(st)}")
+
+    def flops(self):
+        return 2.0 * self.G * self.M * self.N * self.K
+
+
+def n_sets(bytes_per_set):
+    return max(2, -(-ROTATE_BYTES // max(bytes_per_set, 1)))
+
+
+def copies(t, n):
+    return [t] + [t.clone() for _ in range(n - 1)]
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+def wl_w4a4_linear(F, inputs):
+    d = inputs.w4a4_linear(device="cuda")
+    n = n_sets(d["a"].numel() * 2 + d["w"].numel() * 2)
+    qa = QuantCall(F, copies(d["a"], n), F.FP4_NVFP4, F.FP4_FOUR_OVER_SIX)
+    qw = QuantCall(F, copies(d["w"], n), F.FP4_NVFP4, F.FP4_FOUR_OVER_SIX)
+    gm = GemmCall(F, qa, qw, torch.bfloat16)
+    ops = [Op("quantize A nvfp4 4/6 (amax pre-pass + quantize)", "amax_kernel+quant_rows_kernel", "hbm", qa.bytes(),
+              PEAK_HBM_GBS, qa, "GB/s"),
+           Op("quantize W nvfp4 4/6 (amax pre-pass + quantize)", "amax_kernel+quant_rows_kernel", "hbm", qw.bytes(),
+              PEAK_HBM_GBS, qw, "GB/s"),
+           Op("gemm nvfp4 (exact bf16 dequant + bf16 MFMA)", "gemm_kernel<true, true>", "mfma", gm.flops(),
+              PEAK_TFLOPS["bf16"], gm, "TFLOP/s")]
+    cfg = {"workload": "w4a4_linear_nvfp4_four_over_six", "M": 2048, "N": 4096, "K": 4096,
+           "activations": "2048x4096 bf16 N(0,1), 1% columns x30", "weight": "4096x4096 bf16 N(0,0.02)",
+           "output": "bf16", "input_sets_rotated": n}
+    return ops, cfg, "nvfp4 e2m1/e4m3, bf16 MFMA fp32-acc", lambda: cpu_w4a4(d)
+
+
+def wl_moe(F, inputs):
+    d = inputs.moe_mxfp4(device="cuda")
+    n = n_sets(d["w"].numel() * 2 + d["x"].numel() * 2)
+    qw = QuantCall(F, copies(d["w"], n), F.FP4_MXFP4, F.FP4_TRANSPOSE)
+    qx = QuantCall(F, copies(d["x"], n), F.FP4_MXFP4, 0)
+    gm = GemmCall(F, qx, qw, torch.bfloat16)
+    ops = [Op("quantize W^T mxfp4 32x[2880x5760]", "quant_cols_kernel", "hbm", qw.bytes(), PEAK_HBM_GBS, qw, "GB/s"),
+           Op("quantize X mxfp4 32x[512x2880]", "quant_rows_kernel", "hbm", qx.bytes(), PEAK_HBM_GBS, qx, "GB/s"),
+           Op("grouped gemm mxfp4 (scaled FP4 MFMA)", "gemm_kernel<false, true>", "mfma", gm.flops(),
+              PEAK_TFLOPS["fp4"], gm, "TFLOP/s")]
+    cfg = {"workload": "moe_mxfp4_grouped", "experts": 32, "M": 512, "N": 5760, "K": 2880, "output": "bf16",
+           "input_sets_rotated": n}
+    return ops, cfg, "mxfp4 e2m1/e8m0, fp4 MFMA fp32-acc", None
+
+
+def wl_training(F, inputs):
+    d = inputs.training(device="cuda")
+    n = n_sets(d["w"].numel() * 4)
+    ws, gs = copies(d["w"], n), copies(d["grad"], n)
+    f = F.FP4_FOUR_OVER_SIX | F.FP4_BLOCK2D
+    q1 = QuantCall(F, ws, F.FP4_NVFP4, f)
+    q2 = QuantCall(F, ws, F.FP4_NVFP4, f | F.FP4_TRANSPOSE)
+    q3 = QuantCall(F, gs, F.FP4_NVFP4, F.FP4_FOUR_OVER_SIX | F.FP4_STOCHASTIC, seed=d["sr_seed"])
+    ops = [Op("quantize W nvfp4 2D 4/6", "quant_rows_kernel", "hbm", q1.bytes(), PEAK_HBM_GBS, q1, "GB/s"),
+           Op("quantize W^T nvfp4 2D 4/6", "quant_cols_kernel", "hbm", q2.bytes(), PEAK_HBM_GBS, q2, "GB/s"),
+           Op("quantize G nvfp4 4/6 stochastic", "quant_rows_kernel", "hbm", q3.bytes(), PEAK_HBM_GBS, q3, "GB/s")]
+    cfg = {"workload": "training_quantize_8192", "shape": [8192, 8192], "input_sets_rotated": n}
+    return ops, cfg, "nvfp4 e2m1/e4m3", None
+
+
+def wl_rht(F, inputs):
+    d = inputs.rht_activation(device="cuda")
+    n = n_sets(d["x"].numel() * 2 + d["w"].numel() * 2)
+    f = F.FP4_FOUR_OVER_SIX | F.FP4_HADAMARD
+    qx = QuantCall(F, copies(d["x"], n), F.FP4_NVFP4, f, signs=d["signs"])
+    qw = QuantCall(F, copies(d["w"], n), F.FP4_NVFP4, f | F.FP4_TRANSPOSE, signs=d["signs"])
+    gm = GemmCall(F, qx, qw, torch.bfloat16)
+    ops = [Op("quantize X nvfp4 4/6 RHT", "quant_rows_kernel", "hbm", qx.bytes(), PEAK_HBM_GBS, qx, "GB/s"),
+           Op("quantize W^T nvfp4 4/6 RHT", "quant_cols_kernel", "hbm", qw.bytes(), PEAK_HBM_GBS, qw, "GB/s"),
+           Op("gemm nvfp4", "gemm_kernel<true, true>", "mfma", gm.flops(), PEAK_TFLOPS["bf16"], gm, "TFLOP/s")]
+    cfg = {"workload": "rht_activation_nvfp4", "M": 16384, "N": 12288, "K": 4096, "input_sets_rotated": n}
+    return ops, cfg, "nvfp4 e2m1/e4m3, bf16 MFMA fp32-acc", None
+
+
+WORKLOADS = {"w4a4_linear": wl_w4a4_linear, "moe": wl_moe, "training": wl_training, "rht": wl_rht}
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle, untuned, single thread, bounded sample
+# ---------------------------------------------------------------------------
+def cpu_w4a4(d):
+    from threadpoolctl import threadpool_limits
+
+    from block_scaled_fp4_amax_amd import inputs
+    from oracle import oracle as O
+    a = inputs.bf16_bits(d["a"].cpu())
+    w = inputs.bf16_bits(d["w"].cpu())
+    M, K = a.shape
+    N = w.shape[0]
+    rows = 128
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        qa = O.quantize(a, O.NVFP4, flags=O.FOUR_OVER_SIX)
+        t1 = time.perf_counter()
+        qw = O.quantize(w, O.NVFP4, flags=O.FOUR_OVER_SIX)
+        t2 = time.perf_counter()
+        da = O.dequantize(O.NVFP4, qa["codes"][:rows], qa["scales"][:rows], qa["tensor_scale"])
+        dw = O.dequantize(O.NVFP4, qw["codes"], qw["scales"], qw["tensor_scale"])
+        O.gemm_reference(da, dw)
+        t3 = time.perf_counter()
+    t_step = (t1 - t0) + (t2 - t1) + (t3 - t2) * (M / rows)
+    return {"seconds_measured": t3 - t0, "step_seconds_extrapolated": t_step,
+            "sample": f"oracle NVFP4 4/6 quantize of all of A [{M},{K}] and W [{N},{K}] "
+                      f"(incl. tensor amax), dequantize + float64 matmul of {rows} of {M} output rows, "
+                      f"scaled by {M // rows} to the full GEMM",
+            "quantize_GBps": (quant_bytes(M * K, 2, 16, True) + quant_bytes(N * K, 2, 16, True)) / (t2 - t0) / 1e9,
+            "gemm_GFLOPs": 2.0 * rows * N * K / (t3 - t2) / 1e9}
+
+
+# ---------------------------------------------------------------------------
+def source_digest():
+    h = hashlib.sha256()
+    for p in sorted((ROOT / "block_scaled_fp4_amax_amd" / "csrc").iterdir()):
+        h.update(p.read_bytes())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(op_kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    p = ROOT / "profiles" / "hbm_traffic.json"
+    if not p.exists():
+        return None
+    try:
+        t = json.loads(p.read_text())
+    except ValueError:
+        return None
+    if t.get("source_digest") != source_digest():
+        return None
+    e = t.get("workloads", {}).get(workload, {}).get(op_kernel)
+    return e.get("bytes_per_launch") if e else None
+
+
+def run(workload, steps, warmup, with_cpu):
+    import block_scaled_fp4_amax_amd as F
+    from block_scaled_fp4_amax_amd import inputs
+    F.lib()
+    torch.manual_seed(0)
+    ops, cfg, dtype, cpu_fn = WORKLOADS[workload](F, inputs)
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        for op in ops:
+            op.launch(i)
+    torch.cuda.synchronize()
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ops]
+           for _ in range(steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(steps):
+        for j, op in enumerate(ops):
+            evs[i][j][0].record()
+            op.launch(i)
+            evs[i][j][1].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / steps
+    kernels = []
+    roof_s = 0.0
+    for j, op in enumerate(ops):
+        d = [evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(steps)]
+        avg_ms = float(np.mean(d))
+        achieved = op.work / (avg_ms * 1e-3) / (1e9 if op.unit == "GB/s" else 1e12)
+        traffic = traffic_for(op.kernel, workload)
+        kernels.append({"op": op.name, "kernel": op.kernel, "bound": op.bound, "avg_ms": round(avg_ms, 5),
+                        "achieved": round(achieved, 2), "peak": op.peak, "unit": op.unit,
+                        "frac": round(achieved / op.peak, 4), "work_per_launch": op.work,
+                        "traffic": traffic})
+        roof_s += op.roofline_seconds()
+    dom = max(kernels, key=lambda k: k["avg_ms"])
+    value = 100.0 * roof_s / (ms_step * 1e-3)
+    line = {"metric": METRIC, "value": round(value, 2), "unit": "% of roofline (step)", "n_gpus": 1,
+            "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+            "data": "synthetic (seeded generators; no dataset or trained weights)", "config": cfg,
+            "roofline": {"bound": dom["bound"], "achieved": dom["achieved"], "peak": dom["peak"],
+                         "unit": dom["unit"], "frac": dom["frac"], "traffic": dom["traffic"],
+                         "kernel": dom["kernel"]},
+            "kernels": kernels}
+    if with_cpu and cpu_fn is not None:
+        c = cpu_fn()
+        line["cpu_baseline"] = {"value": round(100.0 * roof_s / c["step_seconds_extrapolated"], 6),
+                                "unit": "% of roofline (step)", "cores": 1, "kind": "oracle",
+                                "sample": c["sample"], "step_seconds": round(c["step_seconds_extrapolated"], 3),
+                                "quantize_GBps": round(c["quantize_GBps"], 4),
+                                "gemm_GFLOPs": round(c["gemm_GFLOPs"], 3),
+                                "host": f"{os.cpu_count()} logical CPUs visible"}
+    else:
+        line["cpu_baseline"] = None
+    return line
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="w4a4_linear", choices=[*WORKLOADS, "all"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the multi-GPU sharding is described in DESIGN.md but not built", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    names = list(WORKLOADS) if args.workload == "all" else [args.workload]
+    for nm in names:
+        line = run(nm, args.steps, args.warmup, with_cpu=not args.no_cpu_baseline)
+        print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
