@@ -44,6 +44,25 @@ fp4_status check_device() {
   return ok ? FP4_OK : FP4_ERR_DEVICE;
 }
 
+std::atomic<int> g_cu_count[64];
+
+}  // namespace
+
+int fp4impl::device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    int c = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < 64) g_cu_count[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+namespace {
+
 struct QuantPlan {
   int64_t R = 0, C = 0;
   int blk = 0;
@@ -235,8 +254,19 @@ fp4_status fp4_gemm(int32_t format, int64_t groups, int64_t M, int64_t N, int64_
                      b_scales_group_stride < 0 || c_group_stride < (M - 1) * ldc + N))
     return FP4_ERR_INVALID;
   if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || lda % 16 != 0 || ldb % 16 != 0) return FP4_ERR_ALIGN;
+  // per-group operand panels are addressed with 32-bit offsets
+  if (M * lda >= (int64_t(1) << 31) || N * ldb >= (int64_t(1) << 31) || M * lda_scales >= (int64_t(1) << 31) ||
+      N * ldb_scales >= (int64_t(1) << 31))
+    return FP4_ERR_UNSUPPORTED;
   if (groups > 1 && (a_group_stride % 16 != 0 || b_group_stride % 16 != 0)) return FP4_ERR_ALIGN;
   if (!aligned(c, c_dtype == FP4_BF16 ? 2 : 4)) return FP4_ERR_ALIGN;
+  {
+    // scales are read two (MXFP4) or four (NVFP4) bytes at a time
+    const int64_t sa = nv ? 4 : 2;
+    if (!aligned(a_scales, sa) || !aligned(b_scales, sa) || lda_scales % sa != 0 || ldb_scales % sa != 0 ||
+        (groups > 1 && (a_scales_group_stride % sa != 0 || b_scales_group_stride % sa != 0)))
+      return FP4_ERR_ALIGN;
+  }
   if (nv && (!aligned(a_tensor_scale, 4) || !aligned(b_tensor_scale, 4))) return FP4_ERR_ALIGN;
   fp4_status st = check_device();
   if (st != FP4_OK) return st;
@@ -264,6 +294,10 @@ fp4_status fp4_gemm(int32_t format, int64_t groups, int64_t M, int64_t N, int64_
   g.c_bf16 = c_dtype == FP4_BF16;
   g.ldc = ldc;
   g.c_gs = groups > 1 ? c_group_stride : 0;
+  {
+    const int64_t es = c_dtype == FP4_BF16 ? 2 : 4;
+    g.c_vec_ok = aligned(c, 16) && (ldc * es) % 16 == 0 && (groups == 1 || (c_group_stride * es) % 16 == 0);
+  }
   (void)hipGetLastError();
   return launch_gemm(g, static_cast<hipStream_t>(stream)) == hipSuccess ? FP4_OK : FP4_ERR_HIP;
 }

@@ -72,8 +72,12 @@ struct GemmArgs {
   void* c;
   bool c_bf16;
   int64_t ldc, c_gs;
+  bool c_vec_ok;  // C and its row / group pitches are 16-byte aligned
 };
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream);
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
 
 }  // namespace fp4impl

@@ -170,7 +170,10 @@ fp4_status fp4_dequantize(int32_t format, int64_t batch, int64_t rows, int64_t c
  *   Strides: lda, ldb in bytes (>= K/2, multiples of 16); lda_scales,
  *   ldb_scales in bytes (>= K/blk); ldc and group strides of C in elements;
  *   group strides of codes/scales in bytes. K % 64 == 0; M and N arbitrary
- *   (>= 0). Code pointers 16-byte
+ *   (>= 0). Scale pointers and strides (lda_scales, ldb_scales and the scale
+ *   group strides) must be multiples of 2 (MXFP4) or 4 (NVFP4): scales are
+ *   read two or four bytes at a time. Each group's code and scale panels
+ *   must span less than 2 GiB (else FP4_ERR_UNSUPPORTED). Code pointers 16-byte
  *   aligned; c 4-byte aligned.
  */
 fp4_status fp4_gemm(int32_t format, int64_t groups, int64_t M, int64_t N, int64_t K,
