@@ -8,10 +8,10 @@
 //                      16x16 tile (16 lanes).
 //   quant_cols_kernel  transposed input: blocks run down the columns of X.
 //                      One lane owns a 16-row x 8-column patch (sixteen
-//                      16-byte row loads, so a wave reads 32 rows x 256
-//                      columns with 1 KiB-contiguous accesses) = eight blocks,
-//                      one per source column; an MXFP4 block is a vertical
-//                      lane pair, a 16x16 tile a horizontal one.
+//                      16-byte row loads) = eight blocks, one per source
+//                      column; an MXFP4 block is a vertical lane pair, a
+//                      16x16 tile a horizontal one. Output goes through LDS
+//                      so each output row is written as whole lines.
 //
 // The method is stated in quant_common.h.
 #include "quant_common.h"
@@ -45,30 +45,47 @@ __global__ __launch_bounds__(256) void amax_kernel(QuantArgs a) {
   else { per_row = cols / 8; units = (rows / 16) * per_row; }
   float m = 0.0f;
   const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < units; u += stride) {
-    int64_t r = u / per_row, c = u - r * per_row;
-    if (MODE == kAmaxPlain) {
-      float v[8];
-      load8<TIn>(x + r * a.ld_x + c * 8, v);
+  if constexpr (MODE == kAmaxPlain) {
+    // four 16-byte loads in flight per lane
+    for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < units; u += 4 * stride) {
+      float v[4][8];
 #pragma unroll
-      for (int i = 0; i < 8; i++) m = __builtin_fmaxf(m, __builtin_fabsf(v[i]));
-    } else if (MODE == kAmaxRhtRows) {
-      float v[16];
-      load8<TIn>(x + r * a.ld_x + c * 16, v);
-      load8<TIn>(x + r * a.ld_x + c * 16 + 8, v + 8);
-      rht16(v, a.signs);
-      m = __builtin_fmaxf(m, max_abs16(v));
-    } else {
-      float t[16][8];
+      for (int k = 0; k < 4; k++) {
+        const int64_t uk = u + k * stride;
+        if (uk < units) {
+          const int64_t r = uk / per_row, c = uk - r * per_row;
+          load8<TIn>(x + r * a.ld_x + c * 8, v[k]);
+        } else {
 #pragma unroll
-      for (int i = 0; i < 16; i++) load8<TIn>(x + (r * 16 + i) * a.ld_x + c * 8, t[i]);
+          for (int i = 0; i < 8; i++) v[k][i] = 0.0f;
+        }
+      }
 #pragma unroll
-      for (int j = 0; j < 8; j++) {
+      for (int k = 0; k < 4; k++)
+#pragma unroll
+        for (int i = 0; i < 8; i++) m = __builtin_fmaxf(m, __builtin_fabsf(v[k][i]));
+    }
+  } else {
+    for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < units; u += stride) {
+      const int64_t r = u / per_row, c = u - r * per_row;
+      if constexpr (MODE == kAmaxRhtRows) {
         float v[16];
-#pragma unroll
-        for (int i = 0; i < 16; i++) v[i] = t[i][j];
+        load8<TIn>(x + r * a.ld_x + c * 16, v);
+        load8<TIn>(x + r * a.ld_x + c * 16 + 8, v + 8);
         rht16(v, a.signs);
         m = __builtin_fmaxf(m, max_abs16(v));
+      } else {
+        float t[16][8];
+#pragma unroll
+        for (int i = 0; i < 16; i++) load8<TIn>(x + (r * 16 + i) * a.ld_x + c * 8, t[i]);
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+          float v[16];
+#pragma unroll
+          for (int i = 0; i < 16; i++) v[i] = t[i][j];
+          rht16(v, a.signs);
+          m = __builtin_fmaxf(m, max_abs16(v));
+        }
       }
     }
   }
@@ -187,8 +204,51 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(QuantArgs a) {
 // ------------------------------------------------------------------------
 // Transposed quantization (output = Q(X^T))
 // ------------------------------------------------------------------------
+// A workgroup takes 256 source rows (k) x 128 source columns (n). Lane
+// (wave w, g = lane / 2, h = lane % 2) owns the 16 x 8 patch at
+// k = 64 w + 32 (g / 16) + 16 h, n = 8 (g % 16): sixteen 16-byte row loads.
+// Its eight 16-value blocks (one per source column) land in an LDS image of
+// the workgroup's output, 128 rows of 128 code bytes plus their scale bytes,
+// which the workgroup then stores with consecutive lanes along each output
+// row, so every output row gets one whole 128-byte line per workgroup.
+constexpr int kColsK = 256, kColsN = 128;
+constexpr int kColsPitch = kColsK / 2 + 8;  // staged code row, padded (bytes)
+constexpr int kColsScales = kColsK / 16;    // staged scale bytes per row (NVFP4; MXFP4 uses half)
+
+template <typename TIn>
+struct Patch16x8;
+template <>
+struct Patch16x8<uint16_t> {
+  uint4 r[16];
+  __device__ __forceinline__ void load(const uint16_t* p, int64_t ld) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) r[i] = *reinterpret_cast<const uint4*>(p + i * ld);
+  }
+  __device__ __forceinline__ float get(int i, int j) const {
+    const uint32_t w = (j >> 1) == 0 ? r[i].x : (j >> 1) == 1 ? r[i].y : (j >> 1) == 2 ? r[i].z : r[i].w;
+    return (j & 1) ? bf16_hi(w) : bf16_lo(w);
+  }
+};
+template <>
+struct Patch16x8<float> {
+  float4 r[16][2];
+  __device__ __forceinline__ void load(const float* p, int64_t ld) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      r[i][0] = reinterpret_cast<const float4*>(p + i * ld)[0];
+      r[i][1] = reinterpret_cast<const float4*>(p + i * ld)[1];
+    }
+  }
+  __device__ __forceinline__ float get(int i, int j) const {
+    const float4& f = r[i][j >> 2];
+    return (j & 3) == 0 ? f.x : (j & 3) == 1 ? f.y : (j & 3) == 2 ? f.z : f.w;
+  }
+};
+
 template <typename TIn, bool NV, bool FOS, bool B2D, bool SR, bool RHT>
 __global__ __launch_bounds__(256) void quant_cols_kernel(QuantArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t cst[kColsN * kColsPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t sst[kColsN * kColsScales];
   const int64_t b = blockIdx.z;
   float St = 1.0f, k6 = 0.0f, k4 = 0.0f;
   if constexpr (NV) {
@@ -198,132 +258,155 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(QuantArgs a) {
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane & 1, g = lane >> 1;
-  const int64_t n0 = (int64_t)blockIdx.x * 256 + g * 8;                 // source columns n0..n0+7
-  const int64_t k0 = (int64_t)blockIdx.y * 128 + wave * 32 + h * 16;    // source rows k0..k0+15
-  if (n0 >= a.src_cols || k0 >= a.src_rows) return;
+  const int nl = (g & 15) * 8;                         // patch columns, workgroup-relative
+  const int kl = wave * 64 + (g >> 4) * 32 + h * 16;   // patch rows, workgroup-relative
+  const int64_t nb = (int64_t)blockIdx.x * kColsN, kb = (int64_t)blockIdx.y * kColsK;
+  const int64_t n0 = nb + nl, k0 = kb + kl;
+  // A vertical lane pair (an MXFP4 block) and a horizontal one (a 16 x 16
+  // tile) are valid together: rows come in whole blocks, columns in whole
+  // tiles.
+  if (n0 < a.src_cols && k0 < a.src_rows) {
+    Patch16x8<TIn> t;
+    t.load(reinterpret_cast<const TIn*>(a.x) + b * a.bs_x + k0 * a.ld_x + n0, a.ld_x);
+    const uint64_t Lrow = (uint64_t)b * (uint64_t)a.R;
+    uint8_t* crow = cst + nl * kColsPitch + (kl >> 1);
+    uint8_t* srow = sst + nl * kColsScales;
 
-  const TIn* xp = reinterpret_cast<const TIn*>(a.x) + b * a.bs_x + k0 * a.ld_x + n0;
-  float t[16][8];
+    if constexpr (NV && B2D) {
+      // one 16x16 tile per horizontal lane pair (lanes g and g^1)
+      float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; i++) load8<TIn>(xp + i * a.ld_x, t[i]);
-
-  uint8_t* cbase = a.codes + b * a.bs_c + (k0 >> 1);
-  uint8_t* sbase = a.scales + b * a.bs_s;
-  const uint64_t Lrow = (uint64_t)b * (uint64_t)a.R;
-
-  if constexpr (NV && B2D) {
-    // one 16x16 tile per horizontal lane pair (lanes g and g^1)
-    float amax = 0.0f;
+      for (int i = 0; i < 16; i++)
 #pragma unroll
-    for (int i = 0; i < 16; i++)
+        for (int j = 0; j < 8; j++) amax = __builtin_fmaxf(amax, __builtin_fabsf(t.get(i, j)));
+      amax = __builtin_fmaxf(amax, xor_shfl<2>(amax));
+      NvCand c = nv_candidate(amax, k6, St);
+      if constexpr (FOS) {
+        NvCand c4 = nv_candidate(amax, k4, St);
+        // per source row: FMA chain over this lane's 8 columns, plus the
+        // partner's chain over the other 8 columns; then a pairwise tree over
+        // the 16 source rows
+        float p6[16], p4[16];
 #pragma unroll
-      for (int j = 0; j < 8; j++) amax = __builtin_fmaxf(amax, __builtin_fabsf(t[i][j]));
-    amax = __builtin_fmaxf(amax, xor_shfl<2>(amax));
-    NvCand c = nv_candidate(amax, k6, St);
-    if constexpr (FOS) {
-      NvCand c4 = nv_candidate(amax, k4, St);
-      // per source row: FMA chain over this lane's 8 columns, plus the
-      // partner's chain over the other 8 columns; then a pairwise tree over
-      // the 16 source rows
-      float p6[16], p4[16];
+        for (int i = 0; i < 16; i++) {
+          float q6[8], q4[8];
 #pragma unroll
-      for (int i = 0; i < 16; i++) {
-        float q6[8], q4[8];
+          for (int j = 0; j < 8; j++) {
+            q6[j] = t.get(i, j) * c.r;
+            q4[j] = t.get(i, j) * c4.r;
+          }
+          uint32_t w6 = e2m1_pack2<0>(0u, q6[0], q6[1]);
+          w6 = e2m1_pack2<1>(w6, q6[2], q6[3]);
+          w6 = e2m1_pack2<2>(w6, q6[4], q6[5]);
+          w6 = e2m1_pack2<3>(w6, q6[6], q6[7]);
+          uint32_t w4 = e2m1_pack2<0>(0u, q4[0], q4[1]);
+          w4 = e2m1_pack2<1>(w4, q4[2], q4[3]);
+          w4 = e2m1_pack2<2>(w4, q4[4], q4[5]);
+          w4 = e2m1_pack2<3>(w4, q4[6], q4[7]);
+          p6[i] = sq_chain8(q6, w6);
+          p4[i] = sq_chain8(q4, w4);
+          p6[i] = p6[i] + xor_shfl<2>(p6[i]);
+          p4[i] = p4[i] + xor_shfl<2>(p4[i]);
+        }
 #pragma unroll
-        for (int j = 0; j < 8; j++) { q6[j] = t[i][j] * c.r; q4[j] = t[i][j] * c4.r; }
-        uint32_t w6 = e2m1_pack2<0>(0u, q6[0], q6[1]);
-        w6 = e2m1_pack2<1>(w6, q6[2], q6[3]);
-        w6 = e2m1_pack2<2>(w6, q6[4], q6[5]);
-        w6 = e2m1_pack2<3>(w6, q6[6], q6[7]);
-        uint32_t w4 = e2m1_pack2<0>(0u, q4[0], q4[1]);
-        w4 = e2m1_pack2<1>(w4, q4[2], q4[3]);
-        w4 = e2m1_pack2<2>(w4, q4[4], q4[5]);
-        w4 = e2m1_pack2<3>(w4, q4[6], q4[7]);
-        p6[i] = sq_chain8(q6, w6);
-        p4[i] = sq_chain8(q4, w4);
-        p6[i] = p6[i] + xor_shfl<2>(p6[i]);
-        p4[i] = p4[i] + xor_shfl<2>(p4[i]);
+        for (int width = 1; width < 16; width <<= 1)
+#pragma unroll
+          for (int i = 0; i < 16; i += 2 * width) {
+            p6[i] = p6[i] + p6[i + width];
+            p4[i] = p4[i] + p4[i + width];
+          }
+        if (cand_error(c4, p4[0]) < cand_error(c, p6[0])) c = c4;
       }
 #pragma unroll
-      for (int width = 1; width < 16; width <<= 1)
-#pragma unroll
-        for (int i = 0; i < 16; i += 2 * width) {
-          p6[i] = p6[i] + p6[i + width];
-          p4[i] = p4[i] + p4[i + width];
-        }
-      if (cand_error(c4, p4[0]) < cand_error(c, p6[0])) c = c4;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-      const int64_t n = n0 + j;
-      float q[16];
-#pragma unroll
-      for (int i = 0; i < 16; i++) q[i] = t[i][j] * c.r;
-      uint32_t w0, w1;
-      if constexpr (SR) sr16(q, (Lrow + (uint64_t)n) * (uint64_t)a.C + (uint64_t)k0, a.seed, a.offset, w0, w1);
-      else pack16(q, w0, w1);
-      *reinterpret_cast<uint2*>(cbase + n * a.ld_c) = make_uint2(w0, w1);
-      sbase[n * a.ld_s + (k0 >> 4)] = (uint8_t)c.code;
-    }
-    return;
-  } else {
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-      const int64_t n = n0 + j;
-      float v[16];
-#pragma unroll
-      for (int i = 0; i < 16; i++) v[i] = t[i][j];
-      if constexpr (RHT) rht16(v, a.signs);
-      float amax = max_abs16(v);
-      const uint64_t L0 = (Lrow + (uint64_t)n) * (uint64_t)a.C + (uint64_t)k0;
-      uint32_t w0, w1, sbyte;
-      if constexpr (!NV) {
-        amax = __builtin_fmaxf(amax, xor_shfl<1>(amax));  // vertical lane pair = 32 rows
-        sbyte = e8m0_from_amax(amax);
-        if constexpr (SR) {
-          float q[16];
-#pragma unroll
-          for (int i = 0; i < 16; i++) q[i] = __builtin_ldexpf(v[i], 127 - (int)sbyte);
-          sr16(q, L0, a.seed, a.offset, w0, w1);
-        } else {
-          float sc = e8m0_scale_operand(sbyte);
-          w0 = e2m1_pack2_scaled<0>(0u, v[0], v[1], sc);
-          w0 = e2m1_pack2_scaled<1>(w0, v[2], v[3], sc);
-          w0 = e2m1_pack2_scaled<2>(w0, v[4], v[5], sc);
-          w0 = e2m1_pack2_scaled<3>(w0, v[6], v[7], sc);
-          w1 = e2m1_pack2_scaled<0>(0u, v[8], v[9], sc);
-          w1 = e2m1_pack2_scaled<1>(w1, v[10], v[11], sc);
-          w1 = e2m1_pack2_scaled<2>(w1, v[12], v[13], sc);
-          w1 = e2m1_pack2_scaled<3>(w1, v[14], v[15], sc);
-        }
-        if (h == 0) sbase[n * a.ld_s + (k0 >> 5)] = (uint8_t)sbyte;
-      } else {
-        NvCand c = nv_candidate(amax, k6, St);
+      for (int j = 0; j < 8; j++) {
         float q[16];
 #pragma unroll
-        for (int i = 0; i < 16; i++) q[i] = v[i] * c.r;
-        pack16(q, w0, w1);
-        if constexpr (FOS) {
-          NvCand c4 = nv_candidate(amax, k4, St);
-          float q4[16];
-#pragma unroll
-          for (int i = 0; i < 16; i++) q4[i] = v[i] * c4.r;
-          uint32_t x0, x1;
-          pack16(q4, x0, x1);
-          if (cand_error(c4, sq_sum16(q4, x0, x1)) < cand_error(c, sq_sum16(q, w0, w1))) {
-            c = c4;
-            w0 = x0;
-            w1 = x1;
-#pragma unroll
-            for (int i = 0; i < 16; i++) q[i] = q4[i];
-          }
-        }
-        if constexpr (SR) sr16(q, L0, a.seed, a.offset, w0, w1);
-        sbyte = c.code;
-        sbase[n * a.ld_s + (k0 >> 4)] = (uint8_t)sbyte;
+        for (int i = 0; i < 16; i++) q[i] = t.get(i, j) * c.r;
+        uint32_t w0, w1;
+        if constexpr (SR)
+          sr16(q, (Lrow + (uint64_t)(n0 + j)) * (uint64_t)a.C + (uint64_t)k0, a.seed, a.offset, w0, w1);
+        else
+          pack16(q, w0, w1);
+        *reinterpret_cast<uint2*>(crow + j * kColsPitch) = make_uint2(w0, w1);
+        srow[j * kColsScales + (kl >> 4)] = (uint8_t)c.code;
       }
-      *reinterpret_cast<uint2*>(cbase + n * a.ld_c) = make_uint2(w0, w1);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; i++) v[i] = t.get(i, j);
+        if constexpr (RHT) rht16(v, a.signs);
+        float amax = max_abs16(v);
+        const uint64_t L0 = (Lrow + (uint64_t)(n0 + j)) * (uint64_t)a.C + (uint64_t)k0;
+        uint32_t w0, w1;
+        if constexpr (!NV) {
+          amax = __builtin_fmaxf(amax, xor_shfl<1>(amax));  // vertical lane pair = 32 rows
+          const uint32_t sbyte = e8m0_from_amax(amax);
+          if constexpr (SR) {
+            float q[16];
+#pragma unroll
+            for (int i = 0; i < 16; i++) q[i] = __builtin_ldexpf(v[i], 127 - (int)sbyte);
+            sr16(q, L0, a.seed, a.offset, w0, w1);
+          } else {
+            const float sc = e8m0_scale_operand(sbyte);
+            w0 = e2m1_pack2_scaled<0>(0u, v[0], v[1], sc);
+            w0 = e2m1_pack2_scaled<1>(w0, v[2], v[3], sc);
+            w0 = e2m1_pack2_scaled<2>(w0, v[4], v[5], sc);
+            w0 = e2m1_pack2_scaled<3>(w0, v[6], v[7], sc);
+            w1 = e2m1_pack2_scaled<0>(0u, v[8], v[9], sc);
+            w1 = e2m1_pack2_scaled<1>(w1, v[10], v[11], sc);
+            w1 = e2m1_pack2_scaled<2>(w1, v[12], v[13], sc);
+            w1 = e2m1_pack2_scaled<3>(w1, v[14], v[15], sc);
+          }
+          if (h == 0) srow[j * kColsScales + (kl >> 5)] = (uint8_t)sbyte;
+        } else {
+          NvCand c = nv_candidate(amax, k6, St);
+          float q[16];
+#pragma unroll
+          for (int i = 0; i < 16; i++) q[i] = v[i] * c.r;
+          pack16(q, w0, w1);
+          if constexpr (FOS) {
+            NvCand c4 = nv_candidate(amax, k4, St);
+            float q4[16];
+#pragma unroll
+            for (int i = 0; i < 16; i++) q4[i] = v[i] * c4.r;
+            uint32_t x0, x1;
+            pack16(q4, x0, x1);
+            if (cand_error(c4, sq_sum16(q4, x0, x1)) < cand_error(c, sq_sum16(q, w0, w1))) {
+              c = c4;
+              w0 = x0;
+              w1 = x1;
+#pragma unroll
+              for (int i = 0; i < 16; i++) q[i] = q4[i];
+            }
+          }
+          if constexpr (SR) sr16(q, L0, a.seed, a.offset, w0, w1);
+          srow[j * kColsScales + (kl >> 4)] = (uint8_t)c.code;
+        }
+        *reinterpret_cast<uint2*>(crow + j * kColsPitch) = make_uint2(w0, w1);
+      }
     }
+  }
+  __syncthreads();
+
+  // Store the staged image: 8-byte chunks, 16 lanes per 128-byte output row.
+  const int nrows = (int)(a.src_cols - nb < kColsN ? a.src_cols - nb : kColsN);
+  const int kbytes = (int)(a.src_rows - kb < kColsK ? a.src_rows - kb : kColsK) / 2;
+  uint8_t* cout = a.codes + b * a.bs_c + nb * a.ld_c + (kb >> 1);
+#pragma unroll
+  for (int i = 0; i < (kColsN * kColsK / 2) / (8 * 256); i++) {
+    const int c = threadIdx.x + 256 * i, r = c >> 4, cb = (c & 15) * 8;
+    if (r < nrows && cb < kbytes)
+      *reinterpret_cast<uint2*>(cout + r * a.ld_c + cb) = *reinterpret_cast<const uint2*>(cst + r * kColsPitch + cb);
+  }
+  constexpr int kSPer = NV ? kColsScales : kColsScales / 2;  // scale bytes per row per workgroup
+  const int svalid = NV ? kbytes / 8 : kbytes / 16;
+  uint8_t* sout = a.scales + b * a.bs_s + nb * a.ld_s + kb / (NV ? 16 : 32);
+#pragma unroll
+  for (int i = 0; i < kColsN * kSPer / 256; i++) {
+    const int c = threadIdx.x + 256 * i, r = c / kSPer, sc = c % kSPer;
+    if (r < nrows && sc < svalid) sout[r * a.ld_s + sc] = sst[r * kColsScales + sc];
   }
 }
 
@@ -336,7 +419,8 @@ static void launch_one(const QuantArgs& a, hipStream_t s) {
     if constexpr (B2D && RHT) {
       return;  // rejected by the API
     } else {
-      dim3 grid((unsigned)((a.src_cols + 255) / 256), (unsigned)((a.src_rows + 127) / 128), (unsigned)a.batch);
+      dim3 grid((unsigned)((a.src_cols + kColsN - 1) / kColsN), (unsigned)((a.src_rows + kColsK - 1) / kColsK),
+                (unsigned)a.batch);
       hipLaunchKernelGGL((quant_cols_kernel<TIn, NV, FOS, B2D, SR, RHT>), grid, dim3(256), 0, s, a);
     }
   } else if (B2D) {
