@@ -76,7 +76,9 @@ class QuantCall:
         dev = x.device
         self.opts = F.make_opts(fmt, flags, signs, seed, offset)
         self.codes = torch.empty((self.batch, R, C // 2), dtype=torch.uint8, device=dev)
-        self.scales = torch.empty((self.batch, R, C // self.blk), dtype=torch.uint8, device=dev)
+        self.lds = F.scale_pitch(C // self.blk)  # scale rows padded to 16 bytes, as the GEMM reads them
+        self.scales_buf = torch.empty((self.batch, R, self.lds), dtype=torch.uint8, device=dev)
+        self.scales = self.scales_buf[:, :, : C // self.blk]
         self.ts = torch.empty((self.batch,), dtype=torch.float32, device=dev)
         self.ws_bytes = F.fp4_quantize_workspace(self.batch, self.rows, self.cols, self.opts)
         self.ws = torch.empty((max(self.ws_bytes, 16),), dtype=torch.uint8, device=dev)
@@ -91,8 +93,8 @@ class QuantCall:
         x = self.xs[i % len(self.xs)]
         st = self.lib.fp4_quantize(x.data_ptr(), self.dt, self.batch, self.rows, self.cols, self.cols,
                                    self.rows * self.cols, self.opts_ref, self.codes.data_ptr(), self.C // 2,
-                                   self.R * (self.C // 2), self.scales.data_ptr(), self.C // self.blk,
-                                   self.R * (self.C // self.blk), self.ts.data_ptr(), self.ws.data_ptr(),
+                                   self.R * (self.C // 2), self.scales_buf.data_ptr(), self.lds,
+                                   self.R * self.lds, self.ts.data_ptr(), self.ws.data_ptr(),
                                    self.ws_bytes, self.stream)
         if st != 0:
             raise RuntimeError(f"fp4_quantize: {self.F.fp4_status_str(st)}")
@@ -117,10 +119,10 @@ class GemmCall:
         self.stream = torch.cuda.current_stream().cuda_stream
         a, b = self.a, self.b
         self.args = (a.fmt, self.G, self.M, self.N, self.K, a.codes.data_ptr(), half, self.M * half,
-                     a.scales.data_ptr(), a.scales.shape[-1], self.M * a.scales.shape[-1],
+                     a.scales.data_ptr(), a.scales.stride(1), a.scales.stride(0),
                      a.tensor_scale.data_ptr() if a.tensor_scale is not None else None,
-                     b.codes.data_ptr(), half, self.N * half, b.scales.data_ptr(), b.scales.shape[-1],
-                     self.N * b.scales.shape[-1], b.tensor_scale.data_ptr() if b.tensor_scale is not None else None,
+                     b.codes.data_ptr(), half, self.N * half, b.scales.data_ptr(), b.scales.stride(1),
+                     b.scales.stride(0), b.tensor_scale.data_ptr() if b.tensor_scale is not None else None,
                      self.c.data_ptr(), self.ct, self.N, self.M * self.N, self.stream)
 
     def __call__(self, i):

@@ -148,11 +148,17 @@ def fp4_gemm(fmt, groups, M, N, K, a_codes, lda, a_group_stride, a_scales, lda_s
 # ---------------------------------------------------------------------------
 # torch conveniences (allocation + current stream only)
 # ---------------------------------------------------------------------------
+def scale_pitch(n_blocks: int) -> int:
+    """Scale-row pitch in bytes that fp4_gemm accepts: rounded up to 16."""
+    return (n_blocks + 15) // 16 * 16
+
+
 @dataclass
 class Quantized:
     """Packed FP4 tensor as written by fp4_quantize. Shapes carry an optional
     leading batch dimension: codes [.., R, C/2], scales [.., R, C/blk],
-    tensor_scale [batch] (NVFP4) or None."""
+    tensor_scale [batch] (NVFP4) or None. `scales` may be a view whose row
+    pitch (stride(-2)) exceeds C/blk; quantize() pads it to scale_pitch()."""
     fmt: int
     codes: "torch.Tensor"
     scales: "torch.Tensor"
@@ -206,18 +212,27 @@ def quantize(x, fmt="nvfp4", *, four_over_six=False, block2d=False, transpose=Fa
     blk = 16 if fmt == FP4_NVFP4 else 32
     dev = x3.device
     codes = torch.empty((batch, R, C // 2), dtype=torch.uint8, device=dev)
-    scales = torch.empty((batch, R, max(C // blk, 0)), dtype=torch.uint8, device=dev)
+    lds = scale_pitch(C // blk)
+    scales_buf = torch.empty((batch, R, lds), dtype=torch.uint8, device=dev)
+    scales = scales_buf[:, :, : C // blk]
     ts = torch.empty((batch,), dtype=torch.float32, device=dev) if fmt == FP4_NVFP4 else None
     ws_bytes = fp4_quantize_workspace(batch, rows, cols, opts)
     ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev) if ws_bytes else None
     st = fp4_quantize(x3.data_ptr(), dt, batch, rows, cols, cols, rows * cols, opts, codes.data_ptr(), C // 2,
-                      R * (C // 2), scales.data_ptr(), C // blk, R * (C // blk),
+                      R * (C // 2), scales_buf.data_ptr(), lds, R * lds,
                       ts.data_ptr() if ts is not None else None, ws.data_ptr() if ws is not None else None,
                       ws_bytes, _stream(stream))
     _check(st, "fp4_quantize")
     if squeeze:
         codes, scales = codes[0], scales[0]
     return Quantized(fmt, codes, scales, ts)
+
+
+def _check_scales(scales):
+    """Scales are passed by base pointer and row / batch pitch: the last dim
+    must be dense."""
+    if scales.stride(-1) != 1:
+        raise ValueError("scale rows must be contiguous")
 
 
 def dequantize(q: Quantized, dtype=None, stream=None):
@@ -229,8 +244,9 @@ def dequantize(q: Quantized, dtype=None, stream=None):
     cols = half * 2
     y = torch.empty((batch, rows, cols), dtype=dtype, device=codes.device)
     dt = {torch.bfloat16: FP4_BF16, torch.float32: FP4_F32}[dtype]
+    _check_scales(scales)
     st = fp4_dequantize(q.fmt, batch, rows, cols, codes.data_ptr(), half, rows * half, scales.data_ptr(),
-                        scales.shape[-1], rows * scales.shape[-1],
+                        scales.stride(1), scales.stride(0),
                         q.tensor_scale.data_ptr() if q.tensor_scale is not None else None, y.data_ptr(), dt, cols,
                         rows * cols, _stream(stream))
     _check(st, "fp4_dequantize")
@@ -254,9 +270,11 @@ def gemm(a: Quantized, b: Quantized, out_dtype=None, stream=None):
     K = half * 2
     c = torch.empty((G, M, N), dtype=out_dtype, device=ac.device)
     ct = {torch.bfloat16: FP4_BF16, torch.float32: FP4_F32}[out_dtype]
-    st = fp4_gemm(a.fmt, G, M, N, K, ac.data_ptr(), half, M * half, asc.data_ptr(), asc.shape[-1],
-                  M * asc.shape[-1], a.tensor_scale.data_ptr() if a.tensor_scale is not None else None,
-                  bc.data_ptr(), half, N * half, bsc.data_ptr(), bsc.shape[-1], N * bsc.shape[-1],
+    _check_scales(asc)
+    _check_scales(bsc)
+    st = fp4_gemm(a.fmt, G, M, N, K, ac.data_ptr(), half, M * half, asc.data_ptr(), asc.stride(1),
+                  asc.stride(0), a.tensor_scale.data_ptr() if a.tensor_scale is not None else None,
+                  bc.data_ptr(), half, N * half, bsc.data_ptr(), bsc.stride(1), bsc.stride(0),
                   b.tensor_scale.data_ptr() if b.tensor_scale is not None else None, c.data_ptr(), ct, N, M * N,
                   _stream(stream))
     _check(st, "fp4_gemm")

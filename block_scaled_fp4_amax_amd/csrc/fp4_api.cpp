@@ -260,13 +260,10 @@ fp4_status fp4_gemm(int32_t format, int64_t groups, int64_t M, int64_t N, int64_
     return FP4_ERR_UNSUPPORTED;
   if (groups > 1 && (a_group_stride % 16 != 0 || b_group_stride % 16 != 0)) return FP4_ERR_ALIGN;
   if (!aligned(c, c_dtype == FP4_BF16 ? 2 : 4)) return FP4_ERR_ALIGN;
-  {
-    // scales are read two (MXFP4) or four (NVFP4) bytes at a time
-    const int64_t sa = nv ? 4 : 2;
-    if (!aligned(a_scales, sa) || !aligned(b_scales, sa) || lda_scales % sa != 0 || ldb_scales % sa != 0 ||
-        (groups > 1 && (a_scales_group_stride % sa != 0 || b_scales_group_stride % sa != 0)))
-      return FP4_ERR_ALIGN;
-  }
+  // scale rows are read 16 bytes at a time, up to the next multiple of 16
+  if (!aligned(a_scales, 16) || !aligned(b_scales, 16) || lda_scales % 16 != 0 || ldb_scales % 16 != 0 ||
+      (groups > 1 && (a_scales_group_stride % 16 != 0 || b_scales_group_stride % 16 != 0)))
+    return FP4_ERR_ALIGN;
   if (nv && (!aligned(a_tensor_scale, 4) || !aligned(b_tensor_scale, 4))) return FP4_ERR_ALIGN;
   fp4_status st = check_device();
   if (st != FP4_OK) return st;

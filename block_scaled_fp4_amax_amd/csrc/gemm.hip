@@ -23,18 +23,22 @@
 //
 // Tiling: a workgroup (4 waves, 2 x 2) owns a 256 x BN tile of C (BN = 256
 // for MXFP4 unless fewer tiles than compute units would result, else 128;
-// NVFP4 always 128); each wave owns
-// 128 x BN/2 as 32 x 32 MFMA tiles. The grid is persistent (one workgroup per
-// CU) and walks tiles in an order that keeps operand panels within one XCD's
-// L2. K advances 64 values per stage; each stage's codes (32 bytes per row)
-// and scale bytes are copied global -> LDS with the direct-to-LDS loads, six
-// stages in flight in a ring of distinct LDS arrays. Within a row the two
-// 16-byte halves are stored swapped on rows whose bit 3 is set, so each
-// 16-lane group of a ds_read_b128 hits 16 distinct bank groups. A wave reads
-// the next stage's fragments while its MFMAs on the current stage run. The B matrix feeds the MFMA's first
-// operand and A the second, so lane l holds C[m = l % 32][n = 8 (q / 4) +
-// 4 (l / 32) + q % 4]. The output goes through a per-wave LDS buffer so that
-// global stores write whole row segments (16 or 32 bytes per lane).
+// NVFP4 always 128); each wave owns 128 x BN/2 as 32 x 32 MFMA tiles. The
+// grid is persistent (one workgroup per CU) and walks tiles in an order that
+// keeps operand panels within one XCD's L2.
+//
+// Operand staging is shaped by the number of L2 requests, not by bytes: a
+// stage covers 128 K values, so each row contributes one 64-byte segment
+// (four lanes of a direct-to-LDS copy), and the scale bytes of a row are
+// copied 16 at a time, covering four stages (MXFP4) or two (NVFP4). Four
+// stages are in flight in a ring of distinct LDS arrays, plus two scale
+// chunks. Within a row the four 16-byte pieces are rotated by bits 2-3 of
+// the row so that each 16-lane group of a ds_read_b128 hits 16 distinct bank
+// groups. A wave reads the next half-stage's fragments while its MFMAs on
+// the current one run. The B matrix feeds the MFMA's first operand and A the
+// second, so lane l holds C[m = l % 32][n = 8 (q / 4) + 4 (l / 32) + q % 4].
+// The output goes through an LDS buffer (the fourth stage slot, free between
+// tiles) so that global stores write whole row segments.
 #include "fp4_device.h"
 #include "launch.h"
 
@@ -48,30 +52,54 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kBM = 256;
-constexpr int kRowBytes = 32;  // codes per row per stage (64 values)
-constexpr int kStages = 6;
+constexpr int kBK = 128;             // K values per stage
+constexpr int kRowBytes = kBK / 2;   // code bytes per row per stage
 
-template <int BN>
+template <bool NV, int BN>
 struct Tile {
   static constexpr int kABytes = kBM * kRowBytes;
   static constexpr int kBBytes = BN * kRowBytes;
-  static constexpr int kASBytes = kBM * 4;  // one LDS dword of scale bytes per row per stage
-  static constexpr int kBSBytes = 256 * 4;  // (rows of a 128-wide B tile are loaded twice)
-  static constexpr int kStage = kABytes + kBBytes + kASBytes + kBSBytes;
-  static constexpr int kWN = BN / 2;        // wave tile width
-  static constexpr int kNJ = kWN / 32;      // MFMA tiles across a wave
-  static constexpr int kLoads = BN == 256 ? 6 : 5;  // copies per thread per stage
+  static constexpr int kSlot = kABytes + kBBytes;
+  static constexpr int kCS = NV ? 2 : 4;     // stages per 16-byte scale chunk
+  static constexpr int kSABytes = kBM * 16;  // scale chunk: 16 bytes per row
+  static constexpr int kSBBytes = 256 * 16;  // (rows of a 128-wide B tile are loaded twice)
+  static constexpr int kChunk = kSABytes + kSBBytes;
+  static constexpr int kWN = BN / 2;         // wave tile width
+  static constexpr int kNJ = kWN / 32;       // MFMA tiles across a wave
+  static constexpr int kLA = kABytes / 4096; // 16-byte copies per thread per stage
+  static constexpr int kLB = kBBytes / 4096;
+  static constexpr int kL = kLA + kLB;
+  // epilogue slab: 16 rows when four of them fit in a slot, else 8
+  static constexpr int kEpiPitch = kWN * 4 + 16;
+  static constexpr int kEpiRows = 4 * 16 * kEpiPitch <= kSlot ? 16 : 8;
 };
 
-__device__ __forceinline__ void g2l16(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)l, 16, 0, 0);
+// Direct-to-LDS copy of 16 bytes per lane: lane i's bytes land at LDS
+// address lds + 16 i (lds wave-uniform, passed in m0). Written as inline
+// assembly so that the compiler, which cannot match the copies in flight to
+// the stage slots, adds no vmcnt waits of its own before LDS reads: every
+// wait on these copies is explicit below. The instruction has no output
+// register; m0 is not otherwise used by this kernel.
+__device__ __forceinline__ void g2l16(const void* g, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(g), "s"(lds)
+      : "memory");
 }
-// Sub-dword and dword direct-to-LDS loads fill one LDS dword per lane.
-__device__ __forceinline__ void g2l4(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)l, 4, 0, 0);
+// Scalar (wave-uniform) fp32 load, completed inside the statement. A vector
+// load here would make the compiler wait for every copy in flight before
+// its first use.
+__device__ __forceinline__ float scalar_load_f32(const float* p) {
+  float v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
 }
-__device__ __forceinline__ void g2l2(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)l, 2, 0, 0);
+// LDS byte address of a __shared__ object
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 }
 
 // s_waitcnt vmcnt(n) (gfx9 encoding), leaving expcnt / lgkmcnt unconstrained
@@ -81,20 +109,6 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 // s_waitcnt lgkmcnt(0), leaving vmcnt / expcnt unconstrained
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
-
-// Wait until every copy of stage `need` has landed, given that the copies
-// issued so far cover stages up to `last` (L loads per stage per thread,
-// completing in order); the copies of the later stages may stay in flight.
-template <int L>
-__device__ __forceinline__ void wait_stage_landed(int need, int last) {
-  switch (last - need) {
-    case 4: wait_vmcnt<4 * L>(); break;
-    case 3: wait_vmcnt<3 * L>(); break;
-    case 2: wait_vmcnt<2 * L>(); break;
-    case 1: wait_vmcnt<1 * L>(); break;
-    default: wait_vmcnt<0>(); break;
-  }
-}
 
 // Workgroup barrier without the release/acquire fences of __syncthreads()
 // (those would force vmcnt(0) and drain the copies in flight). The empty asm
@@ -113,7 +127,7 @@ __device__ __forceinline__ void lds_barrier() {
 // about the same time.
 struct TileWalk {
   int64_t tiles_m, tiles_n, T, per, wpx, x, i;
-  __device__ TileWalk(int64_t tm, int64_t tn, int64_t groups) {
+  __device__ __forceinline__ TileWalk(int64_t tm, int64_t tn, int64_t groups) {
     tiles_m = tm;
     tiles_n = tn;
     T = tm * tn * groups;
@@ -122,7 +136,7 @@ struct TileWalk {
     x = blockIdx.x % 8;
     i = blockIdx.x / 8;
   }
-  __device__ bool get(int64_t j, int64_t* grp, int64_t* tm, int64_t* tn) const {
+  __device__ __forceinline__ bool get(int64_t j, int64_t* grp, int64_t* tm, int64_t* tn) const {
     const int64_t k = i + j * wpx;
     if (k >= per) return false;
     const int64_t tile = x * per + k;
@@ -158,27 +172,27 @@ __device__ __forceinline__ f16x8 nv_dequant8(uint32_t w, const NvScale& s) {
 
 }  // namespace
 
-// Store a wave's 128 x WN block of C through its LDS buffer, 16 rows at a
+// Store a wave's 128 x WN block of C through its LDS buffer, ROWS rows at a
 // time. Lane (r32, h) holds row 32 i + r32 of the block and, in register
 // group a of MFMA tile j, the four columns 32 j + 8 a + 4 h + 0..3. The lanes
 // owning the slab's rows write their column groups (fp32) into padded LDS
 // rows; the whole wave then reads back 8 consecutive values per lane,
 // converts them to the output type and stores whole row segments.
-template <int WN, bool OUT_BF16>
+template <int WN, int ROWS, bool OUT_BF16>
 __device__ __forceinline__ void store_wave_tile(const GemmArgs& g, const f32x16 (&acc)[4][WN / 32], float alpha,
                                                 uint8_t* stage, int64_t grp, int64_t mw, int64_t nw, int lane) {
   constexpr int kPitch = WN * 4 + 16;       // padded LDS row pitch (bytes)
   constexpr int kPerRow = WN / 8;           // 8-value chunks per row
-  constexpr int kChunks = 16 * kPerRow;     // per 16-row slab
+  constexpr int kChunks = ROWS * kPerRow;   // per slab
   constexpr int kES = OUT_BF16 ? 2 : 4;
   const int r32 = lane & 31, h = lane >> 5;
   const bool vec = g.c_vec_ok;
 #pragma unroll
   for (int i = 0; i < 4; i++) {
 #pragma unroll
-    for (int half = 0; half < 2; half++) {
-      if ((r32 >> 4) == half) {
-        uint8_t* rowp = stage + (r32 & 15) * kPitch;
+    for (int half = 0; half < 32 / ROWS; half++) {
+      if (r32 / ROWS == half) {
+        uint8_t* rowp = stage + (r32 % ROWS) * kPitch;
 #pragma unroll
         for (int j = 0; j < WN / 32; j++)
 #pragma unroll
@@ -194,7 +208,7 @@ __device__ __forceinline__ void store_wave_tile(const GemmArgs& g, const f32x16 
         const int row = c / kPerRow, col = (c % kPerRow) * 8;
         const float4 v0 = *reinterpret_cast<const float4*>(stage + row * kPitch + col * 4);
         const float4 v1 = *reinterpret_cast<const float4*>(stage + row * kPitch + col * 4 + 16);
-        const int64_t m = mw + i * 32 + 16 * half + row;
+        const int64_t m = mw + i * 32 + ROWS * half + row;
         const int64_t n = nw + col;
         if (m < g.M && n < g.N) {
           uint8_t* dst = reinterpret_cast<uint8_t*>(g.c) + (grp * g.c_gs + m * g.ldc + n) * kES;
@@ -228,17 +242,15 @@ __device__ __forceinline__ void store_wave_tile(const GemmArgs& g, const f32x16 
 
 template <bool NV, int BN, bool OUT_BF16>
 __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
-  using T = Tile<BN>;
+  using T = Tile<NV, BN>;
   constexpr int NJ = T::kNJ;
-  constexpr int L = T::kLoads;
-  __shared__ __attribute__((aligned(16))) uint8_t slot0[T::kStage];
-  __shared__ __attribute__((aligned(16))) uint8_t slot1[T::kStage];
-  __shared__ __attribute__((aligned(16))) uint8_t slot2[T::kStage];
-  __shared__ __attribute__((aligned(16))) uint8_t slot3[T::kStage];
-  __shared__ __attribute__((aligned(16))) uint8_t slot4[T::kStage];
-  __shared__ __attribute__((aligned(16))) uint8_t slot5[T::kStage];
-  constexpr int kOutPitch = T::kWN * 4 + 16;
-  __shared__ __attribute__((aligned(16))) uint8_t outbuf[4 * 16 * kOutPitch];
+  constexpr int CS = T::kCS;
+  __shared__ __attribute__((aligned(16))) uint8_t slot0[T::kSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t slot1[T::kSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t slot2[T::kSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t slot3[T::kSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t chunk0[T::kChunk];
+  __shared__ __attribute__((aligned(16))) uint8_t chunk1[T::kChunk];
 
   const TileWalk walk((g.M + kBM - 1) / kBM, (g.N + BN - 1) / BN, g.groups);
   int64_t grp, tm, tn;
@@ -247,97 +259,144 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int wm = w & 1, wn = w >> 1;
   const int r32 = lane & 31, h = lane >> 5;
-  const int S = (int)(g.K / 64);
+  const uint32_t wl = __builtin_amdgcn_readfirstlane(w);  // the wave index, in a scalar register
+  // LDS addresses of the copy targets
+  const uint32_t L0 = lds_u32(slot0), L1 = lds_u32(slot1), L2 = lds_u32(slot2), L3 = lds_u32(slot3);
+  const uint32_t LC0 = lds_u32(chunk0), LC1 = lds_u32(chunk1);
+  const int S64 = (int)(g.K / 64);      // 64-K half-stages
+  const int S = (S64 + 1) / 2;          // stages; the last one is half when S64 is odd
 
   // Copy sources of the current tile: a wave-uniform base per matrix (kept in
-  // scalar registers and advanced per stage) plus a 32-bit per-lane offset.
-  // Codes: LDS chunk q holds row q / 2, half (q & 1) ^ bit 3 of the row. Rows
-  // past M / N re-read the last row (their results are never stored).
+  // scalar registers) plus 32-bit per-lane offsets. Codes: copy j of thread t
+  // fills LDS piece q = t + 256 j, i.e. row q / 4, piece q % 4, which holds
+  // the row's 16-byte K piece (q % 4) ^ bits 2-3 of the row. Rows past M / N
+  // re-read the last row (their results are never stored). In a final half
+  // stage the pieces beyond K re-read the two below them (bit j of tailmask).
   const uint8_t* a_base;
   const uint8_t* b_base;
   const uint8_t* as_base;
   const uint8_t* bs_base;
-  uint32_t a_off[2], b_off[2], as_off, bs_off;
+  uint32_t a_off[T::kLA], b_off[T::kLB], as_off, bs_off, tailmask;
   auto set_sources = [&](int64_t grp_, int64_t m0_, int64_t n0_) {
     a_base = g.a + grp_ * g.a_gs + m0_ * g.lda;
     b_base = g.b + grp_ * g.b_gs + n0_ * g.ldb;
     as_base = g.as + grp_ * g.as_gs + m0_ * g.lda_s;
     bs_base = g.bs + grp_ * g.bs_gs + n0_ * g.ldb_s;
     const int64_t am = g.M - 1 - m0_, bm = g.N - 1 - n0_;  // last valid row, tile-relative
+    tailmask = 0;
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-      const int q = t + 256 * j, row = q >> 1, half = (q & 1) ^ ((row >> 3) & 1);
-      const int64_t ar = row < am ? row : am;
-      const int64_t br = (row % BN) < bm ? (row % BN) : bm;
-      a_off[j] = (uint32_t)(ar * g.lda + half * 16);
-      b_off[j] = (uint32_t)(br * g.ldb + half * 16);
+    for (int j = 0; j < T::kLA; j++) {
+      const int q = t + 256 * j, row = q >> 2, c = (q & 3) ^ ((row >> 2) & 3);
+      a_off[j] = (uint32_t)((row < am ? row : am) * g.lda + c * 16);
+      tailmask |= (c >= 2 ? 1u : 0u) << j;
+    }
+#pragma unroll
+    for (int j = 0; j < T::kLB; j++) {
+      const int q = t + 256 * j, row = q >> 2, c = (q & 3) ^ ((row >> 2) & 3);
+      b_off[j] = (uint32_t)((row < bm ? row : bm) * g.ldb + c * 16);
+      tailmask |= (c >= 2 ? 1u : 0u) << (8 + j);
     }
     as_off = (uint32_t)((t < am ? t : am) * g.lda_s);
     bs_off = (uint32_t)(((t % BN) < bm ? (t % BN) : bm) * g.ldb_s);
   };
 
-#define G_ISSUE(BASE, SS)                                                               \
+  // Every stage issues the same number of copies, so every wait below is a
+  // compile-time count: a stage at or past S copies one 16-byte line into
+  // its slot instead (never read).
+#define G_ISSUE(SLOT, CHUNK, Y, WITH_CHUNK)                                              \
   do {                                                                                  \
-    const uint8_t* ab_ = a_base + (SS) * kRowBytes;                                     \
-    const uint8_t* bb_ = b_base + (SS) * kRowBytes;                                     \
-    g2l16(ab_ + a_off[0], (BASE) + (w * 64) * 16);                                      \
-    g2l16(ab_ + a_off[1], (BASE) + (256 + w * 64) * 16);                                \
-    g2l16(bb_ + b_off[0], (BASE) + T::kABytes + (w * 64) * 16);                         \
-    if constexpr (BN == 256) g2l16(bb_ + b_off[1], (BASE) + T::kABytes + (256 + w * 64) * 16); \
-    if constexpr (NV) {                                                                 \
-      g2l4(as_base + 4 * (SS) + as_off, (BASE) + T::kABytes + T::kBBytes + w * 256);    \
-      g2l4(bs_base + 4 * (SS) + bs_off, (BASE) + T::kABytes + T::kBBytes + T::kASBytes + w * 256); \
+    const int y_ = (Y);                                                                 \
+    if (y_ < S) {                                                                       \
+      if (WITH_CHUNK) {                                                                 \
+        g2l16(as_base + (y_ / CS) * 16 + as_off, (CHUNK) + wl * 1024);                  \
+        g2l16(bs_base + (y_ / CS) * 16 + bs_off, (CHUNK) + T::kSABytes + wl * 1024);    \
+      }                                                                                 \
+      const uint8_t* ab_ = a_base + (int64_t)y_ * kRowBytes;                            \
+      const uint8_t* bb_ = b_base + (int64_t)y_ * kRowBytes;                            \
+      const uint32_t fix_ = (2 * y_ + 1 >= S64) ? tailmask : 0u;                        \
+      _Pragma("unroll") for (int j = 0; j < T::kLA; j++)                                \
+        g2l16(ab_ + (a_off[j] - ((fix_ >> j) & 1u) * 32u), (SLOT) + (wl * 64 + 256 * j) * 16); \
+      _Pragma("unroll") for (int j = 0; j < T::kLB; j++)                                \
+        g2l16(bb_ + (b_off[j] - ((fix_ >> (8 + j)) & 1u) * 32u),                        \
+              (SLOT) + T::kABytes + (wl * 64 + 256 * j) * 16);                          \
     } else {                                                                            \
-      g2l2(as_base + 2 * (SS) + as_off, (BASE) + T::kABytes + T::kBBytes + w * 256);    \
-      g2l2(bs_base + 2 * (SS) + bs_off, (BASE) + T::kABytes + T::kBBytes + T::kASBytes + w * 256); \
+      _Pragma("unroll") for (int j = 0; j < T::kL + ((WITH_CHUNK) ? 2 : 0); j++)        \
+        g2l16(g.a, (SLOT) + (wl * 64) * 16);                                            \
     }                                                                                   \
   } while (0)
 
   f32x16 acc[4][NJ];
 
-  // Fragments of one stage, raw (codes + scale bytes), double-buffered in
-  // registers. A rows wm*128 + i*32 + r32; B rows wn*kWN + j*32 + r32.
-  const int swz = h ^ ((r32 >> 3) & 1);
-  const int offa = (wm * 128 + r32) * kRowBytes + swz * 16;
-  const int offb = T::kABytes + (wn * T::kWN + r32) * kRowBytes + swz * 16;
-  const int offsa = T::kABytes + T::kBBytes + (wm * 128 + r32) * 4 + (NV ? 2 * h : h);
-  const int offsb = T::kABytes + T::kBBytes + T::kASBytes + (wn * T::kWN + r32) * 4 + (NV ? 2 * h : h);
+  // Fragment addresses: A rows wm*128 + i*32 + r32, B rows wn*kWN + j*32 +
+  // r32; the lane's 16-byte K piece of half-stage kb is 2 kb + h, rotated.
+  const int rot = (r32 >> 2) & 3;
+  const int offa0 = (wm * 128 + r32) * kRowBytes + ((0 + h) ^ rot) * 16;
+  const int offa1 = (wm * 128 + r32) * kRowBytes + ((2 + h) ^ rot) * 16;
+  const int offb0 = T::kABytes + (wn * T::kWN + r32) * kRowBytes + ((0 + h) ^ rot) * 16;
+  const int offb1 = T::kABytes + (wn * T::kWN + r32) * kRowBytes + ((2 + h) ^ rot) * 16;
+  const int offsa = (wm * 128 + r32) * 16;
+  const int offsb = T::kSABytes + (wn * T::kWN + r32) * 16;
   uint4 ca0[4], ca1[4], cb0[NJ], cb1[NJ];
-  uint32_t sa0[4], sa1[4], sb0[NJ], sb1[NJ];
+  // scale words of a stage, double-buffered by stage parity. MXFP4: one
+  // dword per row = the E8M0 bytes of (kb, h) at byte 2 kb + h. NVFP4: two
+  // dwords per row, dword kb holding the four E4M3 bytes of half-stage kb.
+  uint32_t sa0[4][NV ? 2 : 1], sa1[4][NV ? 2 : 1], sb0[NJ][NV ? 2 : 1], sb1[NJ][NV ? 2 : 1];
 
-#define G_READ(BASE, CA, CB, SA, SB)                                                    \
+#define G_READ(SLOT, KB, CA, CB)                                                        \
+  do {                                                                                  \
+    _Pragma("unroll") for (int i = 0; i < 4; i++)                                       \
+      CA[i] = *reinterpret_cast<const uint4*>((SLOT) + ((KB) ? offa1 : offa0) + i * 32 * kRowBytes); \
+    _Pragma("unroll") for (int j = 0; j < NJ; j++)                                      \
+      CB[j] = *reinterpret_cast<const uint4*>((SLOT) + ((KB) ? offb1 : offb0) + j * 32 * kRowBytes); \
+  } while (0)
+
+#define G_READ_SCALES(CHUNK, U, SA, SB)                                                 \
   do {                                                                                  \
     _Pragma("unroll") for (int i = 0; i < 4; i++) {                                     \
-      CA[i] = *reinterpret_cast<const uint4*>((BASE) + offa + i * 32 * kRowBytes);      \
-      if constexpr (NV) SA[i] = *reinterpret_cast<const uint16_t*>((BASE) + offsa + i * 128); \
-      else SA[i] = (BASE)[offsa + i * 128];                                             \
+      if constexpr (NV) {                                                               \
+        const uint2 v_ = *reinterpret_cast<const uint2*>((CHUNK) + offsa + i * 512 + ((U) % CS) * 8); \
+        SA[i][0] = v_.x;                                                                \
+        SA[i][NV ? 1 : 0] = v_.y;                                                       \
+      } else {                                                                          \
+        SA[i][0] = *reinterpret_cast<const uint32_t*>((CHUNK) + offsa + i * 512 + ((U) % CS) * 4); \
+      }                                                                                 \
     }                                                                                   \
     _Pragma("unroll") for (int j = 0; j < NJ; j++) {                                    \
-      CB[j] = *reinterpret_cast<const uint4*>((BASE) + offb + j * 32 * kRowBytes);      \
-      if constexpr (NV) SB[j] = *reinterpret_cast<const uint16_t*>((BASE) + offsb + j * 128); \
-      else SB[j] = (BASE)[offsb + j * 128];                                             \
+      if constexpr (NV) {                                                               \
+        const uint2 v_ = *reinterpret_cast<const uint2*>((CHUNK) + offsb + j * 512 + ((U) % CS) * 8); \
+        SB[j][0] = v_.x;                                                                \
+        SB[j][NV ? 1 : 0] = v_.y;                                                       \
+      } else {                                                                          \
+        SB[j][0] = *reinterpret_cast<const uint32_t*>((CHUNK) + offsb + j * 512 + ((U) % CS) * 4); \
+      }                                                                                 \
     }                                                                                   \
   } while (0)
 
-#define G_MFMAS(CA, CB, SA, SB)                                                         \
+#define G_MFMAS(CA, CB, SA, SB, KB)                                                     \
   do {                                                                                  \
     if constexpr (!NV) {                                                                \
+      uint32_t sa_[4], sb_[NJ];                                                         \
+      _Pragma("unroll") for (int i = 0; i < 4; i++) sa_[i] = (SA[i][0] >> (16 * (KB) + 8 * h)) & 0xffu; \
+      _Pragma("unroll") for (int j = 0; j < NJ; j++) sb_[j] = (SB[j][0] >> (16 * (KB) + 8 * h)) & 0xffu; \
       _Pragma("unroll") for (int i = 0; i < 4; i++) {                                   \
         const i32x8 fa = {(int)CA[i].x, (int)CA[i].y, (int)CA[i].z, (int)CA[i].w, 0, 0, 0, 0}; \
         _Pragma("unroll") for (int j = 0; j < NJ; j++) {                                \
           const i32x8 fb = {(int)CB[j].x, (int)CB[j].y, (int)CB[j].z, (int)CB[j].w, 0, 0, 0, 0}; \
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb, fa, acc[i][j], 4, 4, 0, (int)SB[j], \
-                                                                      0, (int)SA[i]);   \
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb, fa, acc[i][j], 4, 4, 0, (int)sb_[j], \
+                                                                      0, (int)sa_[i]);  \
         }                                                                               \
       }                                                                                 \
     } else {                                                                            \
+      uint32_t pa_[4], pb_[NJ];                                                         \
+      _Pragma("unroll") for (int i = 0; i < 4; i++) pa_[i] = SA[i][(KB) & (NV ? 1 : 0)] >> (16 * h); \
+      _Pragma("unroll") for (int j = 0; j < NJ; j++) pb_[j] = SB[j][(KB) & (NV ? 1 : 0)] >> (16 * h); \
       NvScale na[4], nb[NJ];                                                            \
       _Pragma("unroll") for (int kt = 0; kt < 4; kt++) {                                \
         if ((kt & 1) == 0) {                                                            \
           _Pragma("unroll") for (int i = 0; i < 4; i++)                                 \
-            na[i] = nv_scale(kt == 0 ? (SA[i] & 0xffu) : (SA[i] >> 8));                 \
+            na[i] = nv_scale(kt == 0 ? (pa_[i] & 0xffu) : ((pa_[i] >> 8) & 0xffu));     \
           _Pragma("unroll") for (int j = 0; j < NJ; j++)                                \
-            nb[j] = nv_scale(kt == 0 ? (SB[j] & 0xffu) : (SB[j] >> 8));                 \
+            nb[j] = nv_scale(kt == 0 ? (pb_[j] & 0xffu) : ((pb_[j] >> 8) & 0xffu));     \
         }                                                                               \
         f16x8 ha[4], hb[NJ];                                                            \
         _Pragma("unroll") for (int i = 0; i < 4; i++) {                                 \
@@ -355,34 +414,48 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
     }                                                                                   \
   } while (0)
 
-  // Stage SS sits in slot SS % 6 with its fragments already in registers
-  // (buffer SS % 2): wait for stage SS+1, barrier, start the copy of stage
-  // SS+5 into the slot stage SS-1 used, read stage SS+1's fragments into the
-  // other buffer, then run stage SS. The slots are distinct arrays, so
-  // fragment reads are not serialised behind the copies in flight.
-#define G_STEP(SS, NEXT, REFILL, CA, CB, SA, SB, NCA, NCB, NSA, NSB)                    \
+  // Stage x = x0 + U (U compile-time, x0 a multiple of 8) sits in slot U % 4,
+  // its scales in chunk (U / CS) % 2 and scale buffer U % 2, and its first
+  // half-stage's fragments are in ca0 / cb0. Half-stage 0: read half-stage
+  // 1's fragments (and stage x+1's scales when its chunk is already there),
+  // run half-stage 0. Half-stage 1: wait for stage x+1, barrier, start the
+  // copy of stage x+4 into this slot (every wave is done with it), read stage
+  // x+1's first fragments (and its scales if its chunk came with it), run
+  // half-stage 1. A chunk slot is refilled at stage 4 c - 4 (c the chunk's
+  // index, in chunk-sized steps of CS stages): by then the last stage of the
+  // chunk two back has had its scales read, in half-stage 0 of the stage
+  // before it.
+#define G_STAGE(U, SLOT, NSLOT, CHUNK, NCHUNK, LSLOT, LRCHUNK, SA, SB, NSA, NSB)       \
   do {                                                                                  \
-    if ((SS) + 1 < S) {                                                                 \
-      wait_lgkm0();                                                                     \
-      wait_stage_landed<L>((SS) + 1, min((SS) + kStages - 2, S - 1));                   \
-      lds_barrier();                                                                    \
-      if ((SS) + kStages - 1 < S) G_ISSUE(REFILL, (SS) + kStages - 1);                  \
-      G_READ(NEXT, NCA, NCB, NSA, NSB);                                                 \
+    const int x_ = x0 + (U);                                                            \
+    const bool kb1_ = 2 * x_ + 1 < S64;                                                 \
+    if (kb1_) G_READ(SLOT, 1, ca1, cb1);                                                \
+    if (((U) + 1) % CS != 0 && x_ + 1 < S) G_READ_SCALES(NCHUNK, (U) + 1, NSA, NSB);    \
+    G_MFMAS(ca0, cb0, SA, SB, 0);                                                       \
+    if (kb1_) {                                                                         \
+      if (x_ + 1 < S) {                                                                 \
+        wait_lgkm0();                                                                   \
+        wait_vmcnt<2 * T::kL + (((U) + 2) % CS == 0 ? 2 : 0) + (((U) + 3) % CS == 0 ? 2 : 0)>(); \
+        lds_barrier();                                                                  \
+        G_ISSUE(LSLOT, LRCHUNK, x_ + 4, ((U) + 4) % CS == 0);                           \
+        G_READ(NSLOT, 0, ca0, cb0);                                                     \
+        if (((U) + 1) % CS == 0) G_READ_SCALES(NCHUNK, (U) + 1, NSA, NSB);              \
+      }                                                                                 \
+      G_MFMAS(ca1, cb1, SA, SB, 1);                                                     \
     }                                                                                   \
-    G_MFMAS(CA, CB, SA, SB);                                                            \
   } while (0)
 
-#define G_PROLOGUE()                                                                    \
-  do {                                                                                  \
-    if (S > 0) G_ISSUE(slot0, 0);                                                       \
-    if (S > 1) G_ISSUE(slot1, 1);                                                       \
-    if (S > 2) G_ISSUE(slot2, 2);                                                       \
-    if (S > 3) G_ISSUE(slot3, 3);                                                       \
-    if (S > 4) G_ISSUE(slot4, 4);                                                       \
-  } while (0)
+// chunk holding stage x0 + U's scales (and its LDS address)
+#define G_CH(U) ((((U) / CS) % 2) ? chunk1 : chunk0)
+#define G_LCH(U) ((((U) / CS) % 2) ? LC1 : LC0)
 
+  // copies issued for stages 1..3, which may be in flight when stage 0 is needed
+  constexpr int kAfter0 = 3 * T::kL + (1 % CS == 0 ? 2 : 0) + (2 % CS == 0 ? 2 : 0) + (3 % CS == 0 ? 2 : 0);
   set_sources(grp, tm * kBM, tn * BN);
-  G_PROLOGUE();
+  G_ISSUE(L0, LC0, 0, true);
+  G_ISSUE(L1, LC1, 1, 1 % CS == 0);
+  G_ISSUE(L2, LC1, 2, 2 % CS == 0);
+  G_ISSUE(L3, LC1, 3, 3 % CS == 0);
   for (int64_t jt = 0;; jt++) {
     const int64_t m0 = tm * kBM, n0 = tn * BN, cgrp = grp;
 #pragma unroll
@@ -392,38 +465,49 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
 #pragma unroll
         for (int q = 0; q < 16; q++) acc[i][j][q] = 0.0f;
     if (S > 0) {
-      // the previous tile's output stores are counted too: wait for all
-      wait_vmcnt<0>();
+      wait_vmcnt<kAfter0>();
       lds_barrier();
-      G_READ(slot0, ca0, cb0, sa0, sb0);
+      G_READ(slot0, 0, ca0, cb0);
+      G_READ_SCALES(chunk0, 0, sa0, sb0);
     }
-    for (int s = 0; s < S; s += 6) {
-      G_STEP(s, slot1, slot5, ca0, cb0, sa0, sb0, ca1, cb1, sa1, sb1);
-      if (s + 1 < S) G_STEP(s + 1, slot2, slot0, ca1, cb1, sa1, sb1, ca0, cb0, sa0, sb0);
-      if (s + 2 < S) G_STEP(s + 2, slot3, slot1, ca0, cb0, sa0, sb0, ca1, cb1, sa1, sb1);
-      if (s + 3 < S) G_STEP(s + 3, slot4, slot2, ca1, cb1, sa1, sb1, ca0, cb0, sa0, sb0);
-      if (s + 4 < S) G_STEP(s + 4, slot5, slot3, ca0, cb0, sa0, sb0, ca1, cb1, sa1, sb1);
-      if (s + 5 < S) G_STEP(s + 5, slot0, slot4, ca1, cb1, sa1, sb1, ca0, cb0, sa0, sb0);
+    for (int x0 = 0; x0 < S; x0 += 8) {
+      G_STAGE(0, slot0, slot1, G_CH(0), G_CH(1), L0, G_LCH(4), sa0, sb0, sa1, sb1);
+      if (x0 + 1 < S) G_STAGE(1, slot1, slot2, G_CH(1), G_CH(2), L1, G_LCH(5), sa1, sb1, sa0, sb0);
+      if (x0 + 2 < S) G_STAGE(2, slot2, slot3, G_CH(2), G_CH(3), L2, G_LCH(6), sa0, sb0, sa1, sb1);
+      if (x0 + 3 < S) G_STAGE(3, slot3, slot0, G_CH(3), G_CH(4), L3, G_LCH(7), sa1, sb1, sa0, sb0);
+      if (x0 + 4 < S) G_STAGE(4, slot0, slot1, G_CH(4), G_CH(5), L0, G_LCH(8), sa0, sb0, sa1, sb1);
+      if (x0 + 5 < S) G_STAGE(5, slot1, slot2, G_CH(5), G_CH(6), L1, G_LCH(9), sa1, sb1, sa0, sb0);
+      if (x0 + 6 < S) G_STAGE(6, slot2, slot3, G_CH(6), G_CH(7), L2, G_LCH(10), sa0, sb0, sa1, sb1);
+      if (x0 + 7 < S) G_STAGE(7, slot3, slot0, G_CH(7), G_CH(8), L3, G_LCH(11), sa1, sb1, sa0, sb0);
     }
 
-    // Start the next tile's first copies (every wave is past its last LDS
-    // read of this tile), then store this tile while they are in flight.
+    // Every wave is done with the slots: start the next tile's first three
+    // stages, store this tile through slot 3, then start its fourth stage.
     const bool more = walk.get(jt + 1, &grp, &tm, &tn);
+    wait_lgkm0();
+    lds_barrier();
     if (more) {
-      wait_lgkm0();
-      lds_barrier();
       set_sources(grp, tm * kBM, tn * BN);
-      G_PROLOGUE();
+      G_ISSUE(L0, LC0, 0, true);
+      G_ISSUE(L1, LC1, 1, 1 % CS == 0);
+      G_ISSUE(L2, LC1, 2, 2 % CS == 0);
     }
     float alpha = 1.0f;
-    if constexpr (NV) alpha = g.a_ts[cgrp] * g.b_ts[cgrp];
-    store_wave_tile<T::kWN, OUT_BF16>(g, acc, alpha, outbuf + w * 16 * kOutPitch, cgrp, m0 + wm * 128,
-                                     n0 + wn * T::kWN, lane);
+    if constexpr (NV) alpha = scalar_load_f32(g.a_ts + cgrp) * scalar_load_f32(g.b_ts + cgrp);
+    store_wave_tile<T::kWN, T::kEpiRows, OUT_BF16>(g, acc, alpha, slot3 + w * (T::kEpiRows * T::kEpiPitch), cgrp,
+                                                   m0 + wm * 128, n0 + wn * T::kWN, lane);
     if (!more) break;
+    wait_lgkm0();
+    lds_barrier();
+    G_ISSUE(L3, LC1, 3, 3 % CS == 0);
   }
-#undef G_PROLOGUE
-#undef G_STEP
+  // no copy into LDS may outlive the workgroup
+  wait_vmcnt<0>();
+#undef G_CH
+#undef G_LCH
+#undef G_STAGE
 #undef G_MFMAS
+#undef G_READ_SCALES
 #undef G_READ
 #undef G_ISSUE
 }

@@ -162,19 +162,25 @@ fp4_status fp4_dequantize(int32_t format, int64_t batch, int64_t rows, int64_t c
  *   C_g[m, n] = sum_k deq(A_g)[m, k] * deq(B_g)[n, k],  g < groups,
  * accumulated in fp32, written as fp32 or bf16 (c_dtype, round-to-nearest-
  * even). A_g is [M, K] and B_g is [N, K] (an nn.Linear weight [out, in]),
- * both K-major codes+scales exactly as fp4_quantize writes them (quantize a
- * [K, N] weight with FP4_TRANSPOSE). MXFP4 runs on the gfx950 block-scaled
- * FP4 matrix cores; NVFP4 is dequantized exactly to bf16 in registers and
- * multiplied on the bf16 matrix cores, with S_a * S_b applied in the
+ * both K-major codes+scales as fp4_quantize writes them (quantize a [K, N]
+ * weight with FP4_TRANSPOSE). MXFP4 runs on the gfx950 block-scaled FP4
+ * matrix cores; NVFP4 is dequantized exactly to fp16 in registers and
+ * multiplied on the fp16 matrix cores, with S_a * S_b applied in the
  * epilogue. a_tensor_scale / b_tensor_scale: NVFP4 device float[groups].
  *   Strides: lda, ldb in bytes (>= K/2, multiples of 16); lda_scales,
- *   ldb_scales in bytes (>= K/blk); ldc and group strides of C in elements;
- *   group strides of codes/scales in bytes. K % 64 == 0; M and N arbitrary
- *   (>= 0). Scale pointers and strides (lda_scales, ldb_scales and the scale
- *   group strides) must be multiples of 2 (MXFP4) or 4 (NVFP4): scales are
- *   read two or four bytes at a time. Each group's code and scale panels
- *   must span less than 2 GiB (else FP4_ERR_UNSUPPORTED). Code pointers 16-byte
- *   aligned; c 4-byte aligned.
+ *   ldb_scales in bytes (>= K/blk, multiples of 16); ldc and group strides
+ *   of C in elements; group strides of codes/scales in bytes (multiples of
+ *   16). K % 64 == 0; M and N arbitrary (>= 0). Code and scale pointers
+ *   16-byte aligned; c 4-byte aligned (2 for bf16).
+ *   Scale rows are read in 16-byte pieces up to the next multiple of 16 of
+ *   K/blk, so every scale row must be readable up to that length (true for
+ *   any [rows, ld] buffer with ld a multiple of 16): give fp4_quantize a
+ *   scale pitch rounded up to 16 bytes when its output feeds fp4_gemm.
+ *   Each group's code and scale panels must span less than 2 GiB (else
+ *   FP4_ERR_UNSUPPORTED).
+ * Errors: FP4_ERR_INVALID for bad sizes, strides or NULL operands,
+ * FP4_ERR_ALIGN for misaligned pointers or pitches, FP4_ERR_DEVICE off
+ * gfx950, FP4_ERR_HIP if the launch fails. Nothing is written on error.
  */
 fp4_status fp4_gemm(int32_t format, int64_t groups, int64_t M, int64_t N, int64_t K,
                     const uint8_t* a_codes, int64_t lda, int64_t a_group_stride,

@@ -70,3 +70,14 @@ def mixed_matrix(rows, cols, seed, dtype=torch.bfloat16, device="cpu"):
         x[3, : min(cols, 32)] = torch.tensor([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0] * 4)[: min(cols, 32)]
         x[3, 0] = 6.0
     return x.to(dtype).to(device)
+
+
+def upload_scales(scales):
+    """Upload a [.., R, nb] uint8 scale array with rows padded to the 16-byte
+    pitch fp4_gemm reads; returns the [.., R, nb] view."""
+    import block_scaled_fp4_amax_amd as F
+    a = np.asarray(scales, dtype=np.uint8)
+    nb = a.shape[-1]
+    buf = np.zeros((*a.shape[:-1], F.scale_pitch(nb)), dtype=np.uint8)
+    buf[..., :nb] = a
+    return torch.from_numpy(buf).cuda()[..., :nb]

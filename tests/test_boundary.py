@@ -144,8 +144,8 @@ def test_valid_dequantize_without_gfx950_reports_device(fp4):
     assert d(fp4) == fp4.FP4_ERR_DEVICE
 
 
-def g(fp4, fmt=0, groups=1, M=64, N=64, K=128, a=FAKE, lda=64, ags=0, asc=FAKE, ldas=4, asgs=0, ats=FAKE, b=FAKE,
-      ldb=64, bgs=0, bsc=FAKE, ldbs=4, bsgs=0, bts=FAKE, c=FAKE, ct=0, ldc=64, cgs=0):
+def g(fp4, fmt=0, groups=1, M=64, N=64, K=128, a=FAKE, lda=64, ags=0, asc=FAKE, ldas=16, asgs=0, ats=FAKE, b=FAKE,
+      ldb=64, bgs=0, bsc=FAKE, ldbs=16, bsgs=0, bts=FAKE, c=FAKE, ct=0, ldc=64, cgs=0):
     return fp4.fp4_gemm(fmt, groups, M, N, K, a, lda, ags, asc, ldas, asgs, ats, b, ldb, bgs, bsc, ldbs, bsgs, bts,
                         c, ct, ldc, cgs, None)
 
@@ -157,11 +157,15 @@ def test_gemm_errors(fp4):
     assert g(fp4, lda=32) == fp4.FP4_ERR_INVALID
     assert g(fp4, ldas=2) == fp4.FP4_ERR_INVALID
     assert g(fp4, ldc=32) == fp4.FP4_ERR_INVALID
-    assert g(fp4, fmt=1, ldas=8, ldbs=8, ats=0) == fp4.FP4_ERR_INVALID
-    assert g(fp4, groups=2, ags=4096, bgs=4096, asgs=256, bsgs=256, cgs=100) == fp4.FP4_ERR_INVALID
+    assert g(fp4, fmt=1, ats=0) == fp4.FP4_ERR_INVALID
+    assert g(fp4, groups=2, ags=4096, bgs=4096, asgs=1024, bsgs=1024, cgs=100) == fp4.FP4_ERR_INVALID
     assert g(fp4, a=FAKE + 8) == fp4.FP4_ERR_ALIGN
     assert g(fp4, lda=72) == fp4.FP4_ERR_ALIGN
     assert g(fp4, c=FAKE + 2) == fp4.FP4_ERR_ALIGN
+    # scale rows are read 16 bytes at a time
+    assert g(fp4, asc=FAKE + 8) == fp4.FP4_ERR_ALIGN
+    assert g(fp4, ldbs=24) == fp4.FP4_ERR_ALIGN
+    assert g(fp4, groups=2, ags=4096, bgs=4096, asgs=1032, bsgs=1024, cgs=4096) == fp4.FP4_ERR_ALIGN
     assert g(fp4, M=0, a=0, b=0, c=0) == fp4.FP4_OK
     assert g(fp4, M=-1) == fp4.FP4_ERR_INVALID
 
@@ -169,7 +173,7 @@ def test_gemm_errors(fp4):
 @cpu_only
 def test_valid_gemm_without_gfx950_reports_device(fp4):
     assert g(fp4) == fp4.FP4_ERR_DEVICE
-    assert g(fp4, fmt=1, ldas=8, ldbs=8) == fp4.FP4_ERR_DEVICE
+    assert g(fp4, fmt=1) == fp4.FP4_ERR_DEVICE
 
 
 def test_product_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -13,7 +13,7 @@ import torch
 
 import block_scaled_fp4_amax_amd as F
 from block_scaled_fp4_amax_amd import inputs
-from gpu_util import flag_str, oracle_input
+from gpu_util import flag_str, oracle_input, upload_scales
 
 pytestmark = pytest.mark.gpu
 
@@ -34,7 +34,7 @@ def oracle_operand(O, x, fmt, flags, signs=0, rows=None):
         ts.append(r["tensor_scale"] or 0.0)
         c, s = (r["codes"], r["scales"]) if rows is None else (r["codes"][rows], r["scales"][rows])
         deq.append(O.dequantize(fmt, c, s, r["tensor_scale"]))
-    q = F.Quantized(fmt, torch.from_numpy(np.stack(codes)).cuda(), torch.from_numpy(np.stack(scales)).cuda(),
+    q = F.Quantized(fmt, torch.from_numpy(np.stack(codes)).cuda(), upload_scales(np.stack(scales)),
                     torch.tensor(ts, dtype=torch.float32).cuda() if fmt == NV else None)
     return q, np.stack(deq)
 
@@ -83,6 +83,17 @@ def test_mxfp4_grouped_moe_recipe(oracle, out):
 def test_nvfp4_dense_ragged(oracle, out, flags):
     d = inputs.w4a4_linear(m=200, n=272, k=320)
     run_case(oracle, d["a"], d["w"], NV, flags, flags, out, what="nv-dense")
+
+
+@pytest.mark.parametrize("k", [64, 128, 192, 384, 576, 1088, 2112])
+@pytest.mark.parametrize("fmt", [MX, NV], ids=["mx", "nv"])
+def test_k_pipeline_depths(oracle, fmt, k):
+    """K from one half-stage (64) up to several rounds of the 4-slot stage
+    ring, with and without a final half-stage, and scale chunks that end
+    part-way through a stage group."""
+    d = inputs.w4a4_linear(m=40, n=72, k=k, seed=k)
+    run_case(oracle, d["a"], d["w"], fmt, FOS if fmt == NV else 0, FOS if fmt == NV else 0, torch.float32,
+             what=f"k-sweep K={k}")
 
 
 def test_nvfp4_grouped(oracle):
