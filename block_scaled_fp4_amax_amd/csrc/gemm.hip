@@ -66,27 +66,29 @@ struct Tile {
   static constexpr int kChunk = kSABytes + kSBBytes;
   static constexpr int kWN = BN / 2;         // wave tile width
   static constexpr int kNJ = kWN / 32;       // MFMA tiles across a wave
-  static constexpr int kLA = kABytes / 4096; // 16-byte copies per thread per stage
-  static constexpr int kLB = kBBytes / 4096;
+  // Waves 0 and 1 issue every copy (16 bytes per lane per copy); waves 2
+  // and 3 issue every store of C. The vmcnt counter is per wave, so the
+  // copies are never waited for behind stores, nor the stores at all.
+  static constexpr int kLA = kABytes / 2048; // copies per loader lane per stage
+  static constexpr int kLB = kBBytes / 2048;
   static constexpr int kL = kLA + kLB;
-  // epilogue slab: 16 rows when four of them fit in a slot, else 8
-  static constexpr int kEpiPitch = kWN * 4 + 16;
-  static constexpr int kEpiRows = 4 * 16 * kEpiPitch <= kSlot ? 16 : 8;
+  static constexpr int kLC = 4;              // copies per loader lane for a scale chunk
 };
 
-// Direct-to-LDS copy of 16 bytes per lane: lane i's bytes land at LDS
-// address lds + 16 i (lds wave-uniform, passed in m0). Written as inline
+// Direct-to-LDS copy of 16 bytes per lane from base + off (base
+// wave-uniform, in scalar registers; off a 32-bit lane offset): lane i's
+// bytes land at LDS address lds + 16 i (lds wave-uniform, passed in m0). Written as inline
 // assembly so that the compiler, which cannot match the copies in flight to
 // the stage slots, adds no vmcnt waits of its own before LDS reads: every
 // wait on these copies is explicit below. The instruction has no output
 // register; m0 is not otherwise used by this kernel.
-__device__ __forceinline__ void g2l16(const void* g, uint32_t lds) {
+__device__ __forceinline__ void g2l16(const void* base, uint32_t off, uint32_t lds) {
   asm volatile(
-      "s_mov_b32 m0, %1\n\t"
+      "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
+      "global_load_lds_dwordx4 %0, %1"
       :
-      : "v"(g), "s"(lds)
+      : "v"(off), "s"(base), "s"(lds)
       : "memory");
 }
 // Scalar (wave-uniform) fp32 load, completed inside the statement. A vector
@@ -148,6 +150,15 @@ struct TileWalk {
   }
 };
 
+// An FP4 MFMA operand: the instruction reads the low four of its eight
+// registers (32 E2M1 codes); the high four are left undefined so the
+// compiler need not copy the fragment into a zero-padded tuple.
+__device__ __forceinline__ i32x8 fp4_operand(const uint4& v) {
+  typedef int i32x4v __attribute__((ext_vector_type(4)));
+  const i32x4v q = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+  return __builtin_shufflevector(q, q, 0, 1, 2, 3, -1, -1, -1, -1);
+}
+
 // NVFP4 block scale split for the fp16 dequant: the converter's scale operand
 // (only its exponent is used, so the decoded scale itself serves) and the
 // mantissa factor 1 + m/8 as an fp16 pair.
@@ -172,70 +183,83 @@ __device__ __forceinline__ f16x8 nv_dequant8(uint32_t w, const NvScale& s) {
 
 }  // namespace
 
-// Store a wave's 128 x WN block of C through its LDS buffer, ROWS rows at a
-// time. Lane (r32, h) holds row 32 i + r32 of the block and, in register
-// group a of MFMA tile j, the four columns 32 j + 8 a + 4 h + 0..3. The lanes
-// owning the slab's rows write their column groups (fp32) into padded LDS
-// rows; the whole wave then reads back 8 consecutive values per lane,
-// converts them to the output type and stores whole row segments.
-template <int WN, int ROWS, bool OUT_BF16>
-__device__ __forceinline__ void store_wave_tile(const GemmArgs& g, const f32x16 (&acc)[4][WN / 32], float alpha,
-                                                uint8_t* stage, int64_t grp, int64_t mw, int64_t nw, int lane) {
-  constexpr int kPitch = WN * 4 + 16;       // padded LDS row pitch (bytes)
-  constexpr int kPerRow = WN / 8;           // 8-value chunks per row
-  constexpr int kChunks = ROWS * kPerRow;   // per slab
-  constexpr int kES = OUT_BF16 ? 2 : 4;
+// Output staging. A wave's 128 x WN block of C goes, in fp32, to its own
+// stage slot, RR rows at a time (RR = 128, or 64 when 128 rows do not fit a
+// slot), as rows of 16-byte chunks whose position is XORed with the low row
+// bits so that the lanes' writes and the store waves' reads spread over the
+// banks. Lane (r32, h) holds, in register group a of MFMA tile (i, j), the
+// four columns 32 j + 8 a + 4 h + 0..3 of row 32 i + r32: one chunk.
+template <int WN>
+struct Epi {
+  static constexpr int kRowB = WN * 4;             // staged row bytes (fp32)
+  static constexpr int kCPR = kRowB / 16;          // 16-byte chunks per row
+  static constexpr int kSwz = (kCPR < 16 ? kCPR : 16) - 1;
+};
+
+template <int WN, int RR>
+__device__ __forceinline__ void stage_wave_rows(const f32x16 (&acc)[4][WN / 32], float alpha, uint8_t* region,
+                                                int round, int lane) {
+  using E = Epi<WN>;
   const int r32 = lane & 31, h = lane >> 5;
-  const bool vec = g.c_vec_ok;
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
+  for (int ii = 0; ii < RR / 32; ii++) {
+    const int i = round * (RR / 32) + ii;
+    const int row = ii * 32 + r32;
+    uint8_t* rowp = region + row * E::kRowB;
 #pragma unroll
-    for (int half = 0; half < 32 / ROWS; half++) {
-      if (r32 / ROWS == half) {
-        uint8_t* rowp = stage + (r32 % ROWS) * kPitch;
+    for (int j = 0; j < WN / 32; j++)
 #pragma unroll
-        for (int j = 0; j < WN / 32; j++)
-#pragma unroll
-          for (int a = 0; a < 4; a++)
-            *reinterpret_cast<float4*>(rowp + (j * 32 + 8 * a + 4 * h) * 4) =
-                make_float4(acc[i][j][4 * a] * alpha, acc[i][j][4 * a + 1] * alpha, acc[i][j][4 * a + 2] * alpha,
-                            acc[i][j][4 * a + 3] * alpha);
+      for (int a = 0; a < 4; a++) {
+        const int chunk = (8 * j + 2 * a + h) ^ (row & E::kSwz);
+        *reinterpret_cast<float4*>(rowp + chunk * 16) =
+            make_float4(acc[i][j][4 * a] * alpha, acc[i][j][4 * a + 1] * alpha, acc[i][j][4 * a + 2] * alpha,
+                        acc[i][j][4 * a + 3] * alpha);
       }
-      asm volatile("" ::: "memory");
+  }
+}
+
+// Store wave s (= wave 2 + s) writes rows s*128 + round*RR + [0, RR) of the
+// workgroup tile: each row joins the staged blocks of waves s (columns
+// [0, WN)) and s + 2 (columns [WN, 2 WN)); a lane converts 8 consecutive
+// values and writes them in one piece, consecutive lanes along the row.
+template <int WN, int RR, bool OUT_BF16>
+__device__ __forceinline__ void store_staged_rows(const GemmArgs& g, const uint8_t* reg_lo, const uint8_t* reg_hi,
+                                                  int64_t grp, int64_t m_base, int64_t n0, int lane) {
+  using E = Epi<WN>;
+  constexpr int kGPR = WN / 8;  // 8-value groups per row per block
+  constexpr int kES = OUT_BF16 ? 2 : 4;
+  const bool vec = g.c_vec_ok;
+#pragma unroll 2
+  for (int c0 = 0; c0 < RR * 2 * kGPR; c0 += 64) {
+    const int c = c0 + lane;
+    const int row = c / (2 * kGPR), k = c % (2 * kGPR);
+    const int wn = k / kGPR, p = k % kGPR;
+    const uint8_t* rp = (wn ? reg_hi : reg_lo) + row * E::kRowB;
+    const float4 v0 = *reinterpret_cast<const float4*>(rp + (((2 * p) ^ (row & E::kSwz)) * 16));
+    const float4 v1 = *reinterpret_cast<const float4*>(rp + (((2 * p + 1) ^ (row & E::kSwz)) * 16));
+    const int64_t m = m_base + row;
+    const int64_t n = n0 + wn * WN + p * 8;
+    if (m < g.M && n < g.N) {
+      uint8_t* dst = reinterpret_cast<uint8_t*>(g.c) + (grp * g.c_gs + m * g.ldc + n) * kES;
+      const float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      if (vec && n + 8 <= g.N) {
+        if constexpr (OUT_BF16) {
+          uint32_t o[4];
 #pragma unroll
-      for (int c0 = 0; c0 < kChunks; c0 += 64) {
-        const int c = c0 + lane;
-        const int row = c / kPerRow, col = (c % kPerRow) * 8;
-        const float4 v0 = *reinterpret_cast<const float4*>(stage + row * kPitch + col * 4);
-        const float4 v1 = *reinterpret_cast<const float4*>(stage + row * kPitch + col * 4 + 16);
-        const int64_t m = mw + i * 32 + ROWS * half + row;
-        const int64_t n = nw + col;
-        if (m < g.M && n < g.N) {
-          uint8_t* dst = reinterpret_cast<uint8_t*>(g.c) + (grp * g.c_gs + m * g.ldc + n) * kES;
-          const float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-          if (vec && n + 8 <= g.N) {
-            if constexpr (OUT_BF16) {
-              uint32_t o[4];
-#pragma unroll
-              for (int e = 0; e < 4; e++)
-                o[e] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)vv[2 * e], (__bf16)vv[2 * e + 1]});
-              *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
-            } else {
-              reinterpret_cast<float4*>(dst)[0] = v0;
-              reinterpret_cast<float4*>(dst)[1] = v1;
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; e++) {
-              if (n + e < g.N) {
-                if constexpr (OUT_BF16) reinterpret_cast<__bf16*>(dst)[e] = (__bf16)vv[e];
-                else reinterpret_cast<float*>(dst)[e] = vv[e];
-              }
-            }
-          }
+          for (int e = 0; e < 4; e++) o[e] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)vv[2 * e], (__bf16)vv[2 * e + 1]});
+          *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+        } else {
+          reinterpret_cast<float4*>(dst)[0] = v0;
+          reinterpret_cast<float4*>(dst)[1] = v1;
+        }
+      } else {
+        // row end or unaligned C: element by element
+#pragma unroll 1
+        for (int e = 0; e < 8 && n + e < g.N; e++) {
+          if constexpr (OUT_BF16) reinterpret_cast<__bf16*>(dst)[e] = (__bf16)vv[e];
+          else reinterpret_cast<float*>(dst)[e] = vv[e];
         }
       }
-      asm volatile("" ::: "memory");
     }
   }
 }
@@ -267,61 +291,62 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
   const int S = (S64 + 1) / 2;          // stages; the last one is half when S64 is odd
 
   // Copy sources of the current tile: a wave-uniform base per matrix (kept in
-  // scalar registers) plus 32-bit per-lane offsets. Codes: copy j of thread t
-  // fills LDS piece q = t + 256 j, i.e. row q / 4, piece q % 4, which holds
-  // the row's 16-byte K piece (q % 4) ^ bits 2-3 of the row. Rows past M / N
-  // re-read the last row (their results are never stored). In a final half
-  // stage the pieces beyond K re-read the two below them (bit j of tailmask).
+  // scalar registers) plus per-lane offsets. Loader lane t (< 128), copy j,
+  // fills LDS piece q = t + 128 j, i.e. row q / 4 = t / 4 + 32 j, piece
+  // q % 4, which holds the row's 16-byte K piece (q % 4) ^ bits 2-3 of the
+  // row (= bits 4-5 of t). Rows past M / N re-read the last row (their
+  // results are never stored). In a final half stage the pieces beyond K
+  // re-read the two below them.
   const uint8_t* a_base;
   const uint8_t* b_base;
   const uint8_t* as_base;
   const uint8_t* bs_base;
-  uint32_t a_off[T::kLA], b_off[T::kLB], as_off, bs_off, tailmask;
+  int am, bm;  // last valid row of the tile, tile-relative
+  const int r0 = (t & 127) >> 2;
+  const uint32_t c16 = (uint32_t)(((t & 3) ^ ((t >> 4) & 3)) * 16);
+  const uint32_t tail32 = c16 >= 32 ? 32u : 0u;
+  const uint32_t lda = (uint32_t)g.lda, ldb = (uint32_t)g.ldb;
+  const uint32_t lda_s = (uint32_t)g.lda_s, ldb_s = (uint32_t)g.ldb_s;
   auto set_sources = [&](int64_t grp_, int64_t m0_, int64_t n0_) {
     a_base = g.a + grp_ * g.a_gs + m0_ * g.lda;
     b_base = g.b + grp_ * g.b_gs + n0_ * g.ldb;
     as_base = g.as + grp_ * g.as_gs + m0_ * g.lda_s;
     bs_base = g.bs + grp_ * g.bs_gs + n0_ * g.ldb_s;
-    const int64_t am = g.M - 1 - m0_, bm = g.N - 1 - n0_;  // last valid row, tile-relative
-    tailmask = 0;
-#pragma unroll
-    for (int j = 0; j < T::kLA; j++) {
-      const int q = t + 256 * j, row = q >> 2, c = (q & 3) ^ ((row >> 2) & 3);
-      a_off[j] = (uint32_t)((row < am ? row : am) * g.lda + c * 16);
-      tailmask |= (c >= 2 ? 1u : 0u) << j;
-    }
-#pragma unroll
-    for (int j = 0; j < T::kLB; j++) {
-      const int q = t + 256 * j, row = q >> 2, c = (q & 3) ^ ((row >> 2) & 3);
-      b_off[j] = (uint32_t)((row < bm ? row : bm) * g.ldb + c * 16);
-      tailmask |= (c >= 2 ? 1u : 0u) << (8 + j);
-    }
-    as_off = (uint32_t)((t < am ? t : am) * g.lda_s);
-    bs_off = (uint32_t)(((t % BN) < bm ? (t % BN) : bm) * g.ldb_s);
+    const int64_t am_ = g.M - 1 - m0_, bm_ = g.N - 1 - n0_;
+    am = (int)(am_ < kBM ? am_ : kBM - 1);
+    bm = (int)(bm_ < BN ? bm_ : BN - 1);
   };
+  auto rmin = [](int r, int last) { return (uint32_t)(r < last ? r : last); };
 
   // Every stage issues the same number of copies, so every wait below is a
   // compile-time count: a stage at or past S copies one 16-byte line into
   // its slot instead (never read).
 #define G_ISSUE(SLOT, CHUNK, Y, WITH_CHUNK)                                              \
   do {                                                                                  \
-    const int y_ = (Y);                                                                 \
-    if (y_ < S) {                                                                       \
-      if (WITH_CHUNK) {                                                                 \
-        g2l16(as_base + (y_ / CS) * 16 + as_off, (CHUNK) + wl * 1024);                  \
-        g2l16(bs_base + (y_ / CS) * 16 + bs_off, (CHUNK) + T::kSABytes + wl * 1024);    \
+    if (wl < 2) {                                                                       \
+      const int y_ = (Y);                                                               \
+      if (y_ < S) {                                                                     \
+        if (WITH_CHUNK) {                                                               \
+          const uint8_t* sa_ = as_base + (y_ / CS) * 16;                                \
+          const uint8_t* sb_ = bs_base + (y_ / CS) * 16;                                \
+          _Pragma("unroll") for (int j = 0; j < 2; j++)                                 \
+            g2l16(sa_, rmin(t + 128 * j, am) * lda_s, (CHUNK) + (wl * 64 + 128 * j) * 16); \
+          _Pragma("unroll") for (int j = 0; j < 2; j++)                                 \
+            g2l16(sb_, rmin(BN == 256 ? t + 128 * j : t, bm) * ldb_s,                   \
+                  (CHUNK) + T::kSABytes + (wl * 64 + 128 * j) * 16);                    \
+        }                                                                               \
+        const uint8_t* ab_ = a_base + (int64_t)y_ * kRowBytes;                          \
+        const uint8_t* bb_ = b_base + (int64_t)y_ * kRowBytes;                          \
+        const uint32_t fix_ = (2 * y_ + 1 >= S64) ? tail32 : 0u;                        \
+        _Pragma("unroll") for (int j = 0; j < T::kLA; j++)                              \
+          g2l16(ab_, rmin(r0 + 32 * j, am) * lda + c16 - fix_, (SLOT) + (wl * 64 + 128 * j) * 16); \
+        _Pragma("unroll") for (int j = 0; j < T::kLB; j++)                              \
+          g2l16(bb_, rmin(r0 + 32 * j, bm) * ldb + c16 - fix_,                          \
+                (SLOT) + T::kABytes + (wl * 64 + 128 * j) * 16);                        \
+      } else {                                                                          \
+        _Pragma("unroll") for (int j = 0; j < T::kL + ((WITH_CHUNK) ? T::kLC : 0); j++) \
+          g2l16(g.a, 0u, (SLOT) + (wl * 64) * 16);                                      \
       }                                                                                 \
-      const uint8_t* ab_ = a_base + (int64_t)y_ * kRowBytes;                            \
-      const uint8_t* bb_ = b_base + (int64_t)y_ * kRowBytes;                            \
-      const uint32_t fix_ = (2 * y_ + 1 >= S64) ? tailmask : 0u;                        \
-      _Pragma("unroll") for (int j = 0; j < T::kLA; j++)                                \
-        g2l16(ab_ + (a_off[j] - ((fix_ >> j) & 1u) * 32u), (SLOT) + (wl * 64 + 256 * j) * 16); \
-      _Pragma("unroll") for (int j = 0; j < T::kLB; j++)                                \
-        g2l16(bb_ + (b_off[j] - ((fix_ >> (8 + j)) & 1u) * 32u),                        \
-              (SLOT) + T::kABytes + (wl * 64 + 256 * j) * 16);                          \
-    } else {                                                                            \
-      _Pragma("unroll") for (int j = 0; j < T::kL + ((WITH_CHUNK) ? 2 : 0); j++)        \
-        g2l16(g.a, (SLOT) + (wl * 64) * 16);                                            \
     }                                                                                   \
   } while (0)
 
@@ -372,16 +397,18 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
     }                                                                                   \
   } while (0)
 
-#define G_MFMAS(CA, CB, SA, SB, KB)                                                     \
+  // MFMAs of one half-stage, part [P0, P1) of it: MFMA rows i (MXFP4) or
+  // K sub-steps kt (NVFP4), each 0..3.
+#define G_MFMAS(CA, CB, SA, SB, KB, P0, P1)                                             \
   do {                                                                                  \
     if constexpr (!NV) {                                                                \
       uint32_t sa_[4], sb_[NJ];                                                         \
-      _Pragma("unroll") for (int i = 0; i < 4; i++) sa_[i] = (SA[i][0] >> (16 * (KB) + 8 * h)) & 0xffu; \
+      _Pragma("unroll") for (int i = (P0); i < (P1); i++) sa_[i] = (SA[i][0] >> (16 * (KB) + 8 * h)) & 0xffu; \
       _Pragma("unroll") for (int j = 0; j < NJ; j++) sb_[j] = (SB[j][0] >> (16 * (KB) + 8 * h)) & 0xffu; \
-      _Pragma("unroll") for (int i = 0; i < 4; i++) {                                   \
-        const i32x8 fa = {(int)CA[i].x, (int)CA[i].y, (int)CA[i].z, (int)CA[i].w, 0, 0, 0, 0}; \
+      _Pragma("unroll") for (int i = (P0); i < (P1); i++) {                             \
+        const i32x8 fa = fp4_operand(CA[i]);                                            \
         _Pragma("unroll") for (int j = 0; j < NJ; j++) {                                \
-          const i32x8 fb = {(int)CB[j].x, (int)CB[j].y, (int)CB[j].z, (int)CB[j].w, 0, 0, 0, 0}; \
+          const i32x8 fb = fp4_operand(CB[j]);                                          \
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb, fa, acc[i][j], 4, 4, 0, (int)sb_[j], \
                                                                       0, (int)sa_[i]);  \
         }                                                                               \
@@ -391,7 +418,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
       _Pragma("unroll") for (int i = 0; i < 4; i++) pa_[i] = SA[i][(KB) & (NV ? 1 : 0)] >> (16 * h); \
       _Pragma("unroll") for (int j = 0; j < NJ; j++) pb_[j] = SB[j][(KB) & (NV ? 1 : 0)] >> (16 * h); \
       NvScale na[4], nb[NJ];                                                            \
-      _Pragma("unroll") for (int kt = 0; kt < 4; kt++) {                                \
+      _Pragma("unroll") for (int kt = (P0) & ~1; kt < (P1); kt++) {                     \
         if ((kt & 1) == 0) {                                                            \
           _Pragma("unroll") for (int i = 0; i < 4; i++)                                 \
             na[i] = nv_scale(kt == 0 ? (pa_[i] & 0xffu) : ((pa_[i] >> 8) & 0xffu));     \
@@ -417,11 +444,14 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
   // Stage x = x0 + U (U compile-time, x0 a multiple of 8) sits in slot U % 4,
   // its scales in chunk (U / CS) % 2 and scale buffer U % 2, and its first
   // half-stage's fragments are in ca0 / cb0. Half-stage 0: read half-stage
-  // 1's fragments (and stage x+1's scales when its chunk is already there),
-  // run half-stage 0. Half-stage 1: wait for stage x+1, barrier, start the
-  // copy of stage x+4 into this slot (every wave is done with it), read stage
-  // x+1's first fragments (and its scales if its chunk came with it), run
-  // half-stage 1. A chunk slot is refilled at stage 4 c - 4 (c the chunk's
+  // 1's fragments (and, half-way through, stage x+1's scales when its chunk
+  // is already there), run half-stage 0. Half-stage 1: wait for stage x+1,
+  // barrier, start the copy of stage x+4 into this slot (every wave is done
+  // with it), read stage x+1's first fragments (and its scales if its chunk
+  // came with it), run half-stage 1. The LDS reads are issued on every path,
+  // also past the last stage (they then read data that is never used), so
+  // that the compiler can count them exactly and waits only for the reads a
+  // half-stage consumes. A chunk slot is refilled at stage 4 c - 4 (c the chunk's
   // index, in chunk-sized steps of CS stages): by then the last stage of the
   // chunk two back has had its scales read, in half-stage 0 of the stage
   // before it.
@@ -429,33 +459,39 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
   do {                                                                                  \
     const int x_ = x0 + (U);                                                            \
     const bool kb1_ = 2 * x_ + 1 < S64;                                                 \
-    if (kb1_) G_READ(SLOT, 1, ca1, cb1);                                                \
-    if (((U) + 1) % CS != 0 && x_ + 1 < S) G_READ_SCALES(NCHUNK, (U) + 1, NSA, NSB);    \
-    G_MFMAS(ca0, cb0, SA, SB, 0);                                                       \
-    if (kb1_) {                                                                         \
-      if (x_ + 1 < S) {                                                                 \
-        wait_lgkm0();                                                                   \
-        wait_vmcnt<2 * T::kL + (((U) + 2) % CS == 0 ? 2 : 0) + (((U) + 3) % CS == 0 ? 2 : 0)>(); \
-        lds_barrier();                                                                  \
-        G_ISSUE(LSLOT, LRCHUNK, x_ + 4, ((U) + 4) % CS == 0);                           \
-        G_READ(NSLOT, 0, ca0, cb0);                                                     \
-        if (((U) + 1) % CS == 0) G_READ_SCALES(NCHUNK, (U) + 1, NSA, NSB);              \
-      }                                                                                 \
-      G_MFMAS(ca1, cb1, SA, SB, 1);                                                     \
+    const bool next_ = x_ + 1 < S;                                                      \
+    G_READ(SLOT, 1, ca1, cb1);                                                          \
+    G_MFMAS(ca0, cb0, SA, SB, 0, 0, 2);                                                 \
+    if (((U) + 1) % CS != 0) {                                                          \
+      __builtin_amdgcn_sched_barrier(0);                                                \
+      G_READ_SCALES(NCHUNK, (U) + 1, NSA, NSB);                                         \
+      __builtin_amdgcn_sched_barrier(0);                                                \
     }                                                                                   \
+    G_MFMAS(ca0, cb0, SA, SB, 0, 2, 4);                                                 \
+    if (next_) {                                                                        \
+      wait_lgkm0();                                                                     \
+      if (wl < 2)                                                                       \
+        wait_vmcnt<2 * T::kL + (((U) + 2) % CS == 0 ? T::kLC : 0) + (((U) + 3) % CS == 0 ? T::kLC : 0)>(); \
+      lds_barrier();                                                                    \
+      G_ISSUE(LSLOT, LRCHUNK, x_ + 4, ((U) + 4) % CS == 0);                             \
+    }                                                                                   \
+    G_READ(NSLOT, 0, ca0, cb0);                                                         \
+    if (((U) + 1) % CS == 0) G_READ_SCALES(NCHUNK, (U) + 1, NSA, NSB);                  \
+    if (kb1_) G_MFMAS(ca1, cb1, SA, SB, 1, 0, 4);                                       \
   } while (0)
 
 // chunk holding stage x0 + U's scales (and its LDS address)
 #define G_CH(U) ((((U) / CS) % 2) ? chunk1 : chunk0)
 #define G_LCH(U) ((((U) / CS) % 2) ? LC1 : LC0)
 
-  // copies issued for stages 1..3, which may be in flight when stage 0 is needed
-  constexpr int kAfter0 = 3 * T::kL + (1 % CS == 0 ? 2 : 0) + (2 % CS == 0 ? 2 : 0) + (3 % CS == 0 ? 2 : 0);
+  // A tile starts with stages 0-2 in flight; stage 3 is issued once stage 0
+  // has landed, which keeps a loader wave within the 63 copies its vmcnt
+  // counter can track.
+  constexpr int kAfter0 = 2 * T::kL + (1 % CS == 0 ? T::kLC : 0) + (2 % CS == 0 ? T::kLC : 0);
   set_sources(grp, tm * kBM, tn * BN);
   G_ISSUE(L0, LC0, 0, true);
   G_ISSUE(L1, LC1, 1, 1 % CS == 0);
   G_ISSUE(L2, LC1, 2, 2 % CS == 0);
-  G_ISSUE(L3, LC1, 3, 3 % CS == 0);
   for (int64_t jt = 0;; jt++) {
     const int64_t m0 = tm * kBM, n0 = tn * BN, cgrp = grp;
 #pragma unroll
@@ -465,8 +501,9 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
 #pragma unroll
         for (int q = 0; q < 16; q++) acc[i][j][q] = 0.0f;
     if (S > 0) {
-      wait_vmcnt<kAfter0>();
+      if (wl < 2) wait_vmcnt<kAfter0>();
       lds_barrier();
+      G_ISSUE(L3, LC1, 3, 3 % CS == 0);
       G_READ(slot0, 0, ca0, cb0);
       G_READ_SCALES(chunk0, 0, sa0, sb0);
     }
@@ -481,28 +518,39 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
       if (x0 + 7 < S) G_STAGE(7, slot3, slot0, G_CH(7), G_CH(8), L3, G_LCH(11), sa1, sb1, sa0, sb0);
     }
 
-    // Every wave is done with the slots: start the next tile's first three
-    // stages, store this tile through slot 3, then start its fourth stage.
+    // Every wave is done with the slots: stage the tile's C there, let the
+    // store waves write it out, then start the next tile's first stages.
     const bool more = walk.get(jt + 1, &grp, &tm, &tn);
     wait_lgkm0();
     lds_barrier();
-    if (more) {
-      set_sources(grp, tm * kBM, tn * BN);
-      G_ISSUE(L0, LC0, 0, true);
-      G_ISSUE(L1, LC1, 1, 1 % CS == 0);
-      G_ISSUE(L2, LC1, 2, 2 % CS == 0);
-    }
     float alpha = 1.0f;
     if constexpr (NV) alpha = scalar_load_f32(g.a_ts + cgrp) * scalar_load_f32(g.b_ts + cgrp);
-    store_wave_tile<T::kWN, T::kEpiRows, OUT_BF16>(g, acc, alpha, slot3 + w * (T::kEpiRows * T::kEpiPitch), cgrp,
-                                                   m0 + wm * 128, n0 + wn * T::kWN, lane);
+    {
+      using E = Epi<T::kWN>;
+      constexpr int RR = T::kSlot / E::kRowB >= 128 ? 128 : 64;
+      auto region = [&](int k) -> uint8_t* { return k == 0 ? slot0 : k == 1 ? slot1 : k == 2 ? slot2 : slot3; };
+#pragma unroll
+      for (int round = 0; round < 128 / RR; round++) {
+        stage_wave_rows<T::kWN, RR>(acc, alpha, region(w), round, lane);
+        wait_lgkm0();
+        lds_barrier();
+        if (wl >= 2) {
+          const int sw = wl - 2;
+          store_staged_rows<T::kWN, RR, OUT_BF16>(g, region(sw), region(sw + 2), cgrp,
+                                                  m0 + sw * 128 + round * RR, n0, lane);
+        }
+        wait_lgkm0();
+        lds_barrier();
+      }
+    }
     if (!more) break;
-    wait_lgkm0();
-    lds_barrier();
-    G_ISSUE(L3, LC1, 3, 3 % CS == 0);
+    set_sources(grp, tm * kBM, tn * BN);
+    G_ISSUE(L0, LC0, 0, true);
+    G_ISSUE(L1, LC1, 1, 1 % CS == 0);
+    G_ISSUE(L2, LC1, 2, 2 % CS == 0);
   }
   // no copy into LDS may outlive the workgroup
-  wait_vmcnt<0>();
+  if (wl < 2) wait_vmcnt<0>();
 #undef G_CH
 #undef G_LCH
 #undef G_STAGE
