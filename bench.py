@@ -41,7 +41,7 @@ sys.path.insert(0, str(ROOT))
 
 METRIC = "FP4 quantize GB/s + W4A4 GEMM TFLOPS, each as % of MI355X roofline"
 PEAK_HBM_GBS = 8000.0                       # MI355X HBM3E
-PEAK_TFLOPS = {"bf16": 2500.0, "fp4": 10100.0}  # dense matrix-core peaks
+PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "fp4": 10100.0}  # dense matrix-core peaks
 ROTATE_BYTES = 600 << 20
 
 
@@ -155,12 +155,12 @@ def wl_w4a4_linear(F, inputs):
               PEAK_HBM_GBS, qa, "GB/s"),
            Op("quantize W nvfp4 4/6 (amax pre-pass + quantize)", "amax_kernel+quant_rows_kernel", "hbm", qw.bytes(),
               PEAK_HBM_GBS, qw, "GB/s"),
-           Op("gemm nvfp4 (exact bf16 dequant + bf16 MFMA)", "gemm_kernel<true, true>", "mfma", gm.flops(),
-              PEAK_TFLOPS["bf16"], gm, "TFLOP/s")]
+           Op("gemm nvfp4 (exact fp16 dequant + fp16 MFMA)", "gemm_fp4_kernel<true, 128, true>", "mfma", gm.flops(),
+              PEAK_TFLOPS["f16"], gm, "TFLOP/s")]
     cfg = {"workload": "w4a4_linear_nvfp4_four_over_six", "M": 2048, "N": 4096, "K": 4096,
            "activations": "2048x4096 bf16 N(0,1), 1% columns x30", "weight": "4096x4096 bf16 N(0,0.02)",
            "output": "bf16", "input_sets_rotated": n}
-    return ops, cfg, "nvfp4 e2m1/e4m3, bf16 MFMA fp32-acc", lambda: cpu_w4a4(d)
+    return ops, cfg, "fp4 e2m1 codes (nvfp4); f16 MFMA, f32 accumulate", lambda: cpu_w4a4(d)
 
 
 def wl_moe(F, inputs):
@@ -171,11 +171,11 @@ def wl_moe(F, inputs):
     gm = GemmCall(F, qx, qw, torch.bfloat16)
     ops = [Op("quantize W^T mxfp4 32x[2880x5760]", "quant_cols_kernel", "hbm", qw.bytes(), PEAK_HBM_GBS, qw, "GB/s"),
            Op("quantize X mxfp4 32x[512x2880]", "quant_rows_kernel", "hbm", qx.bytes(), PEAK_HBM_GBS, qx, "GB/s"),
-           Op("grouped gemm mxfp4 (scaled FP4 MFMA)", "gemm_kernel<false, true>", "mfma", gm.flops(),
+           Op("grouped gemm mxfp4 (scaled FP4 MFMA)", "gemm_fp4_kernel<false, 256, true>", "mfma", gm.flops(),
               PEAK_TFLOPS["fp4"], gm, "TFLOP/s")]
     cfg = {"workload": "moe_mxfp4_grouped", "experts": 32, "M": 512, "N": 5760, "K": 2880, "output": "bf16",
            "input_sets_rotated": n}
-    return ops, cfg, "mxfp4 e2m1/e8m0, fp4 MFMA fp32-acc", None
+    return ops, cfg, "fp4 e2m1 codes (mxfp4); fp4 MFMA, f32 accumulate", None
 
 
 def wl_training(F, inputs):
@@ -190,7 +190,7 @@ def wl_training(F, inputs):
            Op("quantize W^T nvfp4 2D 4/6", "quant_cols_kernel", "hbm", q2.bytes(), PEAK_HBM_GBS, q2, "GB/s"),
            Op("quantize G nvfp4 4/6 stochastic", "quant_rows_kernel", "hbm", q3.bytes(), PEAK_HBM_GBS, q3, "GB/s")]
     cfg = {"workload": "training_quantize_8192", "shape": [8192, 8192], "input_sets_rotated": n}
-    return ops, cfg, "nvfp4 e2m1/e4m3", None
+    return ops, cfg, "fp4 e2m1 codes (nvfp4), f32 scale arithmetic", None
 
 
 def wl_rht(F, inputs):
@@ -202,9 +202,10 @@ def wl_rht(F, inputs):
     gm = GemmCall(F, qx, qw, torch.bfloat16)
     ops = [Op("quantize X nvfp4 4/6 RHT", "quant_rows_kernel", "hbm", qx.bytes(), PEAK_HBM_GBS, qx, "GB/s"),
            Op("quantize W^T nvfp4 4/6 RHT", "quant_cols_kernel", "hbm", qw.bytes(), PEAK_HBM_GBS, qw, "GB/s"),
-           Op("gemm nvfp4", "gemm_kernel<true, true>", "mfma", gm.flops(), PEAK_TFLOPS["bf16"], gm, "TFLOP/s")]
+           Op("gemm nvfp4 (exact fp16 dequant + fp16 MFMA)", "gemm_fp4_kernel<true, 128, true>", "mfma", gm.flops(),
+              PEAK_TFLOPS["f16"], gm, "TFLOP/s")]
     cfg = {"workload": "rht_activation_nvfp4", "M": 16384, "N": 12288, "K": 4096, "input_sets_rotated": n}
-    return ops, cfg, "nvfp4 e2m1/e4m3, bf16 MFMA fp32-acc", None
+    return ops, cfg, "fp4 e2m1 codes (nvfp4); f16 MFMA, f32 accumulate", None
 
 
 WORKLOADS = {"w4a4_linear": wl_w4a4_linear, "moe": wl_moe, "training": wl_training, "rht": wl_rht}
@@ -222,7 +223,7 @@ def cpu_w4a4(d):
     w = inputs.bf16_bits(d["w"].cpu())
     M, K = a.shape
     N = w.shape[0]
-    rows = 128
+    rows = 1024
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         qa = O.quantize(a, O.NVFP4, flags=O.FOUR_OVER_SIX)
@@ -244,17 +245,28 @@ def cpu_w4a4(d):
 
 # ---------------------------------------------------------------------------
 def source_digest():
+    """Digest of the device-code sources (kernels and their headers): HBM
+    counters taken on other kernel sources are not reported."""
     h = hashlib.sha256()
     for p in sorted((ROOT / "block_scaled_fp4_amax_amd" / "csrc").iterdir()):
-        h.update(p.read_bytes())
+        if p.suffix in (".hip", ".h"):
+            h.update(p.read_bytes())
     return h.hexdigest()[:16]
 
 
+def kernel_label(rocprof_name):
+    """'void fp4impl::gemm_fp4_kernel<true, 128, true>(fp4impl::GemmArgs)' -> 'gemm_fp4_kernel<true, 128, true>'"""
+    n = rocprof_name.split("(")[0]
+    n = n[len("void "):] if n.startswith("void ") else n
+    return n.split("::")[-1] if "<" not in n else n[n.rfind("::", 0, n.index("<")) + 2:]
+
+
 def traffic_for(op_kernel, workload):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources; else None."""
+    """HBM bytes per launch of one kernel, from the committed rocprofv3
+    counter summary, if it was taken on the current kernel sources; else
+    None (also for ops made of several kernels)."""
     p = ROOT / "profiles" / "hbm_traffic.json"
-    if not p.exists():
+    if not p.exists() or "+" in op_kernel:
         return None
     try:
         t = json.loads(p.read_text())
@@ -264,6 +276,63 @@ def traffic_for(op_kernel, workload):
         return None
     e = t.get("workloads", {}).get(workload, {}).get(op_kernel)
     return e.get("bytes_per_launch") if e else None
+
+
+def read_pmc(dirpath, counter):
+    """{kernel label: [value per dispatch]} from a rocprofv3 --pmc csv tree."""
+    import csv
+    out = {}
+    for f in Path(dirpath).rglob("*counter_collection.csv"):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    out.setdefault(kernel_label(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return out
+
+
+def ingest_pmc(base, copy_bytes, commands):
+    """Turn FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch) into HBM bytes per
+    launch, each counter scaled by what it reads for a plain device copy of
+    copy_bytes. Layout: base/<workload>/{fetch,write}, base/copy/{fetch,write}."""
+    base = Path(base)
+    cf = read_pmc(base / "copy" / "fetch", "FETCH_SIZE")
+    cw = read_pmc(base / "copy" / "write", "WRITE_SIZE")
+    ck = [k for k in cf if "copy" in k.lower()]
+    if not ck:
+        raise SystemExit("no copy kernel in the calibration run")
+    fetch_kib = float(np.median(cf[ck[0]]))
+    write_kib = float(np.median(cw[ck[0]]))
+    f_fetch, f_write = copy_bytes / (fetch_kib * 1024.0), copy_bytes / (write_kib * 1024.0)
+    out = {"source_digest": source_digest(),
+           "calibration": {"copy_kernel": ck[0], "copy_bytes": copy_bytes, "fetch_kib": fetch_kib,
+                           "write_kib": write_kib, "fetch_factor": round(f_fetch, 4), "write_factor": round(f_write, 4)},
+           "commands": commands, "workloads": {}}
+    for wdir in sorted(p for p in base.iterdir() if p.is_dir() and p.name != "copy"):
+        fe, wr = read_pmc(wdir / "fetch", "FETCH_SIZE"), read_pmc(wdir / "write", "WRITE_SIZE")
+        ent = {}
+        for k in fe:
+            if k not in wr:
+                continue
+            fb = float(np.mean(fe[k])) * 1024.0 * f_fetch
+            wb = float(np.mean(wr[k])) * 1024.0 * f_write
+            ent[k] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "bytes_per_launch": round(fb + wb),
+                      "dispatches": len(fe[k])}
+        out["workloads"][wdir.name] = ent
+    dst = ROOT / "profiles" / "hbm_traffic.json"
+    dst.parent.mkdir(exist_ok=True)
+    dst.write_text(json.dumps(out, indent=1) + "\n")
+    print(f"wrote {dst}")
+
+
+def calibrate_copy(nbytes, reps=5):
+    """A plain device-to-device copy of nbytes, for scaling HBM counters."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": nbytes, "launches": reps}), flush=True)
 
 
 def run(workload, steps, warmup, with_cpu):
@@ -333,7 +402,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="w4a4_linear", choices=[*WORKLOADS, "all"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (HBM counter calibration)")
+    ap.add_argument("--ingest-pmc", default=None, metavar="DIR",
+                    help="write profiles/hbm_traffic.json from FETCH_SIZE / WRITE_SIZE runs under DIR (no GPU)")
+    ap.add_argument("--copy-bytes", type=int, default=512 << 20)
+    ap.add_argument("--pmc-command", action="append", default=[], help="command line recorded with the counters")
     args = ap.parse_args()
+    if args.ingest_pmc:
+        ingest_pmc(args.ingest_pmc, args.copy_bytes, args.pmc_command)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
@@ -342,6 +420,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     names = list(WORKLOADS) if args.workload == "all" else [args.workload]
     for nm in names:
         line = run(nm, args.steps, args.warmup, with_cpu=not args.no_cpu_baseline)
