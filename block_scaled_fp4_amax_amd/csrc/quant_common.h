@@ -113,7 +113,15 @@ __device__ __forceinline__ float tensor_scale_prologue(const QuantArgs& a, int64
   } else {
     float m = 0.0f;
     const float* p = a.partials + b * a.nparts;
-    for (int i = threadIdx.x; i < a.nparts; i += blockDim.x) m = __builtin_fmaxf(m, p[i]);
+    if ((a.nparts & 3) == 0) {
+      // 16-byte loads (the workspace is 16-byte aligned)
+      for (int i = 4 * threadIdx.x; i < a.nparts; i += 4 * blockDim.x) {
+        const float4 q = *reinterpret_cast<const float4*>(p + i);
+        m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fmaxf(q.x, q.y), __builtin_fmaxf(q.z, q.w)));
+      }
+    } else {
+      for (int i = threadIdx.x; i < a.nparts; i += blockDim.x) m = __builtin_fmaxf(m, p[i]);
+    }
 #pragma unroll
     for (int s = 32; s >= 1; s >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, s, 64));
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;

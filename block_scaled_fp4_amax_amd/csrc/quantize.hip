@@ -102,15 +102,47 @@ __global__ __launch_bounds__(256) void amax_kernel(QuantArgs a) {
 // ------------------------------------------------------------------------
 // Row-major quantization
 // ------------------------------------------------------------------------
+// 16 consecutive input values as loaded (two 16-byte loads of bf16, four of
+// fp32), so that the loads can be in flight during the tensor-scale prologue.
+template <typename TIn>
+struct Raw16;
+template <>
+struct Raw16<uint16_t> {
+  uint4 w0, w1;
+  __device__ __forceinline__ void load(const uint16_t* p) {
+    w0 = reinterpret_cast<const uint4*>(p)[0];
+    w1 = reinterpret_cast<const uint4*>(p)[1];
+  }
+  __device__ __forceinline__ void unpack(float (&v)[16]) const {
+    const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      v[2 * i] = bf16_lo(w[i]);
+      v[2 * i + 1] = bf16_hi(w[i]);
+    }
+  }
+};
+template <>
+struct Raw16<float> {
+  float4 f[4];
+  __device__ __forceinline__ void load(const float* p) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) f[i] = reinterpret_cast<const float4*>(p)[i];
+  }
+  __device__ __forceinline__ void unpack(float (&v)[16]) const {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      v[4 * i] = f[i].x;
+      v[4 * i + 1] = f[i].y;
+      v[4 * i + 2] = f[i].z;
+      v[4 * i + 3] = f[i].w;
+    }
+  }
+};
+
 template <typename TIn, bool NV, bool FOS, bool B2D, bool SR, bool RHT>
 __global__ __launch_bounds__(256) void quant_rows_kernel(QuantArgs a) {
   const int64_t b = blockIdx.z;
-  float St = 1.0f, k6 = 0.0f, k4 = 0.0f;
-  if constexpr (NV) {
-    St = tensor_scale_prologue<FOS>(a, b);
-    k6 = 1.0f / (6.0f * St);
-    k4 = 1.0f / (4.0f * St);
-  }
   const int64_t upr = a.C >> 4;  // 16-value units per row
   int64_t row, cu;
   if constexpr (B2D) {
@@ -122,12 +154,20 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(QuantArgs a) {
     cu = u - row * upr;
   }
   // validity is uniform across every group of lanes that exchanges data
-  if (row >= a.R || cu >= upr) return;
+  const bool valid = row < a.R && cu < upr;
+  Raw16<TIn> raw;
+  if (valid) raw.load(reinterpret_cast<const TIn*>(a.x) + b * a.bs_x + row * a.ld_x + cu * 16);
 
-  const TIn* xp = reinterpret_cast<const TIn*>(a.x) + b * a.bs_x + row * a.ld_x + cu * 16;
+  float St = 1.0f, k6 = 0.0f, k4 = 0.0f;
+  if constexpr (NV) {
+    St = tensor_scale_prologue<FOS>(a, b);  // every lane takes part
+    k6 = 1.0f / (6.0f * St);
+    k4 = 1.0f / (4.0f * St);
+  }
+  if (!valid) return;
+
   float v[16];
-  load8<TIn>(xp, v);
-  load8<TIn>(xp + 8, v + 8);
+  raw.unpack(v);
   if constexpr (RHT) rht16(v, a.signs);
 
   float amax = max_abs16(v);
@@ -250,12 +290,6 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(QuantArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t cst[kColsN * kColsPitch];
   __shared__ __attribute__((aligned(16))) uint8_t sst[kColsN * kColsScales];
   const int64_t b = blockIdx.z;
-  float St = 1.0f, k6 = 0.0f, k4 = 0.0f;
-  if constexpr (NV) {
-    St = tensor_scale_prologue<FOS>(a, b);
-    k6 = 1.0f / (6.0f * St);
-    k4 = 1.0f / (4.0f * St);
-  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane & 1, g = lane >> 1;
   const int nl = (g & 15) * 8;                         // patch columns, workgroup-relative
@@ -265,9 +299,16 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(QuantArgs a) {
   // A vertical lane pair (an MXFP4 block) and a horizontal one (a 16 x 16
   // tile) are valid together: rows come in whole blocks, columns in whole
   // tiles.
-  if (n0 < a.src_cols && k0 < a.src_rows) {
-    Patch16x8<TIn> t;
-    t.load(reinterpret_cast<const TIn*>(a.x) + b * a.bs_x + k0 * a.ld_x + n0, a.ld_x);
+  const bool valid = n0 < a.src_cols && k0 < a.src_rows;
+  Patch16x8<TIn> t;
+  if (valid) t.load(reinterpret_cast<const TIn*>(a.x) + b * a.bs_x + k0 * a.ld_x + n0, a.ld_x);
+  float St = 1.0f, k6 = 0.0f, k4 = 0.0f;
+  if constexpr (NV) {
+    St = tensor_scale_prologue<FOS>(a, b);  // while the loads are in flight
+    k6 = 1.0f / (6.0f * St);
+    k4 = 1.0f / (4.0f * St);
+  }
+  if (valid) {
     const uint64_t Lrow = (uint64_t)b * (uint64_t)a.R;
     uint8_t* crow = cst + nl * kColsPitch + (kl >> 1);
     uint8_t* srow = sst + nl * kColsScales;
