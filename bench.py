@@ -244,13 +244,32 @@ def cpu_w4a4(d):
 
 
 # ---------------------------------------------------------------------------
-def source_digest():
-    """Digest of the device-code sources (kernels and their headers): HBM
-    counters taken on other kernel sources are not reported."""
+KERNEL_SOURCES = {  # device sources each kernel family is built from
+    "gemm": ["gemm.hip", "fp4_device.h", "launch.h"],
+    "quant": ["quantize.hip", "quant_common.h", "fp4_device.h", "launch.h"],
+    "dequant": ["dequantize.hip", "fp4_device.h", "launch.h"],
+}
+
+
+def kernel_family(label):
+    if label.startswith("gemm"):
+        return "gemm"
+    if label.startswith("dequant"):
+        return "dequant"
+    return "quant"
+
+
+def source_digest(label=None):
+    """Digest of the device sources a kernel is built from (all device
+    sources when label is None): HBM counters taken on other sources are
+    not reported."""
+    csrc = ROOT / "block_scaled_fp4_amax_amd" / "csrc"
+    names = sorted({n for v in KERNEL_SOURCES.values() for n in v}) if label is None else \
+        KERNEL_SOURCES[kernel_family(label)]
     h = hashlib.sha256()
-    for p in sorted((ROOT / "block_scaled_fp4_amax_amd" / "csrc").iterdir()):
-        if p.suffix in (".hip", ".h"):
-            h.update(p.read_bytes())
+    for n in names:
+        h.update(n.encode())
+        h.update((csrc / n).read_bytes())
     return h.hexdigest()[:16]
 
 
@@ -272,10 +291,10 @@ def traffic_for(op_kernel, workload):
         t = json.loads(p.read_text())
     except ValueError:
         return None
-    if t.get("source_digest") != source_digest():
-        return None
     e = t.get("workloads", {}).get(workload, {}).get(op_kernel)
-    return e.get("bytes_per_launch") if e else None
+    if not e or e.get("source_digest") != source_digest(op_kernel):
+        return None
+    return e.get("bytes_per_launch")
 
 
 def read_pmc(dirpath, counter):
@@ -303,8 +322,7 @@ def ingest_pmc(base, copy_bytes, commands):
     fetch_kib = float(np.median(cf[ck[0]]))
     write_kib = float(np.median(cw[ck[0]]))
     f_fetch, f_write = copy_bytes / (fetch_kib * 1024.0), copy_bytes / (write_kib * 1024.0)
-    out = {"source_digest": source_digest(),
-           "calibration": {"copy_kernel": ck[0], "copy_bytes": copy_bytes, "fetch_kib": fetch_kib,
+    out = {"calibration": {"copy_kernel": ck[0], "copy_bytes": copy_bytes, "fetch_kib": fetch_kib,
                            "write_kib": write_kib, "fetch_factor": round(f_fetch, 4), "write_factor": round(f_write, 4)},
            "commands": commands, "workloads": {}}
     for wdir in sorted(p for p in base.iterdir() if p.is_dir() and p.name != "copy"):
@@ -316,7 +334,7 @@ def ingest_pmc(base, copy_bytes, commands):
             fb = float(np.mean(fe[k])) * 1024.0 * f_fetch
             wb = float(np.mean(wr[k])) * 1024.0 * f_write
             ent[k] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "bytes_per_launch": round(fb + wb),
-                      "dispatches": len(fe[k])}
+                      "dispatches": len(fe[k]), "source_digest": source_digest(k) if "<" in k else None}
         out["workloads"][wdir.name] = ent
     dst = ROOT / "profiles" / "hbm_traffic.json"
     dst.parent.mkdir(exist_ok=True)
