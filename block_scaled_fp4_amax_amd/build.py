@@ -37,6 +37,13 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-source flags. gemm.hip: LLVM's machine-sink pass would move a stage's
+# first-half MFMAs past the workgroup barrier into the next block (their
+# results are only used there), so the wave would wait at the barrier with its
+# matrix core idle; the kernel's order is the intended schedule.
+SOURCE_FLAGS = {"gemm.hip": ["-mllvm", "-disable-machine-sink"]}
+
+
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -54,7 +61,7 @@ def build(verbose: bool = False) -> Path:
         obj = BUILD_DIR / (src + ".o")
         objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [hipcc, *HIPCC_FLAGS, *lang, "-c", str(CSRC / src), "-o", str(obj)]
+        cmd = [hipcc, *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), *lang, "-c", str(CSRC / src), "-o", str(obj)]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))

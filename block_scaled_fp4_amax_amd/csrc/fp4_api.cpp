@@ -255,9 +255,13 @@ fp4_status fp4_gemm(int32_t format, int64_t groups, int64_t M, int64_t N, int64_
                      b_scales_group_stride < 0 || c_group_stride < (M - 1) * ldc + N))
     return FP4_ERR_INVALID;
   if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || lda % 16 != 0 || ldb % 16 != 0) return FP4_ERR_ALIGN;
-  // per-group operand panels are addressed with 32-bit offsets
+  // per-group operand panels are addressed with 32-bit offsets, and a
+  // 256-row tile's offsets stay below 2^31 (row pitches below 8 MiB)
   if (M * lda >= (int64_t(1) << 31) || N * ldb >= (int64_t(1) << 31) || M * lda_scales >= (int64_t(1) << 31) ||
       N * ldb_scales >= (int64_t(1) << 31))
+    return FP4_ERR_UNSUPPORTED;
+  if (lda >= (int64_t(1) << 23) || ldb >= (int64_t(1) << 23) || lda_scales >= (int64_t(1) << 23) ||
+      ldb_scales >= (int64_t(1) << 23))
     return FP4_ERR_UNSUPPORTED;
   if (groups > 1 && (a_group_stride % 16 != 0 || b_group_stride % 16 != 0)) return FP4_ERR_ALIGN;
   if (!aligned(c, c_dtype == FP4_BF16 ? 2 : 4)) return FP4_ERR_ALIGN;

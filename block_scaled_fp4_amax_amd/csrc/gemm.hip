@@ -28,17 +28,20 @@
 // keeps operand panels within one XCD's L2.
 //
 // Operand staging is shaped by the number of L2 requests, not by bytes: a
-// stage covers 128 K values, so each row contributes one 64-byte segment
-// (four lanes of a direct-to-LDS copy), and the scale bytes of a row are
-// copied 16 at a time, covering four stages (MXFP4) or two (NVFP4). Four
-// stages are in flight in a ring of distinct LDS arrays, plus two scale
-// chunks. Within a row the four 16-byte pieces are rotated by bits 2-3 of
-// the row so that each 16-lane group of a ds_read_b128 hits 16 distinct bank
-// groups. A wave reads the next half-stage's fragments while its MFMAs on
-// the current one run. The B matrix feeds the MFMA's first operand and A the
-// second, so lane l holds C[m = l % 32][n = 8 (q / 4) + 4 (l / 32) + q % 4].
-// The output goes through an LDS buffer (the fourth stage slot, free between
-// tiles) so that global stores write whole row segments.
+// stage covers 128 K values, so each row contributes one 64-byte segment,
+// and the scale bytes of a row are copied 16 at a time, covering four stages
+// (MXFP4) or two (NVFP4). Stages move global -> LDS with direct-to-LDS
+// buffer loads (16 bytes per lane) whose range check against the tile's rows
+// turns rows past M or N into zeros. All four waves copy, each a quarter of
+// a stage, spread over the MFMAs of a half-stage so that the copies never
+// hold a wave's matrix core idle. Four stages are in flight in a ring of LDS
+// slots, plus two scale chunks. Within a row the four 16-byte pieces are
+// rotated by bits 2-3 of the row so that each 16-lane group of a
+// ds_read_b128 hits 16 distinct bank groups. A wave reads the next
+// half-stage's fragments while its MFMAs on the current one run. The B
+// matrix feeds the MFMA's first operand and A the second, so lane l holds
+// C[m = l % 32][n = 8 (q / 4) + 4 (l / 32) + q % 4]. The output goes through
+// the (then idle) stage slots so that global stores write whole row segments.
 #include "fp4_device.h"
 #include "launch.h"
 
@@ -55,6 +58,12 @@ constexpr int kBM = 256;
 constexpr int kBK = 128;             // K values per stage
 constexpr int kRowBytes = kBK / 2;   // code bytes per row per stage
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// voffset addend that puts every lane of a copy out of range (a stage past
+// the end of K: its copies land zeros in a slot that is never read)
+constexpr uint32_t kPastEnd = 0x80000000u;
+
 template <bool NV, int BN>
 struct Tile {
   static constexpr int kABytes = kBM * kRowBytes;
@@ -64,31 +73,39 @@ struct Tile {
   static constexpr int kSABytes = kBM * 16;  // scale chunk: 16 bytes per row
   static constexpr int kSBBytes = 256 * 16;  // (rows of a 128-wide B tile are loaded twice)
   static constexpr int kChunk = kSABytes + kSBBytes;
+  static constexpr int kChunk0 = 4 * kSlot;  // LDS offset of scale chunk 0; chunk 1 follows
+  static constexpr int kLds = 4 * kSlot + 2 * kChunk;
   static constexpr int kWN = BN / 2;         // wave tile width
   static constexpr int kNJ = kWN / 32;       // MFMA tiles across a wave
-  // Waves 0 and 1 issue every copy (16 bytes per lane per copy); waves 2
-  // and 3 issue every store of C. The vmcnt counter is per wave, so the
-  // copies are never waited for behind stores, nor the stores at all.
-  static constexpr int kLA = kABytes / 2048; // copies per loader lane per stage
-  static constexpr int kLB = kBBytes / 2048;
-  static constexpr int kL = kLA + kLB;
-  static constexpr int kLC = 4;              // copies per loader lane for a scale chunk
+  // A copy moves 1 KB (64 lanes x 16 bytes). Wave w takes the 1 KB blocks
+  // w, w + 4, w + 8, ... of a stage slot and of a scale chunk.
+  static constexpr int kLW = kSlot / 1024 / 4;     // per wave per stage
+  static constexpr int kLWA = kABytes / 1024 / 4;  // of which A rows
+  static constexpr int kLCW = kChunk / 1024 / 4;   // per wave per scale chunk
 };
 
-// Direct-to-LDS copy of 16 bytes per lane from base + off (base
-// wave-uniform, in scalar registers; off a 32-bit lane offset): lane i's
-// bytes land at LDS address lds + 16 i (lds wave-uniform, passed in m0). Written as inline
-// assembly so that the compiler, which cannot match the copies in flight to
-// the stage slots, adds no vmcnt waits of its own before LDS reads: every
-// wait on these copies is explicit below. The instruction has no output
+// Raw buffer resource over [base, base + bytes): loads past its end return
+// zeros (gfx9 descriptor: 48-bit base, stride 0, record count in bytes,
+// 32-bit untyped data format).
+__device__ __forceinline__ i32x4 buffer_rsrc(const uint8_t* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  return i32x4{(int)(uint32_t)b, (int)(uint32_t)((b >> 32) & 0xffffu), (int)bytes, 0x00020000};
+}
+
+// Direct-to-LDS copy of 16 bytes per lane: lane i reads the buffer at byte
+// voff (zeros when its 16 bytes lie past the buffer's end) and its bytes land
+// at LDS address lds + 16 i (lds wave-uniform, passed in m0). Written as
+// inline assembly so that the compiler, which cannot match the copies in
+// flight to the stage slots, adds no vmcnt waits of its own before LDS reads:
+// every wait on these copies is explicit below. The instruction has no output
 // register; m0 is not otherwise used by this kernel.
-__device__ __forceinline__ void g2l16(const void* base, uint32_t off, uint32_t lds) {
+__device__ __forceinline__ void b2l16(const i32x4& rsrc, uint32_t voff, uint32_t lds) {
   asm volatile(
       "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
       :
-      : "v"(off), "s"(base), "s"(lds)
+      : "v"(voff), "s"(rsrc), "s"(lds)
       : "memory");
 }
 // Scalar (wave-uniform) fp32 load, completed inside the statement. A vector
@@ -218,21 +235,22 @@ __device__ __forceinline__ void stage_wave_rows(const f32x16 (&acc)[4][WN / 32],
   }
 }
 
-// Store wave s (= wave 2 + s) writes rows s*128 + round*RR + [0, RR) of the
-// workgroup tile: each row joins the staged blocks of waves s (columns
-// [0, WN)) and s + 2 (columns [WN, 2 WN)); a lane converts 8 consecutive
-// values and writes them in one piece, consecutive lanes along the row.
-template <int WN, int RR, bool OUT_BF16>
+// Wave s writes rows row0 + [0, NR) of a round's staged blocks: each row
+// joins the staged blocks of the waves with wm = s & 1 (columns [0, WN) from
+// reg_lo, [WN, 2 WN) from reg_hi) and goes to output row m_base + row; a lane
+// converts 8 consecutive values and writes them in one piece, consecutive
+// lanes along the row.
+template <int WN, int NR, bool OUT_BF16>
 __device__ __forceinline__ void store_staged_rows(const GemmArgs& g, const uint8_t* reg_lo, const uint8_t* reg_hi,
-                                                  int64_t grp, int64_t m_base, int64_t n0, int lane) {
+                                                  int row0, int64_t grp, int64_t m_base, int64_t n0, int lane) {
   using E = Epi<WN>;
   constexpr int kGPR = WN / 8;  // 8-value groups per row per block
   constexpr int kES = OUT_BF16 ? 2 : 4;
   const bool vec = g.c_vec_ok;
 #pragma unroll 2
-  for (int c0 = 0; c0 < RR * 2 * kGPR; c0 += 64) {
+  for (int c0 = 0; c0 < NR * 2 * kGPR; c0 += 64) {
     const int c = c0 + lane;
-    const int row = c / (2 * kGPR), k = c % (2 * kGPR);
+    const int row = row0 + c / (2 * kGPR), k = c % (2 * kGPR);
     const int wn = k / kGPR, p = k % kGPR;
     const uint8_t* rp = (wn ? reg_hi : reg_lo) + row * E::kRowB;
     const float4 v0 = *reinterpret_cast<const float4*>(rp + (((2 * p) ^ (row & E::kSwz)) * 16));
@@ -269,12 +287,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
   using T = Tile<NV, BN>;
   constexpr int NJ = T::kNJ;
   constexpr int CS = T::kCS;
-  __shared__ __attribute__((aligned(16))) uint8_t slot0[T::kSlot];
-  __shared__ __attribute__((aligned(16))) uint8_t slot1[T::kSlot];
-  __shared__ __attribute__((aligned(16))) uint8_t slot2[T::kSlot];
-  __shared__ __attribute__((aligned(16))) uint8_t slot3[T::kSlot];
-  __shared__ __attribute__((aligned(16))) uint8_t chunk0[T::kChunk];
-  __shared__ __attribute__((aligned(16))) uint8_t chunk1[T::kChunk];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[T::kLds];
 
   const TileWalk walk((g.M + kBM - 1) / kBM, (g.N + BN - 1) / BN, g.groups);
   int64_t grp, tm, tn;
@@ -284,70 +297,66 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
   const int wm = w & 1, wn = w >> 1;
   const int r32 = lane & 31, h = lane >> 5;
   const uint32_t wl = __builtin_amdgcn_readfirstlane(w);  // the wave index, in a scalar register
-  // LDS addresses of the copy targets
-  const uint32_t L0 = lds_u32(slot0), L1 = lds_u32(slot1), L2 = lds_u32(slot2), L3 = lds_u32(slot3);
-  const uint32_t LC0 = lds_u32(chunk0), LC1 = lds_u32(chunk1);
+  const uint32_t L = lds_u32(lds);      // LDS address of the slot ring
   const int S64 = (int)(g.K / 64);      // 64-K half-stages
   const int S = (S64 + 1) / 2;          // stages; the last one is half when S64 is odd
 
-  // Copy sources of the current tile: a wave-uniform base per matrix (kept in
-  // scalar registers) plus per-lane offsets. Loader lane t (< 128), copy j,
-  // fills LDS piece q = t + 128 j, i.e. row q / 4 = t / 4 + 32 j, piece
-  // q % 4, which holds the row's 16-byte K piece (q % 4) ^ bits 2-3 of the
-  // row (= bits 4-5 of t). Rows past M / N re-read the last row (their
-  // results are never stored). In a final half stage the pieces beyond K
-  // re-read the two below them.
-  const uint8_t* a_base;
-  const uint8_t* b_base;
-  const uint8_t* as_base;
-  const uint8_t* bs_base;
-  int am, bm;  // last valid row of the tile, tile-relative
-  const int r0 = (t & 127) >> 2;
-  const uint32_t c16 = (uint32_t)(((t & 3) ^ ((t >> 4) & 3)) * 16);
-  const uint32_t tail32 = c16 >= 32 ? 32u : 0u;
+  // Copy sources. Lane l of a 1 KB block fills LDS piece l % 4 of the
+  // block's row l / 4 with the row's 16-byte K piece (l % 4) ^ (bits 2-3 of
+  // the row) = (l % 4) ^ (bits 4-5 of l), blocks starting at multiples of
+  // 16 rows. Code block q < 16 holds A rows 16 q + [0, 16), block q >= 16 B
+  // rows 16 (q - 16) + [0, 16); scale-chunk blocks hold 64 rows of 16 bytes,
+  // four of A, then four of B (a 128-row B tile's rows twice). The lane
+  // offsets are fixed for the kernel; a tile sets four buffer resources whose
+  // size ends at its last valid row, and a stage adds its K offset.
   const uint32_t lda = (uint32_t)g.lda, ldb = (uint32_t)g.ldb;
-  const uint32_t lda_s = (uint32_t)g.lda_s, ldb_s = (uint32_t)g.ldb_s;
+  const uint32_t piece = (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) * 16);
+  uint32_t voff[T::kLW];
+#pragma unroll
+  for (int j = 0; j < T::kLW; j++) {
+    const int q = w + 4 * j;
+    voff[j] = j < T::kLWA ? (uint32_t)(16 * q + (lane >> 2)) * lda + piece
+                          : (uint32_t)(16 * (q - 16) + (lane >> 2)) * ldb + piece;
+  }
+  const uint32_t voffs_a = (uint32_t)(64 * w + lane) * (uint32_t)g.lda_s;
+  const uint32_t voffs_b = (uint32_t)((64 * w + lane) & (BN - 1)) * (uint32_t)g.ldb_s;
+  i32x4 ra, rb, rsa, rsb;
   auto set_sources = [&](int64_t grp_, int64_t m0_, int64_t n0_) {
-    a_base = g.a + grp_ * g.a_gs + m0_ * g.lda;
-    b_base = g.b + grp_ * g.b_gs + n0_ * g.ldb;
-    as_base = g.as + grp_ * g.as_gs + m0_ * g.lda_s;
-    bs_base = g.bs + grp_ * g.bs_gs + n0_ * g.ldb_s;
-    const int64_t am_ = g.M - 1 - m0_, bm_ = g.N - 1 - n0_;
-    am = (int)(am_ < kBM ? am_ : kBM - 1);
-    bm = (int)(bm_ < BN ? bm_ : BN - 1);
+    const int64_t rows_a = g.M - m0_ < kBM ? g.M - m0_ : kBM;
+    const int64_t rows_b = g.N - n0_ < BN ? g.N - n0_ : BN;
+    ra = buffer_rsrc(g.a + grp_ * g.a_gs + m0_ * g.lda, (uint32_t)(rows_a * g.lda));
+    rb = buffer_rsrc(g.b + grp_ * g.b_gs + n0_ * g.ldb, (uint32_t)(rows_b * g.ldb));
+    rsa = buffer_rsrc(g.as + grp_ * g.as_gs + m0_ * g.lda_s, (uint32_t)(rows_a * g.lda_s));
+    rsb = buffer_rsrc(g.bs + grp_ * g.bs_gs + n0_ * g.ldb_s, (uint32_t)(rows_b * g.ldb_s));
   };
-  auto rmin = [](int r, int last) { return (uint32_t)(r < last ? r : last); };
 
-  // Every stage issues the same number of copies, so every wait below is a
-  // compile-time count: a stage at or past S copies one 16-byte line into
-  // its slot instead (never read).
-#define G_ISSUE(SLOT, CHUNK, Y, WITH_CHUNK)                                              \
+  // Copy k of a stage whose K offsets are YO (codes) and YOS (scale chunk),
+  // into slot LSLOT and, with WITH_CHUNK, scale chunk LCHUNK (LDS
+  // addresses): the chunk's copies first, then A's, then B's. k and
+  // WITH_CHUNK are compile-time after unrolling.
+#define G_COPY(LSLOT, LCHUNK, YO, YOS, WITH_CHUNK, K)                                   \
   do {                                                                                  \
-    if (wl < 2) {                                                                       \
-      const int y_ = (Y);                                                               \
-      if (y_ < S) {                                                                     \
-        if (WITH_CHUNK) {                                                               \
-          const uint8_t* sa_ = as_base + (y_ / CS) * 16;                                \
-          const uint8_t* sb_ = bs_base + (y_ / CS) * 16;                                \
-          _Pragma("unroll") for (int j = 0; j < 2; j++)                                 \
-            g2l16(sa_, rmin(t + 128 * j, am) * lda_s, (CHUNK) + (wl * 64 + 128 * j) * 16); \
-          _Pragma("unroll") for (int j = 0; j < 2; j++)                                 \
-            g2l16(sb_, rmin(BN == 256 ? t + 128 * j : t, bm) * ldb_s,                   \
-                  (CHUNK) + T::kSABytes + (wl * 64 + 128 * j) * 16);                    \
-        }                                                                               \
-        const uint8_t* ab_ = a_base + (int64_t)y_ * kRowBytes;                          \
-        const uint8_t* bb_ = b_base + (int64_t)y_ * kRowBytes;                          \
-        const uint32_t fix_ = (2 * y_ + 1 >= S64) ? tail32 : 0u;                        \
-        _Pragma("unroll") for (int j = 0; j < T::kLA; j++)                              \
-          g2l16(ab_, rmin(r0 + 32 * j, am) * lda + c16 - fix_, (SLOT) + (wl * 64 + 128 * j) * 16); \
-        _Pragma("unroll") for (int j = 0; j < T::kLB; j++)                              \
-          g2l16(bb_, rmin(r0 + 32 * j, bm) * ldb + c16 - fix_,                          \
-                (SLOT) + T::kABytes + (wl * 64 + 128 * j) * 16);                        \
-      } else {                                                                          \
-        _Pragma("unroll") for (int j = 0; j < T::kL + ((WITH_CHUNK) ? T::kLC : 0); j++) \
-          g2l16(g.a, 0u, (SLOT) + (wl * 64) * 16);                                      \
-      }                                                                                 \
+    const int k_ = (K);                                                                 \
+    const int q_ = k_ - ((WITH_CHUNK) ? T::kLCW : 0);                                   \
+    if (q_ < 0) {                                                                       \
+      if (k_ == 0) b2l16(rsa, voffs_a + (YOS), (LCHUNK) + wl * 1024);                   \
+      else b2l16(rsb, voffs_b + (YOS), (LCHUNK) + T::kSABytes + wl * 1024);             \
+    } else {                                                                            \
+      b2l16(q_ < T::kLWA ? ra : rb, voff[q_] + (YO), (LSLOT) + (wl + 4 * q_) * 1024);  \
     }                                                                                   \
+  } while (0)
+  // K offsets of stage Y; a stage at or past S reads nothing (every lane out
+  // of range), so that every stage issues the same number of copies and every
+  // wait below is a compile-time count.
+#define G_YO(Y) ((Y) < S ? (uint32_t)(Y) * kRowBytes : kPastEnd)
+#define G_YOS(Y) ((Y) < S ? (uint32_t)((Y) / CS) * 16 : kPastEnd)
+  // every copy of stage Y at once
+#define G_ISSUE(LSLOT, LCHUNK, Y, WITH_CHUNK)                                            \
+  do {                                                                                  \
+    const int yi_ = (Y);                                                                \
+    const uint32_t yo_ = G_YO(yi_), yos_ = G_YOS(yi_);                                  \
+    _Pragma("unroll") for (int k = 0; k < T::kLW + ((WITH_CHUNK) ? T::kLCW : 0); k++)   \
+      G_COPY(LSLOT, LCHUNK, yo_, yos_, WITH_CHUNK, k);                                  \
   } while (0)
 
   f32x16 acc[4][NJ];
@@ -398,10 +407,19 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
   } while (0)
 
   // MFMAs of one half-stage, part [P0, P1) of it: MFMA rows i (MXFP4) or
-  // K sub-steps kt (NVFP4), each 0..3.
-#define G_MFMAS(CA, CB, SA, SB, KB, P0, P1)                                             \
+  // K sub-steps kt (NVFP4), each 0..3. With CP (compile-time) the whole
+  // half-stage runs with the copies of stage Y (into slot LSLOT, and scale
+  // chunk LCHUNK when WC) spread over it, after the MFMAs they follow: a
+  // copy holds the wave's issue while the texture unit takes its addresses,
+  // and the MFMA in flight covers that time.
+#define G_MFMAS_X(CA, CB, SA, SB, KB, P0, P1, CP, LSLOT, LCHUNK, Y, WC)                 \
   do {                                                                                  \
+    constexpr int nc_ = T::kLW + ((WC) ? T::kLCW : 0);                                  \
+    const uint32_t yo_ = (CP) ? G_YO(Y) : 0u, yos_ = (CP) ? G_YOS(Y) : 0u;              \
+    (void)yo_;                                                                          \
+    (void)yos_;                                                                         \
     if constexpr (!NV) {                                                                \
+      constexpr int nm_ = 4 * NJ;                                                       \
       uint32_t sa_[4], sb_[NJ];                                                         \
       _Pragma("unroll") for (int i = (P0); i < (P1); i++) sa_[i] = (SA[i][0] >> (16 * (KB) + 8 * h)) & 0xffu; \
       _Pragma("unroll") for (int j = 0; j < NJ; j++) sb_[j] = (SB[j][0] >> (16 * (KB) + 8 * h)) & 0xffu; \
@@ -411,9 +429,15 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
           const i32x8 fb = fp4_operand(CB[j]);                                          \
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb, fa, acc[i][j], 4, 4, 0, (int)sb_[j], \
                                                                       0, (int)sa_[i]);  \
+          if constexpr (CP) {                                                           \
+            _Pragma("unroll") for (int c = 0; c < nc_; c++)                             \
+              if ((c * nm_) / nc_ == i * NJ + j) G_COPY(LSLOT, LCHUNK, yo_, yos_, (WC), c); \
+            __builtin_amdgcn_sched_barrier(0);                                          \
+          }                                                                             \
         }                                                                               \
       }                                                                                 \
     } else {                                                                            \
+      constexpr int nm_ = 16 * NJ;                                                      \
       uint32_t pa_[4], pb_[NJ];                                                         \
       _Pragma("unroll") for (int i = 0; i < 4; i++) pa_[i] = SA[i][(KB) & (NV ? 1 : 0)] >> (16 * h); \
       _Pragma("unroll") for (int j = 0; j < NJ; j++) pb_[j] = SB[j][(KB) & (NV ? 1 : 0)] >> (16 * h); \
@@ -435,63 +459,81 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
           hb[j] = nv_dequant8(wb, nb[j]);                                               \
         }                                                                               \
         _Pragma("unroll") for (int i = 0; i < 4; i++)                                   \
-        _Pragma("unroll") for (int j = 0; j < NJ; j++)                                  \
+        _Pragma("unroll") for (int j = 0; j < NJ; j++) {                                \
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(hb[j], ha[i], acc[i][j], 0, 0, 0); \
+          if constexpr (CP) {                                                           \
+            _Pragma("unroll") for (int c = 0; c < nc_; c++)                             \
+              if ((c * nm_) / nc_ == (kt * 4 + i) * NJ + j) G_COPY(LSLOT, LCHUNK, yo_, yos_, (WC), c); \
+            __builtin_amdgcn_sched_barrier(0);                                          \
+          }                                                                             \
+        }                                                                               \
       }                                                                                 \
     }                                                                                   \
   } while (0)
+#define G_MFMAS(CA, CB, SA, SB, KB, P0, P1) G_MFMAS_X(CA, CB, SA, SB, KB, P0, P1, false, 0u, 0u, 0, false)
 
   // Stage x = x0 + U (U compile-time, x0 a multiple of 8) sits in slot U % 4,
   // its scales in chunk (U / CS) % 2 and scale buffer U % 2, and its first
   // half-stage's fragments are in ca0 / cb0. Half-stage 0: read half-stage
   // 1's fragments (and, half-way through, stage x+1's scales when its chunk
-  // is already there), run half-stage 0. Half-stage 1: wait for stage x+1,
-  // barrier, start the copy of stage x+4 into this slot (every wave is done
-  // with it), read stage x+1's first fragments (and its scales if its chunk
-  // came with it), run half-stage 1. The LDS reads are issued on every path,
-  // also past the last stage (they then read data that is never used), so
-  // that the compiler can count them exactly and waits only for the reads a
-  // half-stage consumes. A chunk slot is refilled at stage 4 c - 4 (c the chunk's
-  // index, in chunk-sized steps of CS stages): by then the last stage of the
-  // chunk two back has had its scales read, in half-stage 0 of the stage
-  // before it.
-#define G_STAGE(U, SLOT, NSLOT, CHUNK, NCHUNK, LSLOT, LRCHUNK, SA, SB, NSA, NSB)       \
+  // is already there), run half-stage 0. Half-stage 1: wait for stage x+1
+  // (each wave for its own copies: those of stages x+2 and x+3 may still be
+  // in flight), barrier (every wave is then done with this slot and sees
+  // stage x+1 whole), read stage x+1's first fragments (and its scales if its
+  // chunk came with it), run half-stage 1 with the copies of stage x+4 into
+  // this slot spread over it. The LDS reads are issued on every path, also
+  // past the last stage (they then read data that is never used), so that
+  // the compiler can count them exactly and waits only for the reads a
+  // half-stage consumes. A chunk slot is refilled at stage 4 c - 4 (c the
+  // chunk's index, in chunk-sized steps of CS stages): by then the last stage
+  // of the chunk two back has had its scales read, in half-stage 0 of the
+  // stage before it.
+#define G_STAGE(U)                                                                      \
   do {                                                                                  \
+    uint8_t* const slot_ = lds + ((U) % 4) * T::kSlot;                                  \
+    uint8_t* const nslot_ = lds + (((U) + 1) % 4) * T::kSlot;                           \
+    uint8_t* const nchunk_ = lds + T::kChunk0 + ((((U) + 1) / CS) % 2) * T::kChunk;     \
+    const uint32_t lslot_ = L + ((U) % 4) * T::kSlot;                                   \
+    const uint32_t lrchunk_ = L + T::kChunk0 + ((((U) + 4) / CS) % 2) * T::kChunk;      \
+    auto& sa_c = ((U) % 2) ? sa1 : sa0;                                                 \
+    auto& sb_c = ((U) % 2) ? sb1 : sb0;                                                 \
+    auto& sa_n = ((U) % 2) ? sa0 : sa1;                                                 \
+    auto& sb_n = ((U) % 2) ? sb0 : sb1;                                                 \
     const int x_ = x0 + (U);                                                            \
     const bool kb1_ = 2 * x_ + 1 < S64;                                                 \
     const bool next_ = x_ + 1 < S;                                                      \
-    G_READ(SLOT, 1, ca1, cb1);                                                          \
-    G_MFMAS(ca0, cb0, SA, SB, 0, 0, 2);                                                 \
+    G_READ(slot_, 1, ca1, cb1);                                                         \
+    __builtin_amdgcn_sched_barrier(0);                                                  \
+    G_MFMAS(ca0, cb0, sa_c, sb_c, 0, 0, 2);                                             \
     if (((U) + 1) % CS != 0) {                                                          \
       __builtin_amdgcn_sched_barrier(0);                                                \
-      G_READ_SCALES(NCHUNK, (U) + 1, NSA, NSB);                                         \
+      G_READ_SCALES(nchunk_, (U) + 1, sa_n, sb_n);                                      \
       __builtin_amdgcn_sched_barrier(0);                                                \
     }                                                                                   \
-    G_MFMAS(ca0, cb0, SA, SB, 0, 2, 4);                                                 \
+    G_MFMAS(ca0, cb0, sa_c, sb_c, 0, 2, 4);                                             \
+    __builtin_amdgcn_sched_barrier(0);                                                  \
     if (next_) {                                                                        \
       wait_lgkm0();                                                                     \
-      if (wl < 2)                                                                       \
-        wait_vmcnt<2 * T::kL + (((U) + 2) % CS == 0 ? T::kLC : 0) + (((U) + 3) % CS == 0 ? T::kLC : 0)>(); \
+      wait_vmcnt<2 * T::kLW + (((U) + 2) % CS == 0 ? T::kLCW : 0) + (((U) + 3) % CS == 0 ? T::kLCW : 0)>(); \
       lds_barrier();                                                                    \
-      G_ISSUE(LSLOT, LRCHUNK, x_ + 4, ((U) + 4) % CS == 0);                             \
     }                                                                                   \
-    G_READ(NSLOT, 0, ca0, cb0);                                                         \
-    if (((U) + 1) % CS == 0) G_READ_SCALES(NCHUNK, (U) + 1, NSA, NSB);                  \
-    if (kb1_) G_MFMAS(ca1, cb1, SA, SB, 1, 0, 4);                                       \
+    G_READ(nslot_, 0, ca0, cb0);                                                        \
+    if (((U) + 1) % CS == 0) G_READ_SCALES(nchunk_, (U) + 1, sa_n, sb_n);               \
+    __builtin_amdgcn_sched_barrier(0);                                                  \
+    if (kb1_) G_MFMAS_X(ca1, cb1, sa_c, sb_c, 1, 0, 4, true, lslot_, lrchunk_, x_ + 4, ((U) + 4) % CS == 0); \
   } while (0)
 
-// chunk holding stage x0 + U's scales (and its LDS address)
-#define G_CH(U) ((((U) / CS) % 2) ? chunk1 : chunk0)
-#define G_LCH(U) ((((U) / CS) % 2) ? LC1 : LC0)
-
-  // A tile starts with stages 0-2 in flight; stage 3 is issued once stage 0
-  // has landed, which keeps a loader wave within the 63 copies its vmcnt
-  // counter can track.
-  constexpr int kAfter0 = 2 * T::kL + (1 % CS == 0 ? T::kLC : 0) + (2 % CS == 0 ? T::kLC : 0);
+  // A tile starts with stages 0-3 in flight and waits for stage 0.
+  constexpr int kAfter0 = 3 * T::kLW + (1 % CS == 0 ? T::kLCW : 0) + (2 % CS == 0 ? T::kLCW : 0) +
+                          (3 % CS == 0 ? T::kLCW : 0);
+  auto issue_first_stages = [&]() {
+    G_ISSUE(L, L + T::kChunk0, 0, true);
+    G_ISSUE(L + T::kSlot, L + T::kChunk0 + ((1 / CS) % 2) * T::kChunk, 1, 1 % CS == 0);
+    G_ISSUE(L + 2 * T::kSlot, L + T::kChunk0 + ((2 / CS) % 2) * T::kChunk, 2, 2 % CS == 0);
+    G_ISSUE(L + 3 * T::kSlot, L + T::kChunk0 + ((3 / CS) % 2) * T::kChunk, 3, 3 % CS == 0);
+  };
   set_sources(grp, tm * kBM, tn * BN);
-  G_ISSUE(L0, LC0, 0, true);
-  G_ISSUE(L1, LC1, 1, 1 % CS == 0);
-  G_ISSUE(L2, LC1, 2, 2 % CS == 0);
+  issue_first_stages();
   for (int64_t jt = 0;; jt++) {
     const int64_t m0 = tm * kBM, n0 = tn * BN, cgrp = grp;
 #pragma unroll
@@ -501,26 +543,27 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
 #pragma unroll
         for (int q = 0; q < 16; q++) acc[i][j][q] = 0.0f;
     if (S > 0) {
-      if (wl < 2) wait_vmcnt<kAfter0>();
+      wait_vmcnt<kAfter0>();
       lds_barrier();
-      G_ISSUE(L3, LC1, 3, 3 % CS == 0);
-      G_READ(slot0, 0, ca0, cb0);
-      G_READ_SCALES(chunk0, 0, sa0, sb0);
+      G_READ(lds, 0, ca0, cb0);
+      G_READ_SCALES(lds + T::kChunk0, 0, sa0, sb0);
     }
     for (int x0 = 0; x0 < S; x0 += 8) {
-      G_STAGE(0, slot0, slot1, G_CH(0), G_CH(1), L0, G_LCH(4), sa0, sb0, sa1, sb1);
-      if (x0 + 1 < S) G_STAGE(1, slot1, slot2, G_CH(1), G_CH(2), L1, G_LCH(5), sa1, sb1, sa0, sb0);
-      if (x0 + 2 < S) G_STAGE(2, slot2, slot3, G_CH(2), G_CH(3), L2, G_LCH(6), sa0, sb0, sa1, sb1);
-      if (x0 + 3 < S) G_STAGE(3, slot3, slot0, G_CH(3), G_CH(4), L3, G_LCH(7), sa1, sb1, sa0, sb0);
-      if (x0 + 4 < S) G_STAGE(4, slot0, slot1, G_CH(4), G_CH(5), L0, G_LCH(8), sa0, sb0, sa1, sb1);
-      if (x0 + 5 < S) G_STAGE(5, slot1, slot2, G_CH(5), G_CH(6), L1, G_LCH(9), sa1, sb1, sa0, sb0);
-      if (x0 + 6 < S) G_STAGE(6, slot2, slot3, G_CH(6), G_CH(7), L2, G_LCH(10), sa0, sb0, sa1, sb1);
-      if (x0 + 7 < S) G_STAGE(7, slot3, slot0, G_CH(7), G_CH(8), L3, G_LCH(11), sa1, sb1, sa0, sb0);
+      G_STAGE(0);
+      if (x0 + 1 < S) G_STAGE(1);
+      if (x0 + 2 < S) G_STAGE(2);
+      if (x0 + 3 < S) G_STAGE(3);
+      if (x0 + 4 < S) G_STAGE(4);
+      if (x0 + 5 < S) G_STAGE(5);
+      if (x0 + 6 < S) G_STAGE(6);
+      if (x0 + 7 < S) G_STAGE(7);
     }
 
-    // Every wave is done with the slots: stage the tile's C there, let the
-    // store waves write it out, then start the next tile's first stages.
+    // Every wave is done with the slots once the copies past the last stage
+    // have landed: stage the tile's C there, store it, then start the next
+    // tile's first stages.
     const bool more = walk.get(jt + 1, &grp, &tm, &tn);
+    wait_vmcnt<0>();
     wait_lgkm0();
     lds_barrier();
     float alpha = 1.0f;
@@ -528,36 +571,34 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
     {
       using E = Epi<T::kWN>;
       constexpr int RR = T::kSlot / E::kRowB >= 128 ? 128 : 64;
-      auto region = [&](int k) -> uint8_t* { return k == 0 ? slot0 : k == 1 ? slot1 : k == 2 ? slot2 : slot3; };
+      const int sm = (int)(wl & 1), sh = (int)(wl >> 1);
 #pragma unroll
       for (int round = 0; round < 128 / RR; round++) {
-        stage_wave_rows<T::kWN, RR>(acc, alpha, region(w), round, lane);
+        stage_wave_rows<T::kWN, RR>(acc, alpha, lds + w * T::kSlot, round, lane);
         wait_lgkm0();
         lds_barrier();
-        if (wl >= 2) {
-          const int sw = wl - 2;
-          store_staged_rows<T::kWN, RR, OUT_BF16>(g, region(sw), region(sw + 2), cgrp,
-                                                  m0 + sw * 128 + round * RR, n0, lane);
-        }
+        // wave s: rows (s >> 1) * RR / 2 + [0, RR / 2) of the blocks of waves s & 1 and (s & 1) + 2
+        store_staged_rows<T::kWN, RR / 2, OUT_BF16>(g, lds + sm * T::kSlot, lds + (sm + 2) * T::kSlot,
+                                                     sh * (RR / 2), cgrp, m0 + sm * 128 + round * RR, n0, lane);
         wait_lgkm0();
         lds_barrier();
       }
     }
     if (!more) break;
     set_sources(grp, tm * kBM, tn * BN);
-    G_ISSUE(L0, LC0, 0, true);
-    G_ISSUE(L1, LC1, 1, 1 % CS == 0);
-    G_ISSUE(L2, LC1, 2, 2 % CS == 0);
+    issue_first_stages();
   }
   // no copy into LDS may outlive the workgroup
-  if (wl < 2) wait_vmcnt<0>();
-#undef G_CH
-#undef G_LCH
+  wait_vmcnt<0>();
 #undef G_STAGE
 #undef G_MFMAS
+#undef G_MFMAS_X
 #undef G_READ_SCALES
 #undef G_READ
 #undef G_ISSUE
+#undef G_YO
+#undef G_YOS
+#undef G_COPY
 }
 
 template <bool NV, int BN>

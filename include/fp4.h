@@ -176,8 +176,9 @@ fp4_status fp4_dequantize(int32_t format, int64_t batch, int64_t rows, int64_t c
  *   K/blk, so every scale row must be readable up to that length (true for
  *   any [rows, ld] buffer with ld a multiple of 16): give fp4_quantize a
  *   scale pitch rounded up to 16 bytes when its output feeds fp4_gemm.
- *   Each group's code and scale panels must span less than 2 GiB (else
- *   FP4_ERR_UNSUPPORTED).
+ *   Each group's code and scale panels must span less than 2 GiB, and
+ *   every row pitch (lda, ldb, lda_scales, ldb_scales) must be below 8 MiB
+ *   (else FP4_ERR_UNSUPPORTED).
  * Errors: FP4_ERR_INVALID for bad sizes, strides or NULL operands,
  * FP4_ERR_ALIGN for misaligned pointers or pitches, FP4_ERR_DEVICE off
  * gfx950, FP4_ERR_HIP if the launch fails. Nothing is written on error.

@@ -168,6 +168,10 @@ def test_gemm_errors(fp4):
     assert g(fp4, groups=2, ags=4096, bgs=4096, asgs=1032, bsgs=1024, cgs=4096) == fp4.FP4_ERR_ALIGN
     assert g(fp4, M=0, a=0, b=0, c=0) == fp4.FP4_OK
     assert g(fp4, M=-1) == fp4.FP4_ERR_INVALID
+    # panels past 2 GiB, and row pitches of 8 MiB or more, are not addressed
+    assert g(fp4, M=1 << 16, lda=1 << 15) == fp4.FP4_ERR_UNSUPPORTED
+    assert g(fp4, M=1, lda=1 << 23) == fp4.FP4_ERR_UNSUPPORTED
+    assert g(fp4, N=1, ldbs=1 << 23) == fp4.FP4_ERR_UNSUPPORTED
 
 
 @cpu_only
