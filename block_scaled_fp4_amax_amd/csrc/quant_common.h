@@ -103,9 +103,9 @@ __device__ __forceinline__ void sr16(const float q[16], uint64_t L0, uint64_t se
 // NVFP4 tensor scale for batch item b, computed identically by every
 // workgroup: T from amax_in or the max of the pre-pass partials; S_t = T / D
 // with D = 6 * 448 (4 * 448 under 4/6), replaced by 1 when zero, denormal or
-// not finite. Workgroup (0, 0) of the item stores S_t.
+// not finite. The item's first workgroup (first) stores S_t.
 template <bool FOS>
-__device__ __forceinline__ float tensor_scale_prologue(const QuantArgs& a, int64_t b) {
+__device__ __forceinline__ float tensor_scale_prologue(const QuantArgs& a, int64_t b, bool first) {
   __shared__ float red[4];
   float T;
   if (a.amax_in) {
@@ -130,7 +130,7 @@ __device__ __forceinline__ float tensor_scale_prologue(const QuantArgs& a, int64
   }
   float St = T / (FOS ? 1792.0f : 2688.0f);
   if (!(St >= kFltMin && St <= 3.40282347e38f)) St = 1.0f;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.tensor_scale[b] = St;
+  if (first && threadIdx.x == 0) a.tensor_scale[b] = St;
   return St;
 }
 

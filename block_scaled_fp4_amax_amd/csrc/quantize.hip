@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(QuantArgs a) {
 
   float St = 1.0f, k6 = 0.0f, k4 = 0.0f;
   if constexpr (NV) {
-    St = tensor_scale_prologue<FOS>(a, b);  // every lane takes part
+    St = tensor_scale_prologue<FOS>(a, b, blockIdx.x == 0 && blockIdx.y == 0);  // every lane takes part
     k6 = 1.0f / (6.0f * St);
     k4 = 1.0f / (4.0f * St);
   }
@@ -289,12 +289,22 @@ template <typename TIn, bool NV, bool FOS, bool B2D, bool SR, bool RHT>
 __global__ __launch_bounds__(256) void quant_cols_kernel(QuantArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t cst[kColsN * kColsPitch];
   __shared__ __attribute__((aligned(16))) uint8_t sst[kColsN * kColsScales];
-  const int64_t b = blockIdx.z;
+  // Workgroup order: a column strip (batch item, 128 source columns) is
+  // walked down K by consecutive workgroups of one XCD (workgroup ids go
+  // round-robin to the 8 XCDs, each with its own L2). An output row's 128-byte
+  // segments straddle cache lines whenever its pitch is not a multiple of 128;
+  // the two halves of such a line then come from neighbouring K blocks in the
+  // same L2, which merges them before they reach HBM.
+  const int64_t ncb = (a.src_cols + kColsN - 1) / kColsN, nkb = (a.src_rows + kColsK - 1) / kColsK;
+  const int64_t wid = blockIdx.x, i_x = wid >> 3;
+  const int64_t strip = (i_x / nkb) * 8 + (wid & 7);
+  if (strip >= a.batch * ncb) return;
+  const int64_t b = strip / ncb;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane & 1, g = lane >> 1;
   const int nl = (g & 15) * 8;                         // patch columns, workgroup-relative
   const int kl = wave * 64 + (g >> 4) * 32 + h * 16;   // patch rows, workgroup-relative
-  const int64_t nb = (int64_t)blockIdx.x * kColsN, kb = (int64_t)blockIdx.y * kColsK;
+  const int64_t nb = (strip - b * ncb) * kColsN, kb = (i_x % nkb) * kColsK;
   const int64_t n0 = nb + nl, k0 = kb + kl;
   // A vertical lane pair (an MXFP4 block) and a horizontal one (a 16 x 16
   // tile) are valid together: rows come in whole blocks, columns in whole
@@ -304,7 +314,7 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(QuantArgs a) {
   if (valid) t.load(reinterpret_cast<const TIn*>(a.x) + b * a.bs_x + k0 * a.ld_x + n0, a.ld_x);
   float St = 1.0f, k6 = 0.0f, k4 = 0.0f;
   if constexpr (NV) {
-    St = tensor_scale_prologue<FOS>(a, b);  // while the loads are in flight
+    St = tensor_scale_prologue<FOS>(a, b, nb == 0 && kb == 0);  // while the loads are in flight
     k6 = 1.0f / (6.0f * St);
     k4 = 1.0f / (4.0f * St);
   }
@@ -460,8 +470,10 @@ static void launch_one(const QuantArgs& a, hipStream_t s) {
     if constexpr (B2D && RHT) {
       return;  // rejected by the API
     } else {
-      dim3 grid((unsigned)((a.src_cols + kColsN - 1) / kColsN), (unsigned)((a.src_rows + kColsK - 1) / kColsK),
-                (unsigned)a.batch);
+      // 8 XCD lanes of ceil(strips / 8) column strips, each strip nkb workgroups
+      const int64_t strips = a.batch * ((a.src_cols + kColsN - 1) / kColsN);
+      const int64_t nkb = (a.src_rows + kColsK - 1) / kColsK;
+      dim3 grid((unsigned)(8 * ((strips + 7) / 8) * nkb));
       hipLaunchKernelGGL((quant_cols_kernel<TIn, NV, FOS, B2D, SR, RHT>), grid, dim3(256), 0, s, a);
     }
   } else if (B2D) {
