@@ -99,17 +99,21 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1
 // Stochastic rounding of q to E2M1 with the 16-bit random integer r: with
 // a = |q| < 6 between grid neighbours lo < hi, round up iff
 // r < (a - lo) / (hi - lo) * 2^16; a >= 6 saturates. Returns the 4-bit code.
+// The fraction is read off the fp32 encoding of a: in [1, 6) the grid has two
+// points per binade, so (a - lo) / (hi - lo) * 2^16 is the mantissa's low 22
+// bits / 2^6; in [0.5, 1) it is the mantissa / 2^7; below 0.5 it is a * 2^17,
+// exact in fp32. Each test is the exact comparison of the definition.
 __device__ __forceinline__ uint32_t e2m1_sr(float q, uint32_t r16) {
-  uint32_t sign = (__builtin_bit_cast(uint32_t, q) >> 28) & 8u;
-  float a = __builtin_fabsf(q);
-  uint32_t m = (a >= 0.5f) + (a >= 1.0f) + (a >= 1.5f) + (a >= 2.0f) + (a >= 3.0f) + (a >= 4.0f);
-  // grid value at m and the reciprocal of the gap to the next one
-  float lo = m < 4 ? 0.5f * (float)m : (m == 4 ? 2.0f : (m == 5 ? 3.0f : 4.0f));
-  float inv_gap = m < 4 ? 2.0f : (m < 6 ? 1.0f : 0.5f);
-  float f = (a - lo) * inv_gap;
-  uint32_t up = (float)r16 < f * 65536.0f;
-  m += up;
-  m = a >= 6.0f ? 7u : m;
+  const uint32_t bits = __builtin_bit_cast(uint32_t, q);
+  const uint32_t sign = (bits >> 28) & 8u;
+  const uint32_t ab = bits & 0x7fffffffu;
+  const uint32_t mant = ab & 0x7fffffu;
+  const uint32_t e = (ab >> 23) - 127u;  // binade (used where a >= 1)
+  const uint32_t c_hi = 2u + 2u * e + (mant >> 22) + ((r16 << 6) < (mant & 0x3fffffu));
+  const uint32_t c_mid = 1u + ((r16 << 7) < mant);
+  const uint32_t c_lo = (float)r16 < __builtin_fabsf(q) * 131072.0f;
+  uint32_t m = ab >= 0x3f800000u ? c_hi : (ab >= 0x3f000000u ? c_mid : c_lo);
+  m = ab >= 0x40c00000u ? 7u : m;
   return sign | m;
 }
 
