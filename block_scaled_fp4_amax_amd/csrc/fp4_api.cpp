@@ -158,7 +158,7 @@ fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t batch, int64_t r
   st = check_device();
   if (st != FP4_OK) return st;
 
-  QuantArgs a;
+  QuantArgs a{};
   a.x = x;
   a.x_bf16 = x_dtype == FP4_BF16;
   a.batch = batch;

@@ -38,10 +38,13 @@ def check(F, O, x_cpu, fmt, flags, signs=0x5A3C, seed=1234, offset=5, amax=None,
     return q
 
 
+# 544 columns: 34 NVFP4 blocks per row (ragged against every lane grouping);
+# 1024 columns: rows of whole 16 x 16 tiles and whole workgroup spans
+@pytest.mark.parametrize("shape", [(288, 544), (320, 1024)], ids=["288x544", "320x1024"])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
 @pytest.mark.parametrize("fmt,flags", valid_combos(), ids=lambda v: str(v))
-def test_every_option_combination(fp4, oracle, dtype, fmt, flags):
-    x = mixed_matrix(288, 544, seed=flags * 2 + fmt, dtype=dtype)
+def test_every_option_combination(fp4, oracle, dtype, fmt, flags, shape):
+    x = mixed_matrix(*shape, seed=flags * 2 + fmt, dtype=dtype)
     check(fp4, oracle, x, fmt, flags, what="combo")
 
 
