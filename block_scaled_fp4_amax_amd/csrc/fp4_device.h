@@ -84,11 +84,21 @@ __device__ __forceinline__ uint32_t e8m0_from_amax(float amax) {
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of the
 // two-multiplier S-box over a 128-bit counter, key bumped by the Weyl
 // constants between rounds.
+// Full 32 x 32 -> 64-bit product in one v_mad_u64_u32 (the compiler would
+// otherwise often split it into separate low and high multiplies).
+__device__ __forceinline__ uint64_t mul_wide_u32(uint32_t a, uint32_t b) {
+  uint64_t p, carry;
+  asm("v_mad_u64_u32 %0, %1, %2, %3, 0" : "=v"(p), "=s"(carry) : "v"(a), "v"(b));
+  (void)carry;
+  return p;
+}
+
 __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; r++) {
-    uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
-    uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
+    const uint64_t p0 = mul_wide_u32(0xD2511F53u, c.x), p1 = mul_wide_u32(0xCD9E8D57u, c.z);
+    uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
+    uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
     c = u32x4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
