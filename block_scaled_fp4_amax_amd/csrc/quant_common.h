@@ -29,14 +29,23 @@ struct NvCand {
   bool zero;
 };
 
-__device__ __forceinline__ NvCand nv_candidate(float amax, float k, float St) {
+// The per-workgroup NVFP4 constants: S_t, the candidate multipliers
+// 1 / (6 S_t) and 1 / (4 S_t), and rtab[code] = the reciprocal above for every
+// non-negative E4M3 code (0 for a zero block), filled once per workgroup in
+// LDS so that a block looks its reciprocal up instead of dividing.
+struct NvConsts {
+  float St, k6, k4;
+  const float* rtab;
+};
+
+__device__ __forceinline__ NvCand nv_candidate(float amax, float k, const NvConsts& nc) {
   NvCand c;
   float s = amax * k;
   s = s > kE4M3Max ? kE4M3Max : s;
   c.code = e4m3_encode(s);
-  c.eff = e4m3_decode(c.code) * St;
+  c.eff = e4m3_decode(c.code) * nc.St;
   c.zero = !(c.eff >= kFltMin);
-  c.r = c.zero ? 0.0f : 1.0f / c.eff;
+  c.r = nc.rtab[c.code & 127u];
   return c;
 }
 
@@ -132,6 +141,30 @@ __device__ __forceinline__ float tensor_scale_prologue(const QuantArgs& a, int64
   if (!(St >= kFltMin && St <= 3.40282347e38f)) St = 1.0f;
   if (first && threadIdx.x == 0) a.tensor_scale[b] = St;
   return St;
+}
+
+// S_t (tensor_scale_prologue) and the workgroup's NvConsts; every thread of
+// the (256-thread) workgroup takes part.
+template <bool FOS>
+__device__ __forceinline__ NvConsts nv_prologue(const QuantArgs& a, int64_t b, bool first) {
+  __shared__ float rtab[128];
+  __shared__ float kk[2];
+  NvConsts nc;
+  nc.St = tensor_scale_prologue<FOS>(a, b, first);
+  const int t = threadIdx.x;
+  if (t < 128) {
+    const float eff = e4m3_decode((uint32_t)t) * nc.St;
+    rtab[t] = eff >= kFltMin ? 1.0f / eff : 0.0f;
+  } else if (t == 128) {
+    kk[0] = 1.0f / (6.0f * nc.St);
+  } else if (t == 129) {
+    kk[1] = 1.0f / (4.0f * nc.St);
+  }
+  __syncthreads();
+  nc.k6 = kk[0];
+  nc.k4 = kk[1];
+  nc.rtab = rtab;
+  return nc;
 }
 
 template <typename TIn>

@@ -158,12 +158,8 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(QuantArgs a) {
   Raw16<TIn> raw;
   if (valid) raw.load(reinterpret_cast<const TIn*>(a.x) + b * a.bs_x + row * a.ld_x + cu * 16);
 
-  float St = 1.0f, k6 = 0.0f, k4 = 0.0f;
-  if constexpr (NV) {
-    St = tensor_scale_prologue<FOS>(a, b, blockIdx.x == 0 && blockIdx.y == 0);  // every lane takes part
-    k6 = 1.0f / (6.0f * St);
-    k4 = 1.0f / (4.0f * St);
-  }
+  NvConsts nc{};
+  if constexpr (NV) nc = nv_prologue<FOS>(a, b, blockIdx.x == 0 && blockIdx.y == 0);  // every lane takes part
   if (!valid) return;
 
   float v[16];
@@ -200,13 +196,13 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(QuantArgs a) {
       amax = __builtin_fmaxf(amax, xor_shfl<4>(amax));
       amax = __builtin_fmaxf(amax, xor_shfl<8>(amax));
     }
-    NvCand c = nv_candidate(amax, k6, St);
+    NvCand c = nv_candidate(amax, nc.k6, nc);
     float q[16];
 #pragma unroll
     for (int i = 0; i < 16; i++) q[i] = v[i] * c.r;
     pack16(q, w0, w1);
     if constexpr (FOS) {
-      NvCand c4 = nv_candidate(amax, k4, St);
+      NvCand c4 = nv_candidate(amax, nc.k4, nc);
       float q4[16];
 #pragma unroll
       for (int i = 0; i < 16; i++) q4[i] = v[i] * c4.r;
@@ -312,12 +308,8 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(QuantArgs a) {
   const bool valid = n0 < a.src_cols && k0 < a.src_rows;
   Patch16x8<TIn> t;
   if (valid) t.load(reinterpret_cast<const TIn*>(a.x) + b * a.bs_x + k0 * a.ld_x + n0, a.ld_x);
-  float St = 1.0f, k6 = 0.0f, k4 = 0.0f;
-  if constexpr (NV) {
-    St = tensor_scale_prologue<FOS>(a, b, nb == 0 && kb == 0);  // while the loads are in flight
-    k6 = 1.0f / (6.0f * St);
-    k4 = 1.0f / (4.0f * St);
-  }
+  NvConsts nc{};
+  if constexpr (NV) nc = nv_prologue<FOS>(a, b, nb == 0 && kb == 0);  // while the loads are in flight
   if (valid) {
     const uint64_t Lrow = (uint64_t)b * (uint64_t)a.R;
     uint8_t* crow = cst + nl * kColsPitch + (kl >> 1);
@@ -331,9 +323,9 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(QuantArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; j++) amax = __builtin_fmaxf(amax, __builtin_fabsf(t.get(i, j)));
       amax = __builtin_fmaxf(amax, xor_shfl<2>(amax));
-      NvCand c = nv_candidate(amax, k6, St);
+      NvCand c = nv_candidate(amax, nc.k6, nc);
       if constexpr (FOS) {
-        NvCand c4 = nv_candidate(amax, k4, St);
+        NvCand c4 = nv_candidate(amax, nc.k4, nc);
         // per source row: FMA chain over this lane's 8 columns, plus the
         // partner's chain over the other 8 columns; then a pairwise tree over
         // the 16 source rows
@@ -412,13 +404,13 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(QuantArgs a) {
           }
           if (h == 0) srow[j * kColsScales + (kl >> 5)] = (uint8_t)sbyte;
         } else {
-          NvCand c = nv_candidate(amax, k6, St);
+          NvCand c = nv_candidate(amax, nc.k6, nc);
           float q[16];
 #pragma unroll
           for (int i = 0; i < 16; i++) q[i] = v[i] * c.r;
           pack16(q, w0, w1);
           if constexpr (FOS) {
-            NvCand c4 = nv_candidate(amax, k4, St);
+            NvCand c4 = nv_candidate(amax, nc.k4, nc);
             float q4[16];
 #pragma unroll
             for (int i = 0; i < 16; i++) q4[i] = v[i] * c4.r;
