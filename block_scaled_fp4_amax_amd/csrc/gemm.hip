@@ -140,10 +140,13 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Persistent tile order. The grid has one workgroup per CU (a multiple of 8)
 // and consecutive workgroup ids go round-robin to the 8 XCDs, each with its
-// own L2. Tiles are ordered group-major, then by N tile, then by M tile; XCD
-// x owns the contiguous range [x * per, (x + 1) * per) and its workgroups
-// walk it interleaved, so tiles sharing an operand panel run on one XCD at
-// about the same time.
+// own L2. Within a group, tiles are numbered band by band: a band is
+// kBandN consecutive N tiles, walked M tile by M tile with its N tiles
+// innermost. XCD x owns the contiguous range [x * per, (x + 1) * per) of that
+// numbering and its workgroups walk it interleaved, so the tiles in flight
+// on one XCD form a block of a few M tiles by kBandN N tiles, whose A and B
+// panels its L2 shares.
+constexpr int64_t kBandN = 8;
 struct TileWalk {
   int64_t tiles_m, tiles_n, T, per, wpx, x, i;
   __device__ __forceinline__ TileWalk(int64_t tm, int64_t tn, int64_t groups) {
@@ -160,9 +163,15 @@ struct TileWalk {
     if (k >= per) return false;
     const int64_t tile = x * per + k;
     if (tile >= T) return false;
-    *tm = tile % tiles_m;
-    *tn = (tile / tiles_m) % tiles_n;
-    *grp = tile / (tiles_m * tiles_n);
+    const int64_t per_grp = tiles_m * tiles_n;
+    *grp = tile / per_grp;
+    const int64_t r = tile - *grp * per_grp;
+    const int64_t band = kBandN * tiles_m;
+    const int64_t nb = r / band, rr = r - nb * band;
+    const int64_t rem = tiles_n - nb * kBandN;
+    const int64_t width = rem < kBandN ? rem : kBandN;  // the last band may be narrower
+    *tm = rr / width;
+    *tn = nb * kBandN + (rr - *tm * width);
     return true;
   }
 };
