@@ -154,9 +154,25 @@ __device__ __forceinline__ float max_abs16(const float v[16]) {
   return m;
 }
 
+// v of lane (lane ^ MASK). Masks 1 and 2 are a DPP quad permutation of the
+// source operand, 4, 8 and 16 a ds_swizzle in bit mode (xor within each half
+// of the wave), both without the per-lane address arithmetic of a general
+// cross-lane read; 32 falls back to that. Every lane of an exchanging group
+// must be active.
 template <int MASK>
 __device__ __forceinline__ float xor_shfl(float v) {
-  return __shfl_xor(v, MASK, 64);
+  const int x = __builtin_bit_cast(int, v);
+  int r;
+  if constexpr (MASK == 1) {
+    r = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);  // quad_perm [1, 0, 3, 2]
+  } else if constexpr (MASK == 2) {
+    r = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);  // quad_perm [2, 3, 0, 1]
+  } else if constexpr (MASK == 4 || MASK == 8 || MASK == 16) {
+    r = __builtin_amdgcn_ds_swizzle(x, (MASK << 10) | 0x1F);  // and 0x1F, or 0, xor MASK
+  } else {
+    r = __shfl_xor(x, MASK, 64);
+  }
+  return __builtin_bit_cast(float, r);
 }
 
 }  // namespace fp4dev

@@ -131,8 +131,12 @@ __device__ __forceinline__ float tensor_scale_prologue(const QuantArgs& a, int64
     } else {
       for (int i = threadIdx.x; i < a.nparts; i += blockDim.x) m = __builtin_fmaxf(m, p[i]);
     }
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, s, 64));
+    m = __builtin_fmaxf(m, xor_shfl<32>(m));
+    m = __builtin_fmaxf(m, xor_shfl<16>(m));
+    m = __builtin_fmaxf(m, xor_shfl<8>(m));
+    m = __builtin_fmaxf(m, xor_shfl<4>(m));
+    m = __builtin_fmaxf(m, xor_shfl<2>(m));
+    m = __builtin_fmaxf(m, xor_shfl<1>(m));
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
     T = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));

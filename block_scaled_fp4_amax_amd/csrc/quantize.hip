@@ -89,8 +89,12 @@ __global__ __launch_bounds__(256) void amax_kernel(QuantArgs a) {
       }
     }
   }
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, s, 64));
+  m = __builtin_fmaxf(m, xor_shfl<32>(m));
+  m = __builtin_fmaxf(m, xor_shfl<16>(m));
+  m = __builtin_fmaxf(m, xor_shfl<8>(m));
+  m = __builtin_fmaxf(m, xor_shfl<4>(m));
+  m = __builtin_fmaxf(m, xor_shfl<2>(m));
+  m = __builtin_fmaxf(m, xor_shfl<1>(m));
   __shared__ float red[4];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
