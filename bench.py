@@ -155,7 +155,7 @@ def wl_w4a4_linear(F, inputs):
               PEAK_HBM_GBS, qa, "GB/s"),
            Op("quantize W nvfp4 4/6 (amax pre-pass + quantize)", "amax_kernel+quant_rows_kernel", "hbm", qw.bytes(),
               PEAK_HBM_GBS, qw, "GB/s"),
-           Op("gemm nvfp4 (exact fp16 dequant + fp16 MFMA)", "gemm_fp4_kernel<true, 128, true>", "mfma", gm.flops(),
+           Op("gemm nvfp4 (exact fp16 dequant + fp16 MFMA)", "gemm_fp4_kernel<true, 128, 4, true>", "mfma", gm.flops(),
               PEAK_TFLOPS["f16"], gm, "TFLOP/s")]
     cfg = {"workload": "w4a4_linear_nvfp4_four_over_six", "M": 2048, "N": 4096, "K": 4096,
            "activations": "2048x4096 bf16 N(0,1), 1% columns x30", "weight": "4096x4096 bf16 N(0,0.02)",
@@ -171,7 +171,7 @@ def wl_moe(F, inputs):
     gm = GemmCall(F, qx, qw, torch.bfloat16)
     ops = [Op("quantize W^T mxfp4 32x[2880x5760]", "quant_cols_kernel", "hbm", qw.bytes(), PEAK_HBM_GBS, qw, "GB/s"),
            Op("quantize X mxfp4 32x[512x2880]", "quant_rows_kernel", "hbm", qx.bytes(), PEAK_HBM_GBS, qx, "GB/s"),
-           Op("grouped gemm mxfp4 (scaled FP4 MFMA)", "gemm_fp4_kernel<false, 256, true>", "mfma", gm.flops(),
+           Op("grouped gemm mxfp4 (scaled FP4 MFMA)", "gemm_fp4_kernel<false, 256, 4, true>", "mfma", gm.flops(),
               PEAK_TFLOPS["fp4"], gm, "TFLOP/s")]
     cfg = {"workload": "moe_mxfp4_grouped", "experts": 32, "M": 512, "N": 5760, "K": 2880, "output": "bf16",
            "input_sets_rotated": n}
@@ -202,7 +202,7 @@ def wl_rht(F, inputs):
     gm = GemmCall(F, qx, qw, torch.bfloat16)
     ops = [Op("quantize X nvfp4 4/6 RHT", "quant_rows_kernel", "hbm", qx.bytes(), PEAK_HBM_GBS, qx, "GB/s"),
            Op("quantize W^T nvfp4 4/6 RHT", "quant_cols_kernel", "hbm", qw.bytes(), PEAK_HBM_GBS, qw, "GB/s"),
-           Op("gemm nvfp4 (exact fp16 dequant + fp16 MFMA)", "gemm_fp4_kernel<true, 128, true>", "mfma", gm.flops(),
+           Op("gemm nvfp4 (exact fp16 dequant + fp16 MFMA)", "gemm_fp4_kernel<true, 128, 4, true>", "mfma", gm.flops(),
               PEAK_TFLOPS["f16"], gm, "TFLOP/s")]
     cfg = {"workload": "rht_activation_nvfp4", "M": 16384, "N": 12288, "K": 4096, "input_sets_rotated": n}
     return ops, cfg, "fp4 e2m1 codes (nvfp4); f16 MFMA, f32 accumulate", None
@@ -274,7 +274,7 @@ def source_digest(label=None):
 
 
 def kernel_label(rocprof_name):
-    """'void fp4impl::gemm_fp4_kernel<true, 128, true>(fp4impl::GemmArgs)' -> 'gemm_fp4_kernel<true, 128, true>'"""
+    """'void fp4impl::gemm_fp4_kernel<true, 128, 4, true>(fp4impl::GemmArgs)' -> 'gemm_fp4_kernel<true, 128, 4, true>'"""
     n = rocprof_name.split("(")[0]
     n = n[len("void "):] if n.startswith("void ") else n
     return n.split("::")[-1] if "<" not in n else n[n.rfind("::", 0, n.index("<")) + 2:]

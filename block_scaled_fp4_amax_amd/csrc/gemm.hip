@@ -64,7 +64,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 // the end of K: its copies land zeros in a slot that is never read)
 constexpr uint32_t kPastEnd = 0x80000000u;
 
-template <bool NV, int BN>
+template <bool NV, int BN, int WAVES>
 struct Tile {
   static constexpr int kABytes = kBM * kRowBytes;
   static constexpr int kBBytes = BN * kRowBytes;
@@ -75,13 +75,16 @@ struct Tile {
   static constexpr int kChunk = kSABytes + kSBBytes;
   static constexpr int kChunk0 = 4 * kSlot;  // LDS offset of scale chunk 0; chunk 1 follows
   static constexpr int kLds = 4 * kSlot + 2 * kChunk;
-  static constexpr int kWN = BN / 2;         // wave tile width
-  static constexpr int kNJ = kWN / 32;       // MFMA tiles across a wave
+  // WAVES waves: 2 along M (128 rows each), WAVES / 2 along N
+  static constexpr int kWN = BN / (WAVES / 2);  // wave tile width
+  static constexpr int kNJ = kWN / 32;          // MFMA tiles across a wave
   // A copy moves 1 KB (64 lanes x 16 bytes). Wave w takes the 1 KB blocks
-  // w, w + 4, w + 8, ... of a stage slot and of a scale chunk.
-  static constexpr int kLW = kSlot / 1024 / 4;     // per wave per stage
-  static constexpr int kLWA = kABytes / 1024 / 4;  // of which A rows
-  static constexpr int kLCW = kChunk / 1024 / 4;   // per wave per scale chunk
+  // w, w + WAVES, w + 2 WAVES, ... of a stage slot and of a scale chunk.
+  static constexpr int kLW = kSlot / 1024 / WAVES;     // per wave per stage
+  static constexpr int kLWA = kABytes / 1024 / WAVES;  // of which A rows
+  static constexpr int kLCW = kChunk / 1024 / WAVES;   // per wave per scale chunk
+  // output staging: WAVES / 4 waves share a slot
+  static constexpr int kWPS = WAVES / 4;
 };
 
 // Raw buffer resource over [base, base + bytes): loads past its end return
@@ -244,24 +247,24 @@ __device__ __forceinline__ void stage_wave_rows(const f32x16 (&acc)[4][WN / 32],
   }
 }
 
-// Wave s writes rows row0 + [0, NR) of a round's staged blocks: each row
-// joins the staged blocks of the waves with wm = s & 1 (columns [0, WN) from
-// reg_lo, [WN, 2 WN) from reg_hi) and goes to output row m_base + row; a lane
-// converts 8 consecutive values and writes them in one piece, consecutive
-// lanes along the row.
-template <int WN, int NR, bool OUT_BF16>
-__device__ __forceinline__ void store_staged_rows(const GemmArgs& g, const uint8_t* reg_lo, const uint8_t* reg_hi,
-                                                  int row0, int64_t grp, int64_t m_base, int64_t n0, int lane) {
+// A wave writes rows row0 + [0, NR) of a round's staged blocks: each row
+// joins the NWN staged blocks of the waves with one wm (block wn at
+// reg0 + wn * reg_stride, columns [wn WN, (wn + 1) WN)) and goes to output row
+// m_base + row; a lane converts 8 consecutive values and writes them in one
+// piece, consecutive lanes along the row.
+template <int WN, int NWN, int NR, bool OUT_BF16>
+__device__ __forceinline__ void store_staged_rows(const GemmArgs& g, const uint8_t* reg0, int reg_stride, int row0,
+                                                  int64_t grp, int64_t m_base, int64_t n0, int lane) {
   using E = Epi<WN>;
   constexpr int kGPR = WN / 8;  // 8-value groups per row per block
   constexpr int kES = OUT_BF16 ? 2 : 4;
   const bool vec = g.c_vec_ok;
 #pragma unroll 2
-  for (int c0 = 0; c0 < NR * 2 * kGPR; c0 += 64) {
+  for (int c0 = 0; c0 < NR * NWN * kGPR; c0 += 64) {
     const int c = c0 + lane;
-    const int row = row0 + c / (2 * kGPR), k = c % (2 * kGPR);
+    const int row = row0 + c / (NWN * kGPR), k = c % (NWN * kGPR);
     const int wn = k / kGPR, p = k % kGPR;
-    const uint8_t* rp = (wn ? reg_hi : reg_lo) + row * E::kRowB;
+    const uint8_t* rp = reg0 + wn * reg_stride + row * E::kRowB;
     const float4 v0 = *reinterpret_cast<const float4*>(rp + (((2 * p) ^ (row & E::kSwz)) * 16));
     const float4 v1 = *reinterpret_cast<const float4*>(rp + (((2 * p + 1) ^ (row & E::kSwz)) * 16));
     const int64_t m = m_base + row;
@@ -291,9 +294,9 @@ __device__ __forceinline__ void store_staged_rows(const GemmArgs& g, const uint8
   }
 }
 
-template <bool NV, int BN, bool OUT_BF16>
-__global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
-  using T = Tile<NV, BN>;
+template <bool NV, int BN, int WAVES, bool OUT_BF16>
+__global__ __launch_bounds__(WAVES * 64, 1) void gemm_fp4_kernel(GemmArgs g) {
+  using T = Tile<NV, BN, WAVES>;
   constexpr int NJ = T::kNJ;
   constexpr int CS = T::kCS;
   __shared__ __attribute__((aligned(16))) uint8_t lds[T::kLds];
@@ -323,12 +326,19 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
   uint32_t voff[T::kLW];
 #pragma unroll
   for (int j = 0; j < T::kLW; j++) {
-    const int q = w + 4 * j;
+    const int q = w + WAVES * j;
     voff[j] = j < T::kLWA ? (uint32_t)(16 * q + (lane >> 2)) * lda + piece
                           : (uint32_t)(16 * (q - 16) + (lane >> 2)) * ldb + piece;
   }
-  const uint32_t voffs_a = (uint32_t)(64 * w + lane) * (uint32_t)g.lda_s;
-  const uint32_t voffs_b = (uint32_t)((64 * w + lane) & (BN - 1)) * (uint32_t)g.ldb_s;
+  // scale-chunk block q = w + WAVES j (j < kLCW): A rows 64 q + lane for
+  // q < 4, else B rows (64 (q - 4) + lane) mod BN
+  uint32_t voffs[T::kLCW];
+#pragma unroll
+  for (int j = 0; j < T::kLCW; j++) {
+    const int q = w + WAVES * j;
+    voffs[j] = q < 4 ? (uint32_t)(64 * q + lane) * (uint32_t)g.lda_s
+                     : (uint32_t)((64 * (q - 4) + lane) & (BN - 1)) * (uint32_t)g.ldb_s;
+  }
   i32x4 ra, rb, rsa, rsb;
   auto set_sources = [&](int64_t grp_, int64_t m0_, int64_t n0_) {
     const int64_t rows_a = g.M - m0_ < kBM ? g.M - m0_ : kBM;
@@ -348,10 +358,9 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
     const int k_ = (K);                                                                 \
     const int q_ = k_ - ((WITH_CHUNK) ? T::kLCW : 0);                                   \
     if (q_ < 0) {                                                                       \
-      if (k_ == 0) b2l16(rsa, voffs_a + (YOS), (LCHUNK) + wl * 1024);                   \
-      else b2l16(rsb, voffs_b + (YOS), (LCHUNK) + T::kSABytes + wl * 1024);             \
+      b2l16(wl + WAVES * k_ < 4 ? rsa : rsb, voffs[k_] + (YOS), (LCHUNK) + (wl + WAVES * k_) * 1024); \
     } else {                                                                            \
-      b2l16(q_ < T::kLWA ? ra : rb, voff[q_] + (YO), (LSLOT) + (wl + 4 * q_) * 1024);  \
+      b2l16(q_ < T::kLWA ? ra : rb, voff[q_] + (YO), (LSLOT) + (wl + WAVES * q_) * 1024); \
     }                                                                                   \
   } while (0)
   // K offsets of stage Y; a stage at or past S reads nothing (every lane out
@@ -490,7 +499,9 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
   // in flight), barrier (every wave is then done with this slot and sees
   // stage x+1 whole), read stage x+1's first fragments (and its scales if its
   // chunk came with it), run half-stage 1 with the copies of stage x+4 into
-  // this slot spread over it. The LDS reads are issued on every path, also
+  // this slot spread over it. The last stage keeps the barrier: its copies
+  // (past K, landing zeros) must not overtake another wave's last reads of
+  // this slot or of the scale chunk they refill. The LDS reads are issued on every path, also
   // past the last stage (they then read data that is never used), so that
   // the compiler can count them exactly and waits only for the reads a
   // half-stage consumes. A chunk slot is refilled at stage 4 c - 4 (c the
@@ -521,11 +532,10 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
     }                                                                                   \
     G_MFMAS(ca0, cb0, sa_c, sb_c, 0, 2, 4);                                             \
     __builtin_amdgcn_sched_barrier(0);                                                  \
-    if (next_) {                                                                        \
-      wait_lgkm0();                                                                     \
+    wait_lgkm0();                                                                       \
+    if (next_)                                                                          \
       wait_vmcnt<2 * T::kLW + (((U) + 2) % CS == 0 ? T::kLCW : 0) + (((U) + 3) % CS == 0 ? T::kLCW : 0)>(); \
-      lds_barrier();                                                                    \
-    }                                                                                   \
+    lds_barrier();                                                                      \
     G_READ(nslot_, 0, ca0, cb0);                                                        \
     if (((U) + 1) % CS == 0) G_READ_SCALES(nchunk_, (U) + 1, sa_n, sb_n);               \
     __builtin_amdgcn_sched_barrier(0);                                                  \
@@ -578,17 +588,21 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
     float alpha = 1.0f;
     if constexpr (NV) alpha = scalar_load_f32(g.a_ts + cgrp) * scalar_load_f32(g.b_ts + cgrp);
     {
+      // wave w = wm + 2 wn stages into region(w): slot w / kWPS, part w % kWPS
       using E = Epi<T::kWN>;
-      constexpr int RR = T::kSlot / E::kRowB >= 128 ? 128 : 64;
+      constexpr int kReg = T::kSlot / T::kWPS;
+      constexpr int RR = kReg / E::kRowB >= 128 ? 128 : 64;
+      constexpr int kNR = 2 * RR / WAVES;  // rows each wave stores per round
+      auto region = [&](int v) { return lds + (v / T::kWPS) * T::kSlot + (v % T::kWPS) * kReg; };
       const int sm = (int)(wl & 1), sh = (int)(wl >> 1);
 #pragma unroll
       for (int round = 0; round < 128 / RR; round++) {
-        stage_wave_rows<T::kWN, RR>(acc, alpha, lds + w * T::kSlot, round, lane);
+        stage_wave_rows<T::kWN, RR>(acc, alpha, region(w), round, lane);
         wait_lgkm0();
         lds_barrier();
-        // wave s: rows (s >> 1) * RR / 2 + [0, RR / 2) of the blocks of waves s & 1 and (s & 1) + 2
-        store_staged_rows<T::kWN, RR / 2, OUT_BF16>(g, lds + sm * T::kSlot, lds + (sm + 2) * T::kSlot,
-                                                     sh * (RR / 2), cgrp, m0 + sm * 128 + round * RR, n0, lane);
+        // wave s: rows (s >> 1) * kNR + [0, kNR) of the blocks of the waves with wm = s & 1
+        store_staged_rows<T::kWN, WAVES / 2, kNR, OUT_BF16>(g, region(sm), (int)(region(sm + 2) - region(sm)),
+                                                              sh * kNR, cgrp, m0 + sm * 128 + round * RR, n0, lane);
         wait_lgkm0();
         lds_barrier();
       }
@@ -610,16 +624,22 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
 #undef G_COPY
 }
 
-template <bool NV, int BN>
+template <bool NV, int BN, int WAVES>
 static void launch_tiles(const GemmArgs& g, hipStream_t s) {
   const int64_t T = ((g.N + BN - 1) / BN) * ((g.M + kBM - 1) / kBM) * g.groups;
   int64_t wgs = ((T + 7) / 8) * 8;
   const int64_t cus = device_cu_count();
   if (wgs > cus) wgs = cus - cus % 8;
   dim3 grid((unsigned)wgs);
-  if (g.c_bf16) hipLaunchKernelGGL((gemm_fp4_kernel<NV, BN, true>), grid, dim3(256), 0, s, g);
-  else hipLaunchKernelGGL((gemm_fp4_kernel<NV, BN, false>), grid, dim3(256), 0, s, g);
+  if (g.c_bf16) hipLaunchKernelGGL((gemm_fp4_kernel<NV, BN, WAVES, true>), grid, dim3(WAVES * 64), 0, s, g);
+  else hipLaunchKernelGGL((gemm_fp4_kernel<NV, BN, WAVES, false>), grid, dim3(WAVES * 64), 0, s, g);
 }
+
+// Waves per workgroup. Eight (two per SIMD, 128 x BN/4 each) double the
+// LDS read rate a SIMD can draw, but measured slower end to end on every
+// workload shape (fewer MFMAs per fragment read, more dequant per MFMA for
+// NVFP4), so one wave per SIMD it is.
+constexpr int kWavesMx = 4, kWavesNv = 4;
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   // 256-wide tiles when they still give every compute unit a tile
@@ -628,10 +648,10 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   if (g.nvfp4) {
     // NVFP4 keeps the 256 x 128 tile: its fp16 dequant temporaries do not
     // fit beside 256 accumulators
-    launch_tiles<true, 128>(g, s);
+    launch_tiles<true, 128, kWavesNv>(g, s);
   } else {
-    if (wide) launch_tiles<false, 256>(g, s);
-    else launch_tiles<false, 128>(g, s);
+    if (wide) launch_tiles<false, 256, kWavesMx>(g, s);
+    else launch_tiles<false, 128, kWavesMx>(g, s);
   }
   return hipGetLastError();
 }
