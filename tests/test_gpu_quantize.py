@@ -56,6 +56,43 @@ def test_batched(fp4, oracle, fmt, flags):
     check(fp4, oracle, x, fmt, flags, what="batch3")
 
 
+@pytest.mark.parametrize("fmt,flags", [(MX, 0), (NV, FOS), (NV, FOS | RHT), (NV, FOS | TR), (NV, FOS | TR | RHT),
+                                       (NV, B2D | FOS)])
+def test_padded_input_pitch(fp4, oracle, fmt, flags):
+    """Input rows further apart than their length (ld_x > cols) and a batch
+    stride beyond the item, through the C ABI: every load, including the NVFP4
+    amax pre-pass, must follow ld_x."""
+    rows, cols, pad = 96, 320, 48
+    items = [mixed_matrix(rows, cols, seed=77 + flags), mixed_matrix(rows, cols, seed=78 + flags) * 3]
+    buf = torch.zeros((2, rows + 1, cols + pad), dtype=torch.bfloat16)
+    buf[:, rows, :] = 1e30  # past each item: must never be read
+    buf[:, :, cols:] = -1e30  # past each row: must never be read
+    for b in range(2):
+        buf[b, :rows, :cols] = items[b]
+    xd = buf.cuda()
+    tr = bool(flags & TR)
+    R, C = (cols, rows) if tr else (rows, cols)
+    blk = 16 if fmt == NV else 32
+    opts = fp4.make_opts(fmt, flags, 0x5A3C, 1234, 5, 0)
+    codes = torch.empty((2, R, C // 2), dtype=torch.uint8, device="cuda")
+    lds = fp4.scale_pitch(C // blk)
+    scales = torch.empty((2, R, lds), dtype=torch.uint8, device="cuda")
+    ts = torch.empty((2,), dtype=torch.float32, device="cuda")
+    wsb = fp4.fp4_quantize_workspace(2, rows, cols, opts)
+    ws = torch.empty((max(wsb, 1),), dtype=torch.uint8, device="cuda")
+    print(f"[quantize] padded ld_x fmt={fmt} flags={flag_str(flags)}", flush=True)
+    st = fp4.fp4_quantize(xd.data_ptr(), fp4.FP4_BF16, 2, rows, cols, cols + pad, (rows + 1) * (cols + pad), opts,
+                          codes.data_ptr(), C // 2, R * (C // 2), scales.data_ptr(), lds, R * lds,
+                          ts.data_ptr() if fmt == NV else None, ws.data_ptr(), wsb, None)
+    assert st == fp4.FP4_OK
+    torch.cuda.synchronize()
+    oc, os_, ot = oracle_quantize(oracle, torch.stack(items), fmt, flags, 0x5A3C, 1234, 5)
+    assert_codes_equal(codes.cpu().numpy(), oc, f"codes padded {flag_str(flags)}")
+    assert_codes_equal(scales.cpu().numpy()[:, :, : C // blk], os_, f"scales padded {flag_str(flags)}")
+    if fmt == NV:
+        np.testing.assert_array_equal(ts.cpu().numpy().view(np.uint32), ot.view(np.uint32))
+
+
 def test_worked_example_all_modes(fp4, oracle):
     x = inputs.worked_example().reshape(1, 4096)
     for fmt, flags in [(MX, 0), (NV, 0), (NV, FOS)]:
