@@ -208,7 +208,39 @@ def wl_rht(F, inputs):
     return ops, cfg, "fp4 e2m1 codes (nvfp4); f16 MFMA, f32 accumulate", None
 
 
-WORKLOADS = {"w4a4_linear": wl_w4a4_linear, "moe": wl_moe, "training": wl_training, "rht": wl_rht}
+def wl_training_backward(F, inputs):
+    """Backward GEMMs of a quantized linear Y = X W^T (dgrad, wgrad), each with
+    its operands' quantization: dX = Q(dY) Q(W^T)^T with the weight's 2D
+    16x16 scales (the same scales as its forward quantization), and
+    dW = Q(dY^T) Q(X^T)^T; gradients with stochastic rounding (a different
+    Philox offset for each of the two quantizations of dY)."""
+    d = inputs.training_backward(device="cuda")
+    n = n_sets(d["w"].numel() * 2 + d["grad"].numel() * 2 + d["x"].numel() * 2)
+    gs, ws, xs = copies(d["grad"], n), copies(d["w"], n), copies(d["x"], n)
+    fos, sr, tr = F.FP4_FOUR_OVER_SIX, F.FP4_STOCHASTIC, F.FP4_TRANSPOSE
+    qg = QuantCall(F, gs, F.FP4_NVFP4, fos | sr, seed=d["sr_seed"], offset=0)
+    qwt = QuantCall(F, ws, F.FP4_NVFP4, fos | F.FP4_BLOCK2D | tr)
+    gd = GemmCall(F, qg, qwt, torch.bfloat16)
+    qgt = QuantCall(F, gs, F.FP4_NVFP4, fos | sr | tr, seed=d["sr_seed"], offset=1 << 40)
+    qxt = QuantCall(F, xs, F.FP4_NVFP4, fos | tr)
+    gw = GemmCall(F, qgt, qxt, torch.bfloat16)
+    ops = [Op("quantize dY nvfp4 4/6 stochastic", "quant_rows_kernel", "hbm", qg.bytes(), PEAK_HBM_GBS, qg, "GB/s"),
+           Op("quantize W^T nvfp4 2D 4/6", "quant_cols_kernel", "hbm", qwt.bytes(), PEAK_HBM_GBS, qwt, "GB/s"),
+           Op("dgrad gemm nvfp4 dX = dY W", "gemm_fp4_kernel<true, 128, 4, true>", "mfma", gd.flops(),
+              PEAK_TFLOPS["f16"], gd, "TFLOP/s"),
+           Op("quantize dY^T nvfp4 4/6 stochastic", "quant_cols_kernel", "hbm", qgt.bytes(), PEAK_HBM_GBS, qgt,
+              "GB/s"),
+           Op("quantize X^T nvfp4 4/6", "quant_cols_kernel", "hbm", qxt.bytes(), PEAK_HBM_GBS, qxt, "GB/s"),
+           Op("wgrad gemm nvfp4 dW = dY^T X", "gemm_fp4_kernel<true, 128, 4, true>", "mfma", gw.flops(),
+              PEAK_TFLOPS["f16"], gw, "TFLOP/s")]
+    cfg = {"workload": "training_backward_nvfp4_8192", "M": 8192, "N": 8192, "K": 8192,
+           "gradient": "8192x8192 bf16 Laplace(0,1e-3)", "weight": "8192x8192 bf16 N(0,0.02)",
+           "activations": "8192x8192 bf16 N(0,1)", "output": "bf16", "input_sets_rotated": n}
+    return ops, cfg, "fp4 e2m1 codes (nvfp4); f16 MFMA, f32 accumulate", None
+
+
+WORKLOADS = {"w4a4_linear": wl_w4a4_linear, "moe": wl_moe, "training": wl_training, "rht": wl_rht,
+             "training_backward": wl_training_backward}
 
 
 # ---------------------------------------------------------------------------

@@ -65,6 +65,18 @@ def training(n: int = 8192, seed: int = 4, device="cpu") -> dict:
     return {"w": w, "grad": grad.to(torch.bfloat16), "sr_seed": seed, "sr_offset": 0}
 
 
+def training_backward(m: int = 8192, n: int = 8192, k: int = 8192, seed: int = 6, device="cpu") -> dict:
+    """Backward pass of a quantized linear Y = X W^T: weight W [n, k]
+    0.02 N(0,1), output gradient dY [m, n] Laplace(0, 1e-3) (the training
+    gradient's recipe), activations X [m, k] N(0,1); bf16."""
+    g = _gen(seed, device)
+    w = (0.02 * torch.randn(n, k, generator=g, device=device)).to(torch.bfloat16)
+    u = torch.rand(m, n, generator=g, device=device) - 0.5
+    grad = -1e-3 * torch.sign(u) * torch.log1p(-2.0 * u.abs())
+    x = torch.randn(m, k, generator=g, device=device).to(torch.bfloat16)
+    return {"w": w, "grad": grad.to(torch.bfloat16), "x": x, "sr_seed": seed}
+
+
 def rht_activation(m: int = 16384, k: int = 4096, n: int = 12288, seed: int = 5, device="cpu") -> dict:
     g = _gen(seed, device)
     x = torch.randn(m, k, generator=g, device=device)

@@ -81,3 +81,16 @@ def upload_scales(scales):
     buf = np.zeros((*a.shape[:-1], F.scale_pitch(nb)), dtype=np.uint8)
     buf[..., :nb] = a
     return torch.from_numpy(buf).cuda()[..., :nb]
+
+
+def check_close(c_gpu, ref, absab, K, out_dtype, what):
+    c = c_gpu.double().cpu().numpy()
+    bound = (2 * K + 4) * 2.0 ** -24 * absab
+    if out_dtype == torch.bfloat16:
+        bound = bound + 2.0 ** -8 * np.abs(ref)
+    err = np.abs(c - ref)
+    worst = np.argmax(err - bound)
+    assert (err <= bound + 1e-30).all(), f"{what}: element bound exceeded at {np.unravel_index(worst, err.shape)}"
+    if out_dtype == torch.float32:
+        rel = np.linalg.norm(c - ref) / max(np.linalg.norm(ref), 1e-300)
+        assert rel <= 1e-3, f"{what}: relative Frobenius error {rel}"

@@ -13,7 +13,7 @@ import torch
 
 import block_scaled_fp4_amax_amd as F
 from block_scaled_fp4_amax_amd import inputs
-from gpu_util import flag_str, oracle_input, upload_scales
+from gpu_util import check_close, flag_str, oracle_input, upload_scales
 
 pytestmark = pytest.mark.gpu
 
@@ -37,19 +37,6 @@ def oracle_operand(O, x, fmt, flags, signs=0, rows=None):
     q = F.Quantized(fmt, torch.from_numpy(np.stack(codes)).cuda(), upload_scales(np.stack(scales)),
                     torch.tensor(ts, dtype=torch.float32).cuda() if fmt == NV else None)
     return q, np.stack(deq)
-
-
-def check_close(c_gpu, ref, absab, K, out_dtype, what):
-    c = c_gpu.double().cpu().numpy()
-    bound = (2 * K + 4) * 2.0 ** -24 * absab
-    if out_dtype == torch.bfloat16:
-        bound = bound + 2.0 ** -8 * np.abs(ref)
-    err = np.abs(c - ref)
-    worst = np.argmax(err - bound)
-    assert (err <= bound + 1e-30).all(), f"{what}: element bound exceeded at {np.unravel_index(worst, err.shape)}"
-    if out_dtype == torch.float32:
-        rel = np.linalg.norm(c - ref) / max(np.linalg.norm(ref), 1e-300)
-        assert rel <= 1e-3, f"{what}: relative Frobenius error {rel}"
 
 
 def run_case(O, a, b, fmt, fa, fb, out_dtype, signs=0, what=""):
