@@ -20,6 +20,8 @@ other than the oracle itself:
                        (exact rationals), invariants (saturation, scale 448)
   2D / transpose       transpose symmetry, constant tiles reduce to 1D
   GEMM reference       dequantize + numpy float64 matmul (library routine)
+  grouped GEMM         brute-force sum over k per output element; one group
+                       equals the plain product
 
 Parity of the MXFP4 / NVFP4 / 4-over-6 MAE values on the worked example is
 unpinned by the pages (they print only the float-scale numbers).
@@ -232,3 +234,16 @@ def gemm_reference(a_deq: np.ndarray, b_deq: np.ndarray) -> np.ndarray:
     """The pages' FP32-simulated matmul fallback, evaluated in float64:
     C = deq(A) @ deq(B)^T."""
     return np.asarray(a_deq, np.float64) @ np.asarray(b_deq, np.float64).T
+
+
+def grouped_gemm_reference(a_deq: np.ndarray, b_deq: np.ndarray, offsets) -> np.ndarray:
+    """The mixture-of-experts grouped product: rows offsets[g]:offsets[g+1]
+    of deq(A) [M, K] times deq(B_g)^T, B [G, N, K]; rows outside every group
+    stay NaN (not written). offsets: nondecreasing, G + 1 entries."""
+    a = np.asarray(a_deq, np.float64)
+    b = np.asarray(b_deq, np.float64)
+    c = np.full((a.shape[0], b.shape[1]), np.nan)
+    for g in range(b.shape[0]):
+        lo, hi = int(offsets[g]), int(offsets[g + 1])
+        c[lo:hi] = gemm_reference(a[lo:hi], b[g])
+    return c

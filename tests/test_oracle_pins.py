@@ -433,3 +433,24 @@ def test_gemm_reference_is_the_library_matmul(oracle):
     b = rng.standard_normal((8, 64)).astype(np.float32)
     ref = torch.from_numpy(a).double() @ torch.from_numpy(b).double().T
     np.testing.assert_allclose(oracle.gemm_reference(a, b), ref.numpy(), rtol=1e-12)
+
+
+def test_grouped_gemm_reference_brute_force(oracle):
+    """Each row m of the grouped product is the sum over k for the one group
+    whose row range holds m; empty groups and rows outside every group are
+    handled."""
+    rng = np.random.default_rng(15)
+    offsets = [0, 3, 3, 7, 9]  # group 1 empty
+    a = rng.standard_normal((10, 6)).astype(np.float32)  # row 9 in no group
+    b = rng.standard_normal((4, 5, 6)).astype(np.float32)
+    c = oracle.grouped_gemm_reference(a, b, offsets)
+    for m in range(10):
+        g = [i for i in range(4) if offsets[i] <= m < offsets[i + 1]]
+        for n in range(5):
+            if not g:
+                assert np.isnan(c[m, n])
+                continue
+            want = sum(float(a[m, k]) * float(b[g[0], n, k]) for k in range(6))
+            assert abs(c[m, n] - want) <= 1e-12 * (1 + abs(want))
+    one = oracle.grouped_gemm_reference(a, b[:1], [0, 10])
+    np.testing.assert_allclose(one, a.astype(np.float64) @ b[0].astype(np.float64).T, rtol=1e-12)
