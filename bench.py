@@ -134,6 +134,35 @@ class GemmCall:
         return 2.0 * self.G * self.M * self.N * self.K
 
 
+class GroupedGemmCall:
+    """fp4_gemm_grouped over A [M, K] (one quantized tensor) and B [G, N, K],
+    group rows from device offsets."""
+
+    def __init__(self, F, qa, qb, offsets, out_dtype=torch.bfloat16):
+        self.F, self.lib = F, F.lib()
+        a, b = qa.quantized(), qb.quantized()
+        _, self.M, half = a.codes.shape
+        self.G, self.N = b.codes.shape[0], b.codes.shape[1]
+        self.K = half * 2
+        self.offsets = offsets.to(device=a.codes.device, dtype=torch.int32)
+        self.c = torch.empty((self.M, self.N), dtype=out_dtype, device=a.codes.device)
+        ct = F.FP4_BF16 if out_dtype == torch.bfloat16 else F.FP4_F32
+        self.args = (a.fmt, self.G, self.offsets.data_ptr(), self.M, self.N, self.K, a.codes.data_ptr(), half,
+                     a.scales.data_ptr(), a.scales.stride(1),
+                     a.tensor_scale.data_ptr() if a.tensor_scale is not None else None,
+                     b.codes.data_ptr(), half, self.N * half, b.scales.data_ptr(), b.scales.stride(1),
+                     b.scales.stride(0), b.tensor_scale.data_ptr() if b.tensor_scale is not None else None,
+                     self.c.data_ptr(), ct, self.N, torch.cuda.current_stream().cuda_stream)
+
+    def __call__(self, i):
+        st = self.lib.fp4_gemm_grouped(*self.args)
+        if st != 0:
+            raise RuntimeError(f"fp4_gemm_grouped: {self.F.fp4_status_str(st)}")
+
+    def flops(self):
+        return 2.0 * self.M * self.N * self.K
+
+
 def n_sets(bytes_per_set):
     return max(2, -(-ROTATE_BYTES // max(bytes_per_set, 1)))
 
@@ -155,8 +184,8 @@ def wl_w4a4_linear(F, inputs):
               PEAK_HBM_GBS, qa, "GB/s"),
            Op("quantize W nvfp4 4/6 (amax pre-pass + quantize)", "amax_kernel+quant_rows_kernel", "hbm", qw.bytes(),
               PEAK_HBM_GBS, qw, "GB/s"),
-           Op("gemm nvfp4 (exact fp16 dequant + fp16 MFMA)", "gemm_fp4_kernel<true, 128, 4, true>", "mfma", gm.flops(),
-              PEAK_TFLOPS["f16"], gm, "TFLOP/s")]
+           Op("gemm nvfp4 (exact fp16 dequant + fp16 MFMA)", "gemm_fp4_kernel<true, 128, 4, true, false>", "mfma",
+              gm.flops(), PEAK_TFLOPS["f16"], gm, "TFLOP/s")]
     cfg = {"workload": "w4a4_linear_nvfp4_four_over_six", "M": 2048, "N": 4096, "K": 4096,
            "activations": "2048x4096 bf16 N(0,1), 1% columns x30", "weight": "4096x4096 bf16 N(0,0.02)",
            "output": "bf16", "input_sets_rotated": n}
@@ -171,8 +200,8 @@ def wl_moe(F, inputs):
     gm = GemmCall(F, qx, qw, torch.bfloat16)
     ops = [Op("quantize W^T mxfp4 32x[2880x5760]", "quant_cols_kernel", "hbm", qw.bytes(), PEAK_HBM_GBS, qw, "GB/s"),
            Op("quantize X mxfp4 32x[512x2880]", "quant_rows_kernel", "hbm", qx.bytes(), PEAK_HBM_GBS, qx, "GB/s"),
-           Op("grouped gemm mxfp4 (scaled FP4 MFMA)", "gemm_fp4_kernel<false, 256, 4, true>", "mfma", gm.flops(),
-              PEAK_TFLOPS["fp4"], gm, "TFLOP/s")]
+           Op("grouped gemm mxfp4 (scaled FP4 MFMA)", "gemm_fp4_kernel<false, 256, 4, true, false>", "mfma",
+              gm.flops(), PEAK_TFLOPS["fp4"], gm, "TFLOP/s")]
     cfg = {"workload": "moe_mxfp4_grouped", "experts": 32, "M": 512, "N": 5760, "K": 2880, "output": "bf16",
            "input_sets_rotated": n}
     return ops, cfg, "fp4 e2m1 codes (mxfp4); fp4 MFMA, f32 accumulate", None
@@ -202,8 +231,8 @@ def wl_rht(F, inputs):
     gm = GemmCall(F, qx, qw, torch.bfloat16)
     ops = [Op("quantize X nvfp4 4/6 RHT", "quant_rows_kernel", "hbm", qx.bytes(), PEAK_HBM_GBS, qx, "GB/s"),
            Op("quantize W^T nvfp4 4/6 RHT", "quant_cols_kernel", "hbm", qw.bytes(), PEAK_HBM_GBS, qw, "GB/s"),
-           Op("gemm nvfp4 (exact fp16 dequant + fp16 MFMA)", "gemm_fp4_kernel<true, 128, 4, true>", "mfma", gm.flops(),
-              PEAK_TFLOPS["f16"], gm, "TFLOP/s")]
+           Op("gemm nvfp4 (exact fp16 dequant + fp16 MFMA)", "gemm_fp4_kernel<true, 128, 4, true, false>", "mfma",
+              gm.flops(), PEAK_TFLOPS["f16"], gm, "TFLOP/s")]
     cfg = {"workload": "rht_activation_nvfp4", "M": 16384, "N": 12288, "K": 4096, "input_sets_rotated": n}
     return ops, cfg, "fp4 e2m1 codes (nvfp4); f16 MFMA, f32 accumulate", None
 
@@ -226,12 +255,12 @@ def wl_training_backward(F, inputs):
     gw = GemmCall(F, qgt, qxt, torch.bfloat16)
     ops = [Op("quantize dY nvfp4 4/6 stochastic", "quant_rows_kernel", "hbm", qg.bytes(), PEAK_HBM_GBS, qg, "GB/s"),
            Op("quantize W^T nvfp4 2D 4/6", "quant_cols_kernel", "hbm", qwt.bytes(), PEAK_HBM_GBS, qwt, "GB/s"),
-           Op("dgrad gemm nvfp4 dX = dY W", "gemm_fp4_kernel<true, 128, 4, true>", "mfma", gd.flops(),
+           Op("dgrad gemm nvfp4 dX = dY W", "gemm_fp4_kernel<true, 128, 4, true, false>", "mfma", gd.flops(),
               PEAK_TFLOPS["f16"], gd, "TFLOP/s"),
            Op("quantize dY^T nvfp4 4/6 stochastic", "quant_cols_kernel", "hbm", qgt.bytes(), PEAK_HBM_GBS, qgt,
               "GB/s"),
            Op("quantize X^T nvfp4 4/6", "quant_cols_kernel", "hbm", qxt.bytes(), PEAK_HBM_GBS, qxt, "GB/s"),
-           Op("wgrad gemm nvfp4 dW = dY^T X", "gemm_fp4_kernel<true, 128, 4, true>", "mfma", gw.flops(),
+           Op("wgrad gemm nvfp4 dW = dY^T X", "gemm_fp4_kernel<true, 128, 4, true, false>", "mfma", gw.flops(),
               PEAK_TFLOPS["f16"], gw, "TFLOP/s")]
     cfg = {"workload": "training_backward_nvfp4_8192", "M": 8192, "N": 8192, "K": 8192,
            "gradient": "8192x8192 bf16 Laplace(0,1e-3)", "weight": "8192x8192 bf16 N(0,0.02)",
@@ -239,8 +268,29 @@ def wl_training_backward(F, inputs):
     return ops, cfg, "fp4 e2m1 codes (nvfp4); f16 MFMA, f32 accumulate", None
 
 
+def wl_moe_routed(F, inputs):
+    """MoE layer with router-decided rows per expert: 4096 tokens top-4 over
+    32 experts (16384 rows, 60 to 1709 per expert), one MXFP4 quantize of the
+    routed tokens, and the grouped GEMM reading the row offsets on the
+    device."""
+    d = inputs.moe_routed(device="cuda")
+    n = n_sets(d["w"].numel() * 2 + d["x"].numel() * 2)
+    qw = QuantCall(F, copies(d["w"], n), F.FP4_MXFP4, F.FP4_TRANSPOSE)
+    qx = QuantCall(F, copies(d["x"], n), F.FP4_MXFP4, 0)
+    gm = GroupedGemmCall(F, qx, qw, d["offsets"], torch.bfloat16)
+    ops = [Op("quantize W^T mxfp4 32x[2880x5760]", "quant_cols_kernel", "hbm", qw.bytes(), PEAK_HBM_GBS, qw, "GB/s"),
+           Op("quantize routed X mxfp4 [16384x2880]", "quant_rows_kernel", "hbm", qx.bytes(), PEAK_HBM_GBS, qx,
+              "GB/s"),
+           Op("grouped gemm mxfp4, router row counts", "gemm_fp4_kernel<false, 256, 4, true, true>", "mfma",
+              gm.flops(), PEAK_TFLOPS["fp4"], gm, "TFLOP/s")]
+    cfg = {"workload": "moe_mxfp4_routed", "experts": 32, "tokens": 4096, "top_k": 4, "rows": int(d["offsets"][-1]),
+           "rows_per_expert": [int(v) for v in d["counts"]], "N": 5760, "K": 2880, "output": "bf16",
+           "input_sets_rotated": n}
+    return ops, cfg, "fp4 e2m1 codes (mxfp4); fp4 MFMA, f32 accumulate", None
+
+
 WORKLOADS = {"w4a4_linear": wl_w4a4_linear, "moe": wl_moe, "training": wl_training, "rht": wl_rht,
-             "training_backward": wl_training_backward}
+             "training_backward": wl_training_backward, "moe_routed": wl_moe_routed}
 
 
 # ---------------------------------------------------------------------------
@@ -306,7 +356,8 @@ def source_digest(label=None):
 
 
 def kernel_label(rocprof_name):
-    """'void fp4impl::gemm_fp4_kernel<true, 128, 4, true>(fp4impl::GemmArgs)' -> 'gemm_fp4_kernel<true, 128, 4, true>'"""
+    """'void fp4impl::gemm_fp4_kernel<true, 128, 4, true, false>(fp4impl::GemmArgs)'
+    -> 'gemm_fp4_kernel<true, 128, 4, true, false>'"""
     n = rocprof_name.split("(")[0]
     n = n[len("void "):] if n.startswith("void ") else n
     return n.split("::")[-1] if "<" not in n else n[n.rfind("::", 0, n.index("<")) + 2:]

@@ -4,10 +4,10 @@ W4A4 block-scaled GEMM on AMD MI355X (gfx950).
 The compute lives in ``libfp4.so`` (hand-written HIP kernels behind the C ABI
 of ``include/fp4.h``). This module only marshals arguments:
 
-* ``fp4_quantize``, ``fp4_dequantize``, ``fp4_gemm``,
+* ``fp4_quantize``, ``fp4_dequantize``, ``fp4_gemm``, ``fp4_gemm_grouped``,
   ``fp4_quantize_workspace``, ``fp4_status_str`` -- the C entry points with
   the same names and argument order (integers for device pointers);
-* ``quantize``, ``dequantize``, ``gemm`` -- conveniences over torch device
+* ``quantize``, ``dequantize``, ``gemm``, ``gemm_grouped`` -- conveniences over torch device
   tensors that allocate outputs with torch, pass the current HIP stream and
   raise ``Fp4Error`` on a non-OK status.
 
@@ -44,7 +44,8 @@ FP4_TRANSPOSE = 4
 FP4_STOCHASTIC = 8
 FP4_HADAMARD = 16
 
-EXPORTED_SYMBOLS = ("fp4_quantize_workspace", "fp4_quantize", "fp4_dequantize", "fp4_gemm", "fp4_status_str")
+EXPORTED_SYMBOLS = ("fp4_quantize_workspace", "fp4_quantize", "fp4_dequantize", "fp4_gemm", "fp4_gemm_grouped",
+                    "fp4_status_str")
 
 
 class fp4_quant_opts(ctypes.Structure):
@@ -93,6 +94,12 @@ def lib() -> ctypes.CDLL:
             c_void_p, c_int64, c_int64, c_void_p, c_int64, c_int64, c_void_p,
             c_void_p, c_int64, c_int64, c_void_p, c_int64, c_int64, c_void_p,
             c_void_p, c_int32, c_int64, c_int64, c_void_p]
+        L.fp4_gemm_grouped.restype = c_int32
+        L.fp4_gemm_grouped.argtypes = [
+            c_int32, c_int64, c_void_p, c_int64, c_int64, c_int64,
+            c_void_p, c_int64, c_void_p, c_int64, c_void_p,
+            c_void_p, c_int64, c_int64, c_void_p, c_int64, c_int64, c_void_p,
+            c_void_p, c_int32, c_int64, c_void_p]
         L.fp4_status_str.restype = c_char_p
         L.fp4_status_str.argtypes = [c_int32]
         _lib = L
@@ -143,6 +150,14 @@ def fp4_gemm(fmt, groups, M, N, K, a_codes, lda, a_group_stride, a_scales, lda_s
     return lib().fp4_gemm(fmt, groups, M, N, K, a_codes, lda, a_group_stride, a_scales, lda_scales,
                           a_scales_group_stride, a_tensor_scale, b_codes, ldb, b_group_stride, b_scales, ldb_scales,
                           b_scales_group_stride, b_tensor_scale, c, c_dtype, ldc, c_group_stride, stream)
+
+
+def fp4_gemm_grouped(fmt, groups, group_offsets, M, N, K, a_codes, lda, a_scales, lda_scales, a_tensor_scale,
+                     b_codes, ldb, b_group_stride, b_scales, ldb_scales, b_scales_group_stride, b_tensor_scale, c,
+                     c_dtype, ldc, stream) -> int:
+    return lib().fp4_gemm_grouped(fmt, groups, group_offsets, M, N, K, a_codes, lda, a_scales, lda_scales,
+                                  a_tensor_scale, b_codes, ldb, b_group_stride, b_scales, ldb_scales,
+                                  b_scales_group_stride, b_tensor_scale, c, c_dtype, ldc, stream)
 
 
 # ---------------------------------------------------------------------------
@@ -279,3 +294,36 @@ def gemm(a: Quantized, b: Quantized, out_dtype=None, stream=None):
                   _stream(stream))
     _check(st, "fp4_gemm")
     return c if a.codes.dim() == 3 else c[0]
+
+
+def gemm_grouped(a: Quantized, b: Quantized, offsets, out_dtype=None, stream=None):
+    """Mixture-of-experts grouped GEMM: rows offsets[g]:offsets[g + 1] of
+    A [M, K] times B[g] [N, K]^T, into C [M, N]. `offsets` is a device int32
+    tensor of groups + 1 entries (e.g. a router's cumulative counts)."""
+    import torch
+    out_dtype = out_dtype or torch.float32
+    if a.fmt != b.fmt:
+        raise ValueError("operands must share a format")
+    if a.codes.dim() != 2:
+        raise ValueError("A must be one [M, K] matrix")
+    bc = b.codes if b.codes.dim() == 3 else b.codes.unsqueeze(0)
+    bsc = b.scales if b.scales.dim() == 3 else b.scales.unsqueeze(0)
+    G, N, half = bc.shape
+    M, halfa = a.codes.shape
+    if half != halfa:
+        raise ValueError("operand shapes do not match")
+    if offsets.dtype != torch.int32 or offsets.dim() != 1 or offsets.numel() != G + 1 or not offsets.is_cuda:
+        raise ValueError("offsets must be a device int32 vector of groups + 1 entries")
+    offsets = offsets.contiguous()
+    c = torch.empty((M, N), dtype=out_dtype, device=a.codes.device)
+    ct = {torch.bfloat16: FP4_BF16, torch.float32: FP4_F32}[out_dtype]
+    _check_scales(a.scales.unsqueeze(0))
+    _check_scales(bsc)
+    st = fp4_gemm_grouped(a.fmt, G, offsets.data_ptr(), M, N, half * 2, a.codes.data_ptr(), half,
+                          a.scales.data_ptr(), a.scales.stride(0),
+                          a.tensor_scale.data_ptr() if a.tensor_scale is not None else None,
+                          bc.data_ptr(), half, N * half, bsc.data_ptr(), bsc.stride(1), bsc.stride(0),
+                          b.tensor_scale.data_ptr() if b.tensor_scale is not None else None, c.data_ptr(), ct, N,
+                          _stream(stream))
+    _check(st, "fp4_gemm_grouped")
+    return c

@@ -17,6 +17,8 @@ namespace {
 constexpr uint32_t kKnownFlags = FP4_FOUR_OVER_SIX | FP4_BLOCK2D | FP4_TRANSPOSE | FP4_STOCHASTIC | FP4_HADAMARD;
 constexpr int64_t kMaxGridYZ = 65535;
 constexpr int64_t kMaxGridX = 2147483647;
+// fp4_gemm_grouped: every tile scans the group offsets 64 at a time
+constexpr int64_t kMaxGroupsVar = 4096;
 
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
@@ -301,6 +303,73 @@ fp4_status fp4_gemm(int32_t format, int64_t groups, int64_t M, int64_t N, int64_
     const int64_t es = c_dtype == FP4_BF16 ? 2 : 4;
     g.c_vec_ok = aligned(c, 16) && (ldc * es) % 16 == 0 && (groups == 1 || (c_group_stride * es) % 16 == 0);
   }
+  g.a_ts_gs = 1;
+  g.offs = nullptr;
+  (void)hipGetLastError();
+  return launch_gemm(g, static_cast<hipStream_t>(stream)) == hipSuccess ? FP4_OK : FP4_ERR_HIP;
+}
+
+fp4_status fp4_gemm_grouped(int32_t format, int64_t groups, const int32_t* group_offsets, int64_t M, int64_t N,
+                            int64_t K, const uint8_t* a_codes, int64_t lda, const uint8_t* a_scales,
+                            int64_t lda_scales, const float* a_tensor_scale,
+                            const uint8_t* b_codes, int64_t ldb, int64_t b_group_stride,
+                            const uint8_t* b_scales, int64_t ldb_scales, int64_t b_scales_group_stride,
+                            const float* b_tensor_scale, void* c, int32_t c_dtype, int64_t ldc, void* stream) {
+  if (format != FP4_MXFP4 && format != FP4_NVFP4) return FP4_ERR_INVALID;
+  if (c_dtype != FP4_F32 && c_dtype != FP4_BF16) return FP4_ERR_INVALID;
+  if (groups < 0 || M < 0 || N < 0 || K < 0) return FP4_ERR_INVALID;
+  if (K % 64 != 0) return FP4_ERR_INVALID;
+  if (groups > kMaxGroupsVar || (N + 127) / 128 > kMaxGridX) return FP4_ERR_UNSUPPORTED;
+  if (groups == 0 || M == 0 || N == 0) return FP4_OK;
+  const bool nv = format == FP4_NVFP4;
+  const int64_t blk = nv ? 16 : 32;
+  if (!group_offsets || !a_codes || !a_scales || !b_codes || !b_scales || !c) return FP4_ERR_INVALID;
+  if (nv && (!a_tensor_scale || !b_tensor_scale)) return FP4_ERR_INVALID;
+  if (lda < K / 2 || ldb < K / 2 || lda_scales < K / blk || ldb_scales < K / blk || ldc < N) return FP4_ERR_INVALID;
+  if (groups > 1 && (b_group_stride < 0 || b_scales_group_stride < 0)) return FP4_ERR_INVALID;
+  if (!aligned(group_offsets, 4)) return FP4_ERR_ALIGN;
+  if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || lda % 16 != 0 || ldb % 16 != 0) return FP4_ERR_ALIGN;
+  if (M * lda >= (int64_t(1) << 31) || N * ldb >= (int64_t(1) << 31) || M * lda_scales >= (int64_t(1) << 31) ||
+      N * ldb_scales >= (int64_t(1) << 31))
+    return FP4_ERR_UNSUPPORTED;
+  if (lda >= (int64_t(1) << 23) || ldb >= (int64_t(1) << 23) || lda_scales >= (int64_t(1) << 23) ||
+      ldb_scales >= (int64_t(1) << 23))
+    return FP4_ERR_UNSUPPORTED;
+  if (groups > 1 && b_group_stride % 16 != 0) return FP4_ERR_ALIGN;
+  if (!aligned(c, c_dtype == FP4_BF16 ? 2 : 4)) return FP4_ERR_ALIGN;
+  if (!aligned(a_scales, 16) || !aligned(b_scales, 16) || lda_scales % 16 != 0 || ldb_scales % 16 != 0 ||
+      (groups > 1 && b_scales_group_stride % 16 != 0))
+    return FP4_ERR_ALIGN;
+  if (nv && (!aligned(a_tensor_scale, 4) || !aligned(b_tensor_scale, 4))) return FP4_ERR_ALIGN;
+  fp4_status st = check_device();
+  if (st != FP4_OK) return st;
+  GemmArgs g;
+  g.nvfp4 = nv;
+  g.groups = groups;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.a = a_codes;
+  g.lda = lda;
+  g.a_gs = 0;
+  g.as = a_scales;
+  g.lda_s = lda_scales;
+  g.as_gs = 0;
+  g.a_ts = a_tensor_scale;
+  g.a_ts_gs = 0;
+  g.b = b_codes;
+  g.ldb = ldb;
+  g.b_gs = groups > 1 ? b_group_stride : 0;
+  g.bs = b_scales;
+  g.ldb_s = ldb_scales;
+  g.bs_gs = groups > 1 ? b_scales_group_stride : 0;
+  g.b_ts = b_tensor_scale;
+  g.c = c;
+  g.c_bf16 = c_dtype == FP4_BF16;
+  g.ldc = ldc;
+  g.c_gs = 0;
+  g.c_vec_ok = aligned(c, 16) && (ldc * (c_dtype == FP4_BF16 ? 2 : 4)) % 16 == 0;
+  g.offs = group_offsets;
   (void)hipGetLastError();
   return launch_gemm(g, static_cast<hipStream_t>(stream)) == hipSuccess ? FP4_OK : FP4_ERR_HIP;
 }

@@ -42,6 +42,8 @@
 // matrix feeds the MFMA's first operand and A the second, so lane l holds
 // C[m = l % 32][n = 8 (q / 4) + 4 (l / 32) + q % 4]. The output goes through
 // the (then idle) stage slots so that global stores write whole row segments.
+#include <type_traits>
+
 #include "fp4_device.h"
 #include "launch.h"
 
@@ -179,6 +181,103 @@ struct TileWalk {
   }
 };
 
+// Where a tile sits: its group, its first A (and C) row m0 and the end of
+// the group's rows mend (rows in [m0, min(m0 + kBM, mend)) are valid), and
+// its first column n0.
+struct TilePos {
+  int64_t grp, m0, mend, n0;
+};
+
+// Groups of equal size: group g's A, C panels start at g times their group
+// strides, so row indices are group-local.
+struct DenseWalk {
+  TileWalk w;
+  int64_t M;
+  int bn;
+  __device__ __forceinline__ DenseWalk(const GemmArgs& g, int BN)
+      : w((g.M + kBM - 1) / kBM, (g.N + BN - 1) / BN, g.groups), M(g.M), bn(BN) {}
+  __device__ __forceinline__ bool get(int64_t j, TilePos* p) const {
+    int64_t tm, tn;
+    if (!w.get(j, &p->grp, &tm, &tn)) return false;
+    p->m0 = tm * kBM;
+    p->mend = M;
+    p->n0 = tn * bn;
+    return true;
+  }
+};
+
+// Group g's rows are [offs[g], offs[g + 1]) of one A and one C; the offsets
+// live in device memory (a router writes them), so every workgroup counts
+// the M tiles itself: group g has ceil(rows_g / kBM) of them, and the M
+// tiles of all groups, concatenated in group order, take the place of one
+// group's M tiles in the banded walk. Each offset is clamped into [0, M] and
+// each group's end to at least its start, so any offsets keep every access
+// inside A and C. A wave scans the groups 64 at a time (lane l holds group
+// c + l), with a prefix sum of the tile counts.
+__device__ __forceinline__ void group_rows(const int32_t* offs, int64_t G, int64_t M, int64_t g, int64_t* s,
+                                           int64_t* e) {
+  int64_t a = 0, b = 0;
+  if (g < G) {
+    a = offs[g];
+    b = offs[g + 1];
+    a = a < 0 ? 0 : (a > M ? M : a);
+    b = b < a ? a : (b > M ? M : b);
+  }
+  *s = a;
+  *e = b;
+}
+__device__ __forceinline__ int wave_inclusive_sum(int x, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+struct VarWalk {
+  TileWalk w;
+  const int32_t* offs;
+  int64_t G, M;
+  int bn;
+  __device__ __forceinline__ static int64_t count_tiles(const GemmArgs& g) {
+    const int lane = threadIdx.x & 63;
+    int64_t total = 0;
+    for (int64_t c = 0; c < g.groups; c += 64) {
+      int64_t s, e;
+      group_rows(g.offs, g.groups, g.M, c + lane, &s, &e);
+      const int n = (int)((e - s + kBM - 1) / kBM);
+      total += __builtin_amdgcn_readlane(wave_inclusive_sum(n, lane), 63);
+    }
+    return total;
+  }
+  __device__ __forceinline__ VarWalk(const GemmArgs& g, int BN)
+      : w(count_tiles(g), (g.N + BN - 1) / BN, 1), offs(g.offs), G(g.groups), M(g.M), bn(BN) {}
+  __device__ __forceinline__ bool get(int64_t j, TilePos* p) const {
+    int64_t grp0, tmg, tn;
+    if (!w.get(j, &grp0, &tmg, &tn)) return false;
+    const int lane = threadIdx.x & 63;
+    int64_t before = 0;
+    for (int64_t c = 0; c < G; c += 64) {
+      int64_t s, e;
+      group_rows(offs, G, M, c + lane, &s, &e);
+      const int n = (int)((e - s + kBM - 1) / kBM);
+      const int incl = wave_inclusive_sum(n, lane);
+      const uint64_t hit = __ballot(before + incl > tmg);
+      if (hit) {
+        const int l = __builtin_ctzll(hit);
+        const int64_t first = before + __builtin_amdgcn_readlane(incl - n, l);
+        p->grp = c + l;
+        p->m0 = (int64_t)__builtin_amdgcn_readlane((int)s, l) + (tmg - first) * kBM;
+        p->mend = __builtin_amdgcn_readlane((int)e, l);
+        p->n0 = tn * bn;
+        return true;
+      }
+      before += __builtin_amdgcn_readlane(incl, 63);
+    }
+    return false;  // not reached: the tile count came from the same offsets
+  }
+};
+
 // An FP4 MFMA operand: the instruction reads the low four of its eight
 // registers (32 E2M1 codes); the high four are left undefined so the
 // compiler need not copy the fragment into a zero-padded tuple.
@@ -254,7 +353,7 @@ __device__ __forceinline__ void stage_wave_rows(const f32x16 (&acc)[4][WN / 32],
 // piece, consecutive lanes along the row.
 template <int WN, int NWN, int NR, bool OUT_BF16>
 __device__ __forceinline__ void store_staged_rows(const GemmArgs& g, const uint8_t* reg0, int reg_stride, int row0,
-                                                  int64_t grp, int64_t m_base, int64_t n0, int lane) {
+                                                  int64_t grp, int64_t m_base, int64_t m_end, int64_t n0, int lane) {
   using E = Epi<WN>;
   constexpr int kGPR = WN / 8;  // 8-value groups per row per block
   constexpr int kES = OUT_BF16 ? 2 : 4;
@@ -269,7 +368,7 @@ __device__ __forceinline__ void store_staged_rows(const GemmArgs& g, const uint8
     const float4 v1 = *reinterpret_cast<const float4*>(rp + (((2 * p + 1) ^ (row & E::kSwz)) * 16));
     const int64_t m = m_base + row;
     const int64_t n = n0 + wn * WN + p * 8;
-    if (m < g.M && n < g.N) {
+    if (m < m_end && n < g.N) {
       uint8_t* dst = reinterpret_cast<uint8_t*>(g.c) + (grp * g.c_gs + m * g.ldc + n) * kES;
       const float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
       if (vec && n + 8 <= g.N) {
@@ -294,16 +393,17 @@ __device__ __forceinline__ void store_staged_rows(const GemmArgs& g, const uint8
   }
 }
 
-template <bool NV, int BN, int WAVES, bool OUT_BF16>
+template <bool NV, int BN, int WAVES, bool OUT_BF16, bool VAR>
 __global__ __launch_bounds__(WAVES * 64, 1) void gemm_fp4_kernel(GemmArgs g) {
   using T = Tile<NV, BN, WAVES>;
   constexpr int NJ = T::kNJ;
   constexpr int CS = T::kCS;
   __shared__ __attribute__((aligned(16))) uint8_t lds[T::kLds];
 
-  const TileWalk walk((g.M + kBM - 1) / kBM, (g.N + BN - 1) / BN, g.groups);
-  int64_t grp, tm, tn;
-  if (!walk.get(0, &grp, &tm, &tn)) return;
+  using Walk = typename std::conditional<VAR, VarWalk, DenseWalk>::type;
+  const Walk walk(g, BN);
+  TilePos pos;
+  if (!walk.get(0, &pos)) return;
 
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int wm = w & 1, wn = w >> 1;
@@ -340,8 +440,8 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_fp4_kernel(GemmArgs g) {
                      : (uint32_t)((64 * (q - 4) + lane) & (BN - 1)) * (uint32_t)g.ldb_s;
   }
   i32x4 ra, rb, rsa, rsb;
-  auto set_sources = [&](int64_t grp_, int64_t m0_, int64_t n0_) {
-    const int64_t rows_a = g.M - m0_ < kBM ? g.M - m0_ : kBM;
+  auto set_sources = [&](int64_t grp_, int64_t m0_, int64_t mend_, int64_t n0_) {
+    const int64_t rows_a = mend_ - m0_ < kBM ? mend_ - m0_ : kBM;
     const int64_t rows_b = g.N - n0_ < BN ? g.N - n0_ : BN;
     ra = buffer_rsrc(g.a + grp_ * g.a_gs + m0_ * g.lda, (uint32_t)(rows_a * g.lda));
     rb = buffer_rsrc(g.b + grp_ * g.b_gs + n0_ * g.ldb, (uint32_t)(rows_b * g.ldb));
@@ -551,10 +651,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_fp4_kernel(GemmArgs g) {
     G_ISSUE(L + 2 * T::kSlot, L + T::kChunk0 + ((2 / CS) % 2) * T::kChunk, 2, 2 % CS == 0);
     G_ISSUE(L + 3 * T::kSlot, L + T::kChunk0 + ((3 / CS) % 2) * T::kChunk, 3, 3 % CS == 0);
   };
-  set_sources(grp, tm * kBM, tn * BN);
+  set_sources(pos.grp, pos.m0, pos.mend, pos.n0);
   issue_first_stages();
   for (int64_t jt = 0;; jt++) {
-    const int64_t m0 = tm * kBM, n0 = tn * BN, cgrp = grp;
+    const int64_t m0 = pos.m0, mend = pos.mend, n0 = pos.n0, cgrp = pos.grp;
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
@@ -581,12 +681,12 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_fp4_kernel(GemmArgs g) {
     // Every wave is done with the slots once the copies past the last stage
     // have landed: stage the tile's C there, store it, then start the next
     // tile's first stages.
-    const bool more = walk.get(jt + 1, &grp, &tm, &tn);
+    const bool more = walk.get(jt + 1, &pos);
     wait_vmcnt<0>();
     wait_lgkm0();
     lds_barrier();
     float alpha = 1.0f;
-    if constexpr (NV) alpha = scalar_load_f32(g.a_ts + cgrp) * scalar_load_f32(g.b_ts + cgrp);
+    if constexpr (NV) alpha = scalar_load_f32(g.a_ts + cgrp * g.a_ts_gs) * scalar_load_f32(g.b_ts + cgrp);
     {
       // wave w = wm + 2 wn stages into region(w): slot w / kWPS, part w % kWPS
       using E = Epi<T::kWN>;
@@ -602,13 +702,14 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_fp4_kernel(GemmArgs g) {
         lds_barrier();
         // wave s: rows (s >> 1) * kNR + [0, kNR) of the blocks of the waves with wm = s & 1
         store_staged_rows<T::kWN, WAVES / 2, kNR, OUT_BF16>(g, region(sm), (int)(region(sm + 2) - region(sm)),
-                                                              sh * kNR, cgrp, m0 + sm * 128 + round * RR, n0, lane);
+                                                              sh * kNR, cgrp, m0 + sm * 128 + round * RR, mend, n0,
+                                                              lane);
         wait_lgkm0();
         lds_barrier();
       }
     }
     if (!more) break;
-    set_sources(grp, tm * kBM, tn * BN);
+    set_sources(pos.grp, pos.m0, pos.mend, pos.n0);
     issue_first_stages();
   }
   // no copy into LDS may outlive the workgroup
@@ -624,15 +725,27 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_fp4_kernel(GemmArgs g) {
 #undef G_COPY
 }
 
-template <bool NV, int BN, int WAVES>
-static void launch_tiles(const GemmArgs& g, hipStream_t s) {
-  const int64_t T = ((g.N + BN - 1) / BN) * ((g.M + kBM - 1) / kBM) * g.groups;
+// M tiles of the launch: exact for equal groups; for groups given by row
+// offsets (known only on the device), the most M rows can split into,
+// sum ceil(rows_g / kBM) <= floor((M + groups (kBM - 1)) / kBM).
+static int64_t m_tiles(const GemmArgs& g) {
+  return g.offs ? (g.M + g.groups * (kBM - 1)) / kBM : ((g.M + kBM - 1) / kBM) * g.groups;
+}
+
+template <bool NV, int BN, int WAVES, bool VAR>
+static void launch_tiles_v(const GemmArgs& g, hipStream_t s) {
+  const int64_t T = ((g.N + BN - 1) / BN) * m_tiles(g);
   int64_t wgs = ((T + 7) / 8) * 8;
   const int64_t cus = device_cu_count();
   if (wgs > cus) wgs = cus - cus % 8;
   dim3 grid((unsigned)wgs);
-  if (g.c_bf16) hipLaunchKernelGGL((gemm_fp4_kernel<NV, BN, WAVES, true>), grid, dim3(WAVES * 64), 0, s, g);
-  else hipLaunchKernelGGL((gemm_fp4_kernel<NV, BN, WAVES, false>), grid, dim3(WAVES * 64), 0, s, g);
+  if (g.c_bf16) hipLaunchKernelGGL((gemm_fp4_kernel<NV, BN, WAVES, true, VAR>), grid, dim3(WAVES * 64), 0, s, g);
+  else hipLaunchKernelGGL((gemm_fp4_kernel<NV, BN, WAVES, false, VAR>), grid, dim3(WAVES * 64), 0, s, g);
+}
+template <bool NV, int BN, int WAVES>
+static void launch_tiles(const GemmArgs& g, hipStream_t s) {
+  if (g.offs) launch_tiles_v<NV, BN, WAVES, true>(g, s);
+  else launch_tiles_v<NV, BN, WAVES, false>(g, s);
 }
 
 // Waves per workgroup. Eight (two per SIMD, 128 x BN/4 each) double the
@@ -643,7 +756,7 @@ constexpr int kWavesMx = 4, kWavesNv = 4;
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   // 256-wide tiles when they still give every compute unit a tile
-  const int64_t t256 = ((g.N + 255) / 256) * ((g.M + kBM - 1) / kBM) * g.groups;
+  const int64_t t256 = ((g.N + 255) / 256) * (g.offs ? (g.M + kBM - 1) / kBM : m_tiles(g));
   const bool wide = t256 >= device_cu_count();
   if (g.nvfp4) {
     // NVFP4 keeps the 256 x 128 tile: its fp16 dequant temporaries do not

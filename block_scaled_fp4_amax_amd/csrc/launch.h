@@ -64,6 +64,7 @@ struct GemmArgs {
   const uint8_t* as;
   int64_t lda_s, as_gs;
   const float* a_ts;
+  int64_t a_ts_gs;  // a_ts step per group: 1, or 0 when one scale covers all of A
   const uint8_t* b;
   int64_t ldb, b_gs;
   const uint8_t* bs;
@@ -73,6 +74,10 @@ struct GemmArgs {
   bool c_bf16;
   int64_t ldc, c_gs;
   bool c_vec_ok;  // C and its row / group pitches are 16-byte aligned
+  // NULL: `groups` equal groups of M rows at the group strides. Else device
+  // int32[groups + 1]: group g is rows [offs[g], offs[g + 1]) of one A and
+  // one C of M rows (group strides of A and C zero).
+  const int32_t* offs;
 };
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream);

@@ -17,6 +17,14 @@ Workloads (LLM-shaped, synthetic; no dataset or trained weights are used):
   rht_activation  activations [16384, 4096] ~N(0, 1) with 0.5% of entries
                   replaced by Student-t (df = 2) draws; random 16-bit sign
                   mask; weight [4096, 12288] ~N(0, 0.02) as [K, N]; bf16.
+  training_backward  weight [8192, 8192] ~N(0, 0.02), output gradient
+                  [8192, 8192] ~Laplace(0, 1e-3), activations [8192, 8192]
+                  ~N(0, 1); bf16.
+  moe_routed      32 experts as moe_mxfp4, 4096 tokens routed top-4 by
+                  logits N(0, 1) plus a per-expert bias 0.5 N(0, 1) (a skewed,
+                  load-imbalanced router): per-expert row counts, their
+                  offsets, and the routed tokens [sum of counts, 2880]
+                  ~N(0, 1) grouped by expert; bf16.
 Every size is a parameter so the tests can draw smaller instances from the
 same recipe.
 """
@@ -94,3 +102,31 @@ def rht_activation(m: int = 16384, k: int = 4096, n: int = 12288, seed: int = 5,
 def bf16_bits(t: torch.Tensor):
     """numpy uint16 view of a bf16 CPU tensor (the oracle's bf16 input form)."""
     return t.contiguous().cpu().view(torch.int16).numpy().view("uint16")
+
+
+def router_counts(tokens: int, experts: int, topk: int, seed: int, skew: float = 0.5) -> torch.Tensor:
+    """Rows per expert from a top-k router over logits N(0, 1) + skew * a
+    per-expert bias N(0, 1). int64 [experts]."""
+    g = _gen(seed, "cpu")
+    bias = skew * torch.randn(experts, generator=g)
+    logits = torch.randn(tokens, experts, generator=g) + bias
+    top = logits.topk(topk, dim=1).indices
+    return torch.bincount(top.flatten(), minlength=experts)
+
+
+def offsets_of(counts) -> torch.Tensor:
+    """Group row offsets (int32, groups + 1 entries) of a list of counts."""
+    c = torch.as_tensor(counts, dtype=torch.int64)
+    return torch.cat([torch.zeros(1, dtype=torch.int64), c.cumsum(0)]).to(torch.int32)
+
+
+def moe_routed(experts: int = 32, tokens: int = 4096, topk: int = 4, k: int = 2880, n: int = 5760, seed: int = 7,
+               counts=None, device="cpu") -> dict:
+    counts = router_counts(tokens, experts, topk, seed) if counts is None else torch.as_tensor(counts)
+    offsets = offsets_of(counts)
+    g = _gen(seed + 1, device)
+    w = torch.empty(experts, k, n, dtype=torch.bfloat16, device=device)
+    for e in range(experts):
+        w[e] = (0.02 * torch.randn(k, n, generator=g, device=device)).to(torch.bfloat16)
+    x = torch.randn(int(offsets[-1]), k, generator=g, device=device).to(torch.bfloat16)
+    return {"w": w, "x": x, "counts": counts, "offsets": offsets}

@@ -192,6 +192,35 @@ fp4_status fp4_gemm(int32_t format, int64_t groups, int64_t M, int64_t N, int64_
                     const float* b_tensor_scale,
                     void* c, int32_t c_dtype, int64_t ldc, int64_t c_group_stride, void* stream);
 
+/*
+ * fp4_gemm_grouped -- the grouped GEMM of a mixture-of-experts layer, where
+ * a router decides how many rows (tokens) each group (expert) gets ("FP4",
+ * section "Inferencia e Treinamento FP4": MoE weights in MXFP4, FP4 matrix
+ * products with higher-precision accumulation):
+ *   C[m, n] = sum_k deq(A)[m, k] * deq(B_g)[n, k]
+ *             for offsets[g] <= m < offsets[g + 1], g < groups.
+ * A [M, K] holds every group's rows back to back, as one fp4_quantize call
+ * writes them (one NVFP4 tensor scale, a_tensor_scale: device float[1]);
+ * B_g [N, K] at b_group_stride (b_tensor_scale: NVFP4 device float[groups]);
+ * C [M, N], row pitch ldc in elements. Rows of C outside every group are not
+ * written. Formats, strides, alignment and the 2 GiB / 8 MiB limits are as
+ * for fp4_gemm, with A and C taken as one group of M rows.
+ *   group_offsets: DEVICE int32[groups + 1], read by the kernel (stream-
+ *   ordered), so counts that a router computed on the device need no host
+ *   round trip. Meant to be nondecreasing from 0 to M; the kernel clamps
+ *   each offset into [0, M] and each group's end to at least its start, so
+ *   no offsets make it access memory outside A, B and C (but overlapping
+ *   groups write the same rows in an unspecified order).
+ *   Work per tile grows with groups / 64; groups > 4096 ->
+ *   FP4_ERR_UNSUPPORTED. Errors as for fp4_gemm.
+ */
+fp4_status fp4_gemm_grouped(int32_t format, int64_t groups, const int32_t* group_offsets, int64_t M, int64_t N,
+                            int64_t K, const uint8_t* a_codes, int64_t lda, const uint8_t* a_scales,
+                            int64_t lda_scales, const float* a_tensor_scale,
+                            const uint8_t* b_codes, int64_t ldb, int64_t b_group_stride,
+                            const uint8_t* b_scales, int64_t ldb_scales, int64_t b_scales_group_stride,
+                            const float* b_tensor_scale, void* c, int32_t c_dtype, int64_t ldc, void* stream);
+
 /* Static string naming a status code; never NULL. */
 const char* fp4_status_str(int32_t status);
 

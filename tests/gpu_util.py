@@ -94,3 +94,22 @@ def check_close(c_gpu, ref, absab, K, out_dtype, what):
     if out_dtype == torch.float32:
         rel = np.linalg.norm(c - ref) / max(np.linalg.norm(ref), 1e-300)
         assert rel <= 1e-3, f"{what}: relative Frobenius error {rel}"
+
+
+def oracle_operand(O, x, fmt, flags, signs=0, rows=None):
+    """Oracle-quantize x ([G, r, c] CPU). Returns the uploaded Quantized and the
+    oracle's dequantized values [G, R, C] (float32), optionally only for the
+    output rows `rows`."""
+    x3 = x.unsqueeze(0) if x.dim() == 2 else x
+    codes, scales, ts, deq = [], [], [], []
+    for b in range(x3.shape[0]):
+        r = O.quantize(oracle_input(x3[b]), fmt, flags=flags, rht_signs=signs)
+        codes.append(r["codes"])
+        scales.append(r["scales"])
+        ts.append(r["tensor_scale"] or 0.0)
+        c, s = (r["codes"], r["scales"]) if rows is None else (r["codes"][rows], r["scales"][rows])
+        deq.append(O.dequantize(fmt, c, s, r["tensor_scale"]))
+    import block_scaled_fp4_amax_amd as F
+    q = F.Quantized(fmt, torch.from_numpy(np.stack(codes)).cuda(), upload_scales(np.stack(scales)),
+                    torch.tensor(ts, dtype=torch.float32).cuda() if fmt == O.NVFP4 else None)
+    return q, np.stack(deq)

@@ -13,30 +13,12 @@ import torch
 
 import block_scaled_fp4_amax_amd as F
 from block_scaled_fp4_amax_amd import inputs
-from gpu_util import check_close, flag_str, oracle_input, upload_scales
+from gpu_util import check_close, flag_str, oracle_operand
 
 pytestmark = pytest.mark.gpu
 
 MX, NV = 0, 1
 FOS, B2D, TR, SR, RHT = 1, 2, 4, 8, 16
-
-
-def oracle_operand(O, x, fmt, flags, signs=0, rows=None):
-    """Oracle-quantize x ([G, r, c] CPU). Returns the uploaded Quantized and the
-    oracle's dequantized values [G, R, C] (float32), optionally only for the
-    output rows `rows`."""
-    x3 = x.unsqueeze(0) if x.dim() == 2 else x
-    codes, scales, ts, deq = [], [], [], []
-    for b in range(x3.shape[0]):
-        r = O.quantize(oracle_input(x3[b]), fmt, flags=flags, rht_signs=signs)
-        codes.append(r["codes"])
-        scales.append(r["scales"])
-        ts.append(r["tensor_scale"] or 0.0)
-        c, s = (r["codes"], r["scales"]) if rows is None else (r["codes"][rows], r["scales"][rows])
-        deq.append(O.dequantize(fmt, c, s, r["tensor_scale"]))
-    q = F.Quantized(fmt, torch.from_numpy(np.stack(codes)).cuda(), upload_scales(np.stack(scales)),
-                    torch.tensor(ts, dtype=torch.float32).cuda() if fmt == NV else None)
-    return q, np.stack(deq)
 
 
 def run_case(O, a, b, fmt, fa, fb, out_dtype, signs=0, what=""):
