@@ -134,6 +134,42 @@ class GemmCall:
         return 2.0 * self.G * self.M * self.N * self.K
 
 
+class GemmQuantizeOutputCall:
+    """fp4_gemm_quantize_output: the product quantized in the epilogue to
+    NVFP4 4/6 with a supplied amax (taken once, untimed, from the unfused
+    product: the amax a previous step would hand over)."""
+
+    def __init__(self, F, qa, qb, amax):
+        self.F, self.lib = F, F.lib()
+        a, b = qa.quantized(), qb.quantized()
+        self.G, self.M, half = a.codes.shape
+        self.N = b.codes.shape[1]
+        self.K = half * 2
+        dev = a.codes.device
+        self.amax = amax.to(device=dev, dtype=torch.float32).reshape(-1).contiguous()
+        self.opts = F.make_opts(F.FP4_NVFP4, F.FP4_FOUR_OVER_SIX, 0, 0, 0, self.amax.data_ptr())
+        self.codes = torch.empty((self.G, self.M, self.N // 2), dtype=torch.uint8, device=dev)
+        self.lds = F.scale_pitch(self.N // 16)
+        self.scales = torch.empty((self.G, self.M, self.lds), dtype=torch.uint8, device=dev)
+        self.ts = torch.empty((self.G,), dtype=torch.float32, device=dev)
+        self.args = (a.fmt, self.G, self.M, self.N, self.K, a.codes.data_ptr(), half, self.M * half,
+                     a.scales.data_ptr(), a.scales.stride(1), a.scales.stride(0),
+                     a.tensor_scale.data_ptr() if a.tensor_scale is not None else None,
+                     b.codes.data_ptr(), half, self.N * half, b.scales.data_ptr(), b.scales.stride(1),
+                     b.scales.stride(0), b.tensor_scale.data_ptr() if b.tensor_scale is not None else None,
+                     ctypes.byref(self.opts), self.codes.data_ptr(), self.N // 2, self.M * (self.N // 2),
+                     self.scales.data_ptr(), self.lds, self.M * self.lds, self.ts.data_ptr(),
+                     torch.cuda.current_stream().cuda_stream)
+
+    def __call__(self, i):
+        st = self.lib.fp4_gemm_quantize_output(*self.args)
+        if st != 0:
+            raise RuntimeError(f"fp4_gemm_quantize_output: {self.F.fp4_status_str(st)}")
+
+    def flops(self):
+        return 2.0 * self.G * self.M * self.N * self.K
+
+
 class GroupedGemmCall:
     """fp4_gemm_grouped over A [M, K] (one quantized tensor) and B [G, N, K],
     group rows from device offsets."""
@@ -184,7 +220,7 @@ def wl_w4a4_linear(F, inputs):
               PEAK_HBM_GBS, qa, "GB/s"),
            Op("quantize W nvfp4 4/6 (amax pre-pass + quantize)", "amax_kernel+quant_rows_kernel", "hbm", qw.bytes(),
               PEAK_HBM_GBS, qw, "GB/s"),
-           Op("gemm nvfp4 (exact fp16 dequant + fp16 MFMA)", "gemm_fp4_kernel<true, 128, 4, true, false>", "mfma",
+           Op("gemm nvfp4 (exact fp16 dequant + fp16 MFMA)", "gemm_fp4_kernel<true, 128, 4, 1, false>", "mfma",
               gm.flops(), PEAK_TFLOPS["f16"], gm, "TFLOP/s")]
     cfg = {"workload": "w4a4_linear_nvfp4_four_over_six", "M": 2048, "N": 4096, "K": 4096,
            "activations": "2048x4096 bf16 N(0,1), 1% columns x30", "weight": "4096x4096 bf16 N(0,0.02)",
@@ -200,7 +236,7 @@ def wl_moe(F, inputs):
     gm = GemmCall(F, qx, qw, torch.bfloat16)
     ops = [Op("quantize W^T mxfp4 32x[2880x5760]", "quant_cols_kernel", "hbm", qw.bytes(), PEAK_HBM_GBS, qw, "GB/s"),
            Op("quantize X mxfp4 32x[512x2880]", "quant_rows_kernel", "hbm", qx.bytes(), PEAK_HBM_GBS, qx, "GB/s"),
-           Op("grouped gemm mxfp4 (scaled FP4 MFMA)", "gemm_fp4_kernel<false, 256, 4, true, false>", "mfma",
+           Op("grouped gemm mxfp4 (scaled FP4 MFMA)", "gemm_fp4_kernel<false, 256, 4, 1, false>", "mfma",
               gm.flops(), PEAK_TFLOPS["fp4"], gm, "TFLOP/s")]
     cfg = {"workload": "moe_mxfp4_grouped", "experts": 32, "M": 512, "N": 5760, "K": 2880, "output": "bf16",
            "input_sets_rotated": n}
@@ -231,7 +267,7 @@ def wl_rht(F, inputs):
     gm = GemmCall(F, qx, qw, torch.bfloat16)
     ops = [Op("quantize X nvfp4 4/6 RHT", "quant_rows_kernel", "hbm", qx.bytes(), PEAK_HBM_GBS, qx, "GB/s"),
            Op("quantize W^T nvfp4 4/6 RHT", "quant_cols_kernel", "hbm", qw.bytes(), PEAK_HBM_GBS, qw, "GB/s"),
-           Op("gemm nvfp4 (exact fp16 dequant + fp16 MFMA)", "gemm_fp4_kernel<true, 128, 4, true, false>", "mfma",
+           Op("gemm nvfp4 (exact fp16 dequant + fp16 MFMA)", "gemm_fp4_kernel<true, 128, 4, 1, false>", "mfma",
               gm.flops(), PEAK_TFLOPS["f16"], gm, "TFLOP/s")]
     cfg = {"workload": "rht_activation_nvfp4", "M": 16384, "N": 12288, "K": 4096, "input_sets_rotated": n}
     return ops, cfg, "fp4 e2m1 codes (nvfp4); f16 MFMA, f32 accumulate", None
@@ -255,16 +291,42 @@ def wl_training_backward(F, inputs):
     gw = GemmCall(F, qgt, qxt, torch.bfloat16)
     ops = [Op("quantize dY nvfp4 4/6 stochastic", "quant_rows_kernel", "hbm", qg.bytes(), PEAK_HBM_GBS, qg, "GB/s"),
            Op("quantize W^T nvfp4 2D 4/6", "quant_cols_kernel", "hbm", qwt.bytes(), PEAK_HBM_GBS, qwt, "GB/s"),
-           Op("dgrad gemm nvfp4 dX = dY W", "gemm_fp4_kernel<true, 128, 4, true, false>", "mfma", gd.flops(),
+           Op("dgrad gemm nvfp4 dX = dY W", "gemm_fp4_kernel<true, 128, 4, 1, false>", "mfma", gd.flops(),
               PEAK_TFLOPS["f16"], gd, "TFLOP/s"),
            Op("quantize dY^T nvfp4 4/6 stochastic", "quant_cols_kernel", "hbm", qgt.bytes(), PEAK_HBM_GBS, qgt,
               "GB/s"),
            Op("quantize X^T nvfp4 4/6", "quant_cols_kernel", "hbm", qxt.bytes(), PEAK_HBM_GBS, qxt, "GB/s"),
-           Op("wgrad gemm nvfp4 dW = dY^T X", "gemm_fp4_kernel<true, 128, 4, true, false>", "mfma", gw.flops(),
+           Op("wgrad gemm nvfp4 dW = dY^T X", "gemm_fp4_kernel<true, 128, 4, 1, false>", "mfma", gw.flops(),
               PEAK_TFLOPS["f16"], gw, "TFLOP/s")]
     cfg = {"workload": "training_backward_nvfp4_8192", "M": 8192, "N": 8192, "K": 8192,
            "gradient": "8192x8192 bf16 Laplace(0,1e-3)", "weight": "8192x8192 bf16 N(0,0.02)",
            "activations": "8192x8192 bf16 N(0,1)", "output": "bf16", "input_sets_rotated": n}
+    return ops, cfg, "fp4 e2m1 codes (nvfp4); f16 MFMA, f32 accumulate", None
+
+
+def wl_w4a4_fused(F, inputs):
+    """The W4A4 linear layer handing NVFP4 4/6 activations to the next one:
+    its GEMM quantizes C in the epilogue instead of storing bf16 C."""
+    d = inputs.w4a4_linear(device="cuda")
+    n = n_sets(d["a"].numel() * 2 + d["w"].numel() * 2)
+    qa = QuantCall(F, copies(d["a"], n), F.FP4_NVFP4, F.FP4_FOUR_OVER_SIX)
+    qw = QuantCall(F, copies(d["w"], n), F.FP4_NVFP4, F.FP4_FOUR_OVER_SIX)
+    qa(0)
+    qw(0)
+    probe = GemmCall(F, qa, qw, torch.float32)
+    probe(0)
+    amax = probe.c.abs().amax().reshape(1)
+    del probe
+    gq = GemmQuantizeOutputCall(F, qa, qw, amax)
+    ops = [Op("quantize A nvfp4 4/6 (amax pre-pass + quantize)", "amax_kernel+quant_rows_kernel", "hbm", qa.bytes(),
+              PEAK_HBM_GBS, qa, "GB/s"),
+           Op("quantize W nvfp4 4/6 (amax pre-pass + quantize)", "amax_kernel+quant_rows_kernel", "hbm", qw.bytes(),
+              PEAK_HBM_GBS, qw, "GB/s"),
+           Op("gemm nvfp4, output quantized to nvfp4 4/6 in the epilogue", "gemm_fp4_kernel<true, 128, 4, 3, false>",
+              "mfma", gq.flops(), PEAK_TFLOPS["f16"], gq, "TFLOP/s")]
+    cfg = {"workload": "w4a4_linear_nvfp4_fused_output_quantize", "M": 2048, "N": 4096, "K": 4096,
+           "activations": "2048x4096 bf16 N(0,1), 1% columns x30", "weight": "4096x4096 bf16 N(0,0.02)",
+           "output": "nvfp4 4/6 codes + scales, amax supplied", "input_sets_rotated": n}
     return ops, cfg, "fp4 e2m1 codes (nvfp4); f16 MFMA, f32 accumulate", None
 
 
@@ -281,7 +343,7 @@ def wl_moe_routed(F, inputs):
     ops = [Op("quantize W^T mxfp4 32x[2880x5760]", "quant_cols_kernel", "hbm", qw.bytes(), PEAK_HBM_GBS, qw, "GB/s"),
            Op("quantize routed X mxfp4 [16384x2880]", "quant_rows_kernel", "hbm", qx.bytes(), PEAK_HBM_GBS, qx,
               "GB/s"),
-           Op("grouped gemm mxfp4, router row counts", "gemm_fp4_kernel<false, 256, 4, true, true>", "mfma",
+           Op("grouped gemm mxfp4, router row counts", "gemm_fp4_kernel<false, 256, 4, 1, true>", "mfma",
               gm.flops(), PEAK_TFLOPS["fp4"], gm, "TFLOP/s")]
     cfg = {"workload": "moe_mxfp4_routed", "experts": 32, "tokens": 4096, "top_k": 4, "rows": int(d["offsets"][-1]),
            "rows_per_expert": [int(v) for v in d["counts"]], "N": 5760, "K": 2880, "output": "bf16",
@@ -290,7 +352,7 @@ def wl_moe_routed(F, inputs):
 
 
 WORKLOADS = {"w4a4_linear": wl_w4a4_linear, "moe": wl_moe, "training": wl_training, "rht": wl_rht,
-             "training_backward": wl_training_backward, "moe_routed": wl_moe_routed}
+             "training_backward": wl_training_backward, "moe_routed": wl_moe_routed, "w4a4_fused": wl_w4a4_fused}
 
 
 # ---------------------------------------------------------------------------
@@ -356,8 +418,8 @@ def source_digest(label=None):
 
 
 def kernel_label(rocprof_name):
-    """'void fp4impl::gemm_fp4_kernel<true, 128, 4, true, false>(fp4impl::GemmArgs)'
-    -> 'gemm_fp4_kernel<true, 128, 4, true, false>'"""
+    """'void fp4impl::gemm_fp4_kernel<true, 128, 4, 1, false>(fp4impl::GemmArgs)'
+    -> 'gemm_fp4_kernel<true, 128, 4, 1, false>'"""
     n = rocprof_name.split("(")[0]
     n = n[len("void "):] if n.startswith("void ") else n
     return n.split("::")[-1] if "<" not in n else n[n.rfind("::", 0, n.index("<")) + 2:]

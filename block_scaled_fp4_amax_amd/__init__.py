@@ -5,9 +5,11 @@ The compute lives in ``libfp4.so`` (hand-written HIP kernels behind the C ABI
 of ``include/fp4.h``). This module only marshals arguments:
 
 * ``fp4_quantize``, ``fp4_dequantize``, ``fp4_gemm``, ``fp4_gemm_grouped``,
-  ``fp4_quantize_workspace``, ``fp4_status_str`` -- the C entry points with
+  ``fp4_gemm_quantize_output``, ``fp4_quantize_workspace``,
+  ``fp4_status_str`` -- the C entry points with
   the same names and argument order (integers for device pointers);
-* ``quantize``, ``dequantize``, ``gemm``, ``gemm_grouped`` -- conveniences over torch device
+* ``quantize``, ``dequantize``, ``gemm``, ``gemm_grouped``,
+  ``gemm_quantize_output`` -- conveniences over torch device
   tensors that allocate outputs with torch, pass the current HIP stream and
   raise ``Fp4Error`` on a non-OK status.
 
@@ -45,7 +47,7 @@ FP4_STOCHASTIC = 8
 FP4_HADAMARD = 16
 
 EXPORTED_SYMBOLS = ("fp4_quantize_workspace", "fp4_quantize", "fp4_dequantize", "fp4_gemm", "fp4_gemm_grouped",
-                    "fp4_status_str")
+                    "fp4_gemm_quantize_output", "fp4_status_str")
 
 
 class fp4_quant_opts(ctypes.Structure):
@@ -100,6 +102,13 @@ def lib() -> ctypes.CDLL:
             c_void_p, c_int64, c_void_p, c_int64, c_void_p,
             c_void_p, c_int64, c_int64, c_void_p, c_int64, c_int64, c_void_p,
             c_void_p, c_int32, c_int64, c_void_p]
+        L.fp4_gemm_quantize_output.restype = c_int32
+        L.fp4_gemm_quantize_output.argtypes = [
+            c_int32, c_int64, c_int64, c_int64, c_int64,
+            c_void_p, c_int64, c_int64, c_void_p, c_int64, c_int64, c_void_p,
+            c_void_p, c_int64, c_int64, c_void_p, c_int64, c_int64, c_void_p,
+            ctypes.POINTER(fp4_quant_opts), c_void_p, c_int64, c_int64, c_void_p, c_int64, c_int64, c_void_p,
+            c_void_p]
         L.fp4_status_str.restype = c_char_p
         L.fp4_status_str.argtypes = [c_int32]
         _lib = L
@@ -150,6 +159,19 @@ def fp4_gemm(fmt, groups, M, N, K, a_codes, lda, a_group_stride, a_scales, lda_s
     return lib().fp4_gemm(fmt, groups, M, N, K, a_codes, lda, a_group_stride, a_scales, lda_scales,
                           a_scales_group_stride, a_tensor_scale, b_codes, ldb, b_group_stride, b_scales, ldb_scales,
                           b_scales_group_stride, b_tensor_scale, c, c_dtype, ldc, c_group_stride, stream)
+
+
+def fp4_gemm_quantize_output(fmt, groups, M, N, K, a_codes, lda, a_group_stride, a_scales, lda_scales,
+                             a_scales_group_stride, a_tensor_scale, b_codes, ldb, b_group_stride, b_scales, ldb_scales,
+                             b_scales_group_stride, b_tensor_scale, out_opts: fp4_quant_opts, out_codes, ld_out_codes,
+                             out_codes_group_stride, out_scales, ld_out_scales, out_scales_group_stride,
+                             out_tensor_scale, stream) -> int:
+    return lib().fp4_gemm_quantize_output(fmt, groups, M, N, K, a_codes, lda, a_group_stride, a_scales, lda_scales,
+                                          a_scales_group_stride, a_tensor_scale, b_codes, ldb, b_group_stride,
+                                          b_scales, ldb_scales, b_scales_group_stride, b_tensor_scale,
+                                          ctypes.byref(out_opts), out_codes, ld_out_codes, out_codes_group_stride,
+                                          out_scales, ld_out_scales, out_scales_group_stride, out_tensor_scale,
+                                          stream)
 
 
 def fp4_gemm_grouped(fmt, groups, group_offsets, M, N, K, a_codes, lda, a_scales, lda_scales, a_tensor_scale,
@@ -294,6 +316,51 @@ def gemm(a: Quantized, b: Quantized, out_dtype=None, stream=None):
                   _stream(stream))
     _check(st, "fp4_gemm")
     return c if a.codes.dim() == 3 else c[0]
+
+
+def gemm_quantize_output(a: Quantized, b: Quantized, fmt="nvfp4", *, four_over_six=False, stochastic=False,
+                         hadamard=False, rht_signs=0, seed=0, offset=0, amax=None, stream=None) -> Quantized:
+    """deq(A[g]) @ deq(B[g])^T quantized along its rows in the GEMM's epilogue
+    (format `fmt`, options as for quantize); NVFP4 needs `amax`, the tensor
+    amax per group that S_t derives from."""
+    import torch
+    if a.fmt != b.fmt:
+        raise ValueError("operands must share a format")
+    ac = a.codes if a.codes.dim() == 3 else a.codes.unsqueeze(0)
+    asc = a.scales if a.scales.dim() == 3 else a.scales.unsqueeze(0)
+    bc = b.codes if b.codes.dim() == 3 else b.codes.unsqueeze(0)
+    bsc = b.scales if b.scales.dim() == 3 else b.scales.unsqueeze(0)
+    G, M, half = ac.shape
+    Gb, N, halfb = bc.shape
+    if G != Gb or half != halfb:
+        raise ValueError("operand shapes do not match")
+    qfmt = _fmt(fmt)
+    flags = ((FP4_FOUR_OVER_SIX if four_over_six else 0) | (FP4_STOCHASTIC if stochastic else 0)
+             | (FP4_HADAMARD if hadamard else 0))
+    amax_t = None
+    if amax is not None:
+        amax_t = torch.as_tensor(amax, dtype=torch.float32, device=ac.device).reshape(-1).contiguous()
+    opts = make_opts(qfmt, flags, rht_signs, seed, offset, amax_t.data_ptr() if amax_t is not None else 0)
+    blk = 16 if qfmt == FP4_NVFP4 else 32
+    dev = ac.device
+    codes = torch.empty((G, M, N // 2), dtype=torch.uint8, device=dev)
+    lds = scale_pitch(N // blk)
+    scales_buf = torch.empty((G, M, lds), dtype=torch.uint8, device=dev)
+    ts = torch.empty((G,), dtype=torch.float32, device=dev) if qfmt == FP4_NVFP4 else None
+    _check_scales(asc)
+    _check_scales(bsc)
+    st = fp4_gemm_quantize_output(a.fmt, G, M, N, half * 2, ac.data_ptr(), half, M * half, asc.data_ptr(),
+                                  asc.stride(1), asc.stride(0),
+                                  a.tensor_scale.data_ptr() if a.tensor_scale is not None else None,
+                                  bc.data_ptr(), half, N * half, bsc.data_ptr(), bsc.stride(1), bsc.stride(0),
+                                  b.tensor_scale.data_ptr() if b.tensor_scale is not None else None, opts,
+                                  codes.data_ptr(), N // 2, M * (N // 2), scales_buf.data_ptr(), lds, M * lds,
+                                  ts.data_ptr() if ts is not None else None, _stream(stream))
+    _check(st, "fp4_gemm_quantize_output")
+    scales = scales_buf[:, :, : N // blk]
+    if a.codes.dim() == 2:
+        codes, scales = codes[0], scales[0]
+    return Quantized(qfmt, codes, scales, ts)
 
 
 def gemm_grouped(a: Quantized, b: Quantized, offsets, out_dtype=None, stream=None):

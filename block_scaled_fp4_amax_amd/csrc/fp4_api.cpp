@@ -235,6 +235,66 @@ fp4_status fp4_dequantize(int32_t format, int64_t batch, int64_t rows, int64_t c
   return launch_dequantize(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FP4_OK : FP4_ERR_HIP;
 }
 
+// Checks shared by the dense GEMM entry points (everything but the output)
+// and the operand half of GemmArgs.
+static fp4_status plan_gemm_operands(int32_t format, int64_t groups, int64_t M, int64_t N, int64_t K,
+                                     const uint8_t* a_codes, int64_t lda, int64_t a_group_stride,
+                                     const uint8_t* a_scales, int64_t lda_scales, int64_t a_scales_group_stride,
+                                     const float* a_tensor_scale,
+                                     const uint8_t* b_codes, int64_t ldb, int64_t b_group_stride,
+                                     const uint8_t* b_scales, int64_t ldb_scales, int64_t b_scales_group_stride,
+                                     const float* b_tensor_scale, GemmArgs* g) {
+  if (format != FP4_MXFP4 && format != FP4_NVFP4) return FP4_ERR_INVALID;
+  if (groups < 0 || M < 0 || N < 0 || K < 0) return FP4_ERR_INVALID;
+  if (K % 64 != 0) return FP4_ERR_INVALID;
+  if (groups > kMaxGridYZ || (M + 127) / 128 > kMaxGridYZ || (N + 127) / 128 > kMaxGridX) return FP4_ERR_UNSUPPORTED;
+  const bool nv = format == FP4_NVFP4;
+  const int64_t blk = nv ? 16 : 32;
+  if (!a_codes || !a_scales || !b_codes || !b_scales) return FP4_ERR_INVALID;
+  if (nv && (!a_tensor_scale || !b_tensor_scale)) return FP4_ERR_INVALID;
+  if (lda < K / 2 || ldb < K / 2 || lda_scales < K / blk || ldb_scales < K / blk) return FP4_ERR_INVALID;
+  if (groups > 1 && (a_group_stride < 0 || b_group_stride < 0 || a_scales_group_stride < 0 ||
+                     b_scales_group_stride < 0))
+    return FP4_ERR_INVALID;
+  if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || lda % 16 != 0 || ldb % 16 != 0) return FP4_ERR_ALIGN;
+  // per-group operand panels are addressed with 32-bit offsets, and a
+  // 256-row tile's offsets stay below 2^31 (row pitches below 8 MiB)
+  if (M * lda >= (int64_t(1) << 31) || N * ldb >= (int64_t(1) << 31) || M * lda_scales >= (int64_t(1) << 31) ||
+      N * ldb_scales >= (int64_t(1) << 31))
+    return FP4_ERR_UNSUPPORTED;
+  if (lda >= (int64_t(1) << 23) || ldb >= (int64_t(1) << 23) || lda_scales >= (int64_t(1) << 23) ||
+      ldb_scales >= (int64_t(1) << 23))
+    return FP4_ERR_UNSUPPORTED;
+  if (groups > 1 && (a_group_stride % 16 != 0 || b_group_stride % 16 != 0)) return FP4_ERR_ALIGN;
+  // scale rows are read 16 bytes at a time, up to the next multiple of 16
+  if (!aligned(a_scales, 16) || !aligned(b_scales, 16) || lda_scales % 16 != 0 || ldb_scales % 16 != 0 ||
+      (groups > 1 && (a_scales_group_stride % 16 != 0 || b_scales_group_stride % 16 != 0)))
+    return FP4_ERR_ALIGN;
+  if (nv && (!aligned(a_tensor_scale, 4) || !aligned(b_tensor_scale, 4))) return FP4_ERR_ALIGN;
+  *g = GemmArgs{};
+  g->nvfp4 = nv;
+  g->groups = groups;
+  g->M = M;
+  g->N = N;
+  g->K = K;
+  g->a = a_codes;
+  g->lda = lda;
+  g->a_gs = groups > 1 ? a_group_stride : 0;
+  g->as = a_scales;
+  g->lda_s = lda_scales;
+  g->as_gs = groups > 1 ? a_scales_group_stride : 0;
+  g->a_ts = a_tensor_scale;
+  g->a_ts_gs = 1;
+  g->b = b_codes;
+  g->ldb = ldb;
+  g->b_gs = groups > 1 ? b_group_stride : 0;
+  g->bs = b_scales;
+  g->ldb_s = ldb_scales;
+  g->bs_gs = groups > 1 ? b_scales_group_stride : 0;
+  g->b_ts = b_tensor_scale;
+  return FP4_OK;
+}
+
 fp4_status fp4_gemm(int32_t format, int64_t groups, int64_t M, int64_t N, int64_t K,
                     const uint8_t* a_codes, int64_t lda, int64_t a_group_stride,
                     const uint8_t* a_scales, int64_t lda_scales, int64_t a_scales_group_stride,
@@ -249,52 +309,16 @@ fp4_status fp4_gemm(int32_t format, int64_t groups, int64_t M, int64_t N, int64_
   if (K % 64 != 0) return FP4_ERR_INVALID;
   if (groups > kMaxGridYZ || (M + 127) / 128 > kMaxGridYZ || (N + 127) / 128 > kMaxGridX) return FP4_ERR_UNSUPPORTED;
   if (groups == 0 || M == 0 || N == 0) return FP4_OK;
-  const bool nv = format == FP4_NVFP4;
-  const int64_t blk = nv ? 16 : 32;
-  if (!a_codes || !a_scales || !b_codes || !b_scales || !c) return FP4_ERR_INVALID;
-  if (nv && (!a_tensor_scale || !b_tensor_scale)) return FP4_ERR_INVALID;
-  if (lda < K / 2 || ldb < K / 2 || lda_scales < K / blk || ldb_scales < K / blk || ldc < N) return FP4_ERR_INVALID;
-  if (groups > 1 && (a_group_stride < 0 || b_group_stride < 0 || a_scales_group_stride < 0 ||
-                     b_scales_group_stride < 0 || c_group_stride < (M - 1) * ldc + N))
-    return FP4_ERR_INVALID;
-  if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || lda % 16 != 0 || ldb % 16 != 0) return FP4_ERR_ALIGN;
-  // per-group operand panels are addressed with 32-bit offsets, and a
-  // 256-row tile's offsets stay below 2^31 (row pitches below 8 MiB)
-  if (M * lda >= (int64_t(1) << 31) || N * ldb >= (int64_t(1) << 31) || M * lda_scales >= (int64_t(1) << 31) ||
-      N * ldb_scales >= (int64_t(1) << 31))
-    return FP4_ERR_UNSUPPORTED;
-  if (lda >= (int64_t(1) << 23) || ldb >= (int64_t(1) << 23) || lda_scales >= (int64_t(1) << 23) ||
-      ldb_scales >= (int64_t(1) << 23))
-    return FP4_ERR_UNSUPPORTED;
-  if (groups > 1 && (a_group_stride % 16 != 0 || b_group_stride % 16 != 0)) return FP4_ERR_ALIGN;
-  if (!aligned(c, c_dtype == FP4_BF16 ? 2 : 4)) return FP4_ERR_ALIGN;
-  // scale rows are read 16 bytes at a time, up to the next multiple of 16
-  if (!aligned(a_scales, 16) || !aligned(b_scales, 16) || lda_scales % 16 != 0 || ldb_scales % 16 != 0 ||
-      (groups > 1 && (a_scales_group_stride % 16 != 0 || b_scales_group_stride % 16 != 0)))
-    return FP4_ERR_ALIGN;
-  if (nv && (!aligned(a_tensor_scale, 4) || !aligned(b_tensor_scale, 4))) return FP4_ERR_ALIGN;
-  fp4_status st = check_device();
-  if (st != FP4_OK) return st;
   GemmArgs g;
-  g.nvfp4 = nv;
-  g.groups = groups;
-  g.M = M;
-  g.N = N;
-  g.K = K;
-  g.a = a_codes;
-  g.lda = lda;
-  g.a_gs = groups > 1 ? a_group_stride : 0;
-  g.as = a_scales;
-  g.lda_s = lda_scales;
-  g.as_gs = groups > 1 ? a_scales_group_stride : 0;
-  g.a_ts = a_tensor_scale;
-  g.b = b_codes;
-  g.ldb = ldb;
-  g.b_gs = groups > 1 ? b_group_stride : 0;
-  g.bs = b_scales;
-  g.ldb_s = ldb_scales;
-  g.bs_gs = groups > 1 ? b_scales_group_stride : 0;
-  g.b_ts = b_tensor_scale;
+  fp4_status st = plan_gemm_operands(format, groups, M, N, K, a_codes, lda, a_group_stride, a_scales, lda_scales,
+                                     a_scales_group_stride, a_tensor_scale, b_codes, ldb, b_group_stride, b_scales,
+                                     ldb_scales, b_scales_group_stride, b_tensor_scale, &g);
+  if (st != FP4_OK) return st;
+  if (!c || ldc < N) return FP4_ERR_INVALID;
+  if (groups > 1 && c_group_stride < (M - 1) * ldc + N) return FP4_ERR_INVALID;
+  if (!aligned(c, c_dtype == FP4_BF16 ? 2 : 4)) return FP4_ERR_ALIGN;
+  st = check_device();
+  if (st != FP4_OK) return st;
   g.c = c;
   g.c_bf16 = c_dtype == FP4_BF16;
   g.ldc = ldc;
@@ -303,8 +327,62 @@ fp4_status fp4_gemm(int32_t format, int64_t groups, int64_t M, int64_t N, int64_
     const int64_t es = c_dtype == FP4_BF16 ? 2 : 4;
     g.c_vec_ok = aligned(c, 16) && (ldc * es) % 16 == 0 && (groups == 1 || (c_group_stride * es) % 16 == 0);
   }
-  g.a_ts_gs = 1;
-  g.offs = nullptr;
+  (void)hipGetLastError();
+  return launch_gemm(g, static_cast<hipStream_t>(stream)) == hipSuccess ? FP4_OK : FP4_ERR_HIP;
+}
+
+fp4_status fp4_gemm_quantize_output(int32_t format, int64_t groups, int64_t M, int64_t N, int64_t K,
+                                    const uint8_t* a_codes, int64_t lda, int64_t a_group_stride,
+                                    const uint8_t* a_scales, int64_t lda_scales, int64_t a_scales_group_stride,
+                                    const float* a_tensor_scale,
+                                    const uint8_t* b_codes, int64_t ldb, int64_t b_group_stride,
+                                    const uint8_t* b_scales, int64_t ldb_scales, int64_t b_scales_group_stride,
+                                    const float* b_tensor_scale, const fp4_quant_opts* out_opts,
+                                    uint8_t* out_codes, int64_t ld_out_codes, int64_t out_codes_group_stride,
+                                    uint8_t* out_scales, int64_t ld_out_scales, int64_t out_scales_group_stride,
+                                    float* out_tensor_scale, void* stream) {
+  if (format != FP4_MXFP4 && format != FP4_NVFP4) return FP4_ERR_INVALID;
+  if (!out_opts || out_opts->size != sizeof(fp4_quant_opts)) return FP4_ERR_INVALID;
+  if (out_opts->format != FP4_MXFP4 && out_opts->format != FP4_NVFP4) return FP4_ERR_INVALID;
+  if (out_opts->flags & ~kKnownFlags) return FP4_ERR_INVALID;
+  const bool qnv = out_opts->format == FP4_NVFP4;
+  if (out_opts->flags & (FP4_BLOCK2D | FP4_TRANSPOSE)) return FP4_ERR_UNSUPPORTED;
+  if (!qnv && (out_opts->flags & FP4_FOUR_OVER_SIX)) return FP4_ERR_UNSUPPORTED;
+  if (groups < 0 || M < 0 || N < 0 || K < 0) return FP4_ERR_INVALID;
+  const int64_t qblk = qnv ? 16 : 32;
+  if (K % 64 != 0 || N % qblk != 0) return FP4_ERR_INVALID;
+  if (groups > kMaxGridYZ || (M + 127) / 128 > kMaxGridYZ || (N + 127) / 128 > kMaxGridX) return FP4_ERR_UNSUPPORTED;
+  if (groups == 0 || M == 0 || N == 0) return FP4_OK;
+  GemmArgs g;
+  fp4_status st = plan_gemm_operands(format, groups, M, N, K, a_codes, lda, a_group_stride, a_scales, lda_scales,
+                                     a_scales_group_stride, a_tensor_scale, b_codes, ldb, b_group_stride, b_scales,
+                                     ldb_scales, b_scales_group_stride, b_tensor_scale, &g);
+  if (st != FP4_OK) return st;
+  if (!out_codes || !out_scales || ld_out_codes < N / 2 || ld_out_scales < N / qblk) return FP4_ERR_INVALID;
+  if (qnv && (!out_tensor_scale || !out_opts->amax_in)) return FP4_ERR_INVALID;
+  if (groups > 1 && (out_codes_group_stride < (M - 1) * ld_out_codes + N / 2 ||
+                     out_scales_group_stride < (M - 1) * ld_out_scales + N / qblk))
+    return FP4_ERR_INVALID;
+  if (!aligned(out_codes, 8) || ld_out_codes % 8 != 0 || (groups > 1 && out_codes_group_stride % 8 != 0))
+    return FP4_ERR_ALIGN;
+  if (qnv && (!aligned(out_tensor_scale, 4) || !aligned(out_opts->amax_in, 4))) return FP4_ERR_ALIGN;
+  st = check_device();
+  if (st != FP4_OK) return st;
+  g.qc = out_codes;
+  g.ldqc = ld_out_codes;
+  g.qc_gs = groups > 1 ? out_codes_group_stride : 0;
+  g.qs = out_scales;
+  g.ldqs = ld_out_scales;
+  g.qs_gs = groups > 1 ? out_scales_group_stride : 0;
+  g.q_ts = out_tensor_scale;
+  g.q_amax = out_opts->amax_in;
+  g.q_nv = qnv;
+  g.q_fos = (out_opts->flags & FP4_FOUR_OVER_SIX) != 0;
+  g.q_sr = (out_opts->flags & FP4_STOCHASTIC) != 0;
+  g.q_rht = (out_opts->flags & FP4_HADAMARD) != 0;
+  g.q_signs = out_opts->rht_signs;
+  g.q_seed = out_opts->seed;
+  g.q_offset = out_opts->offset;
   (void)hipGetLastError();
   return launch_gemm(g, static_cast<hipStream_t>(stream)) == hipSuccess ? FP4_OK : FP4_ERR_HIP;
 }
@@ -343,7 +421,7 @@ fp4_status fp4_gemm_grouped(int32_t format, int64_t groups, const int32_t* group
   if (nv && (!aligned(a_tensor_scale, 4) || !aligned(b_tensor_scale, 4))) return FP4_ERR_ALIGN;
   fp4_status st = check_device();
   if (st != FP4_OK) return st;
-  GemmArgs g;
+  GemmArgs g{};
   g.nvfp4 = nv;
   g.groups = groups;
   g.M = M;

@@ -46,6 +46,7 @@
 
 #include "fp4_device.h"
 #include "launch.h"
+#include "quant_common.h"
 
 namespace fp4impl {
 using namespace fp4dev;
@@ -351,6 +352,10 @@ __device__ __forceinline__ void stage_wave_rows(const f32x16 (&acc)[4][WN / 32],
 // reg0 + wn * reg_stride, columns [wn WN, (wn + 1) WN)) and goes to output row
 // m_base + row; a lane converts 8 consecutive values and writes them in one
 // piece, consecutive lanes along the row.
+// What the epilogue writes: C in fp32 or bf16, or C quantized along its rows
+// (MXFP4 or NVFP4 codes and scales).
+enum OutKind { kOutF32 = 0, kOutBF16 = 1, kOutMX = 2, kOutNV = 3 };
+
 template <int WN, int NWN, int NR, bool OUT_BF16>
 __device__ __forceinline__ void store_staged_rows(const GemmArgs& g, const uint8_t* reg0, int reg_stride, int row0,
                                                   int64_t grp, int64_t m_base, int64_t m_end, int64_t n0, int lane) {
@@ -393,7 +398,69 @@ __device__ __forceinline__ void store_staged_rows(const GemmArgs& g, const uint8
   }
 }
 
-template <bool NV, int BN, int WAVES, bool OUT_BF16, bool VAR>
+// NVFP4 constants of the quantized output of group grp: S_t from the
+// caller's amax of C exactly as fp4_quantize forms it, the candidate
+// multipliers, and no reciprocal table (a block divides instead).
+__device__ __forceinline__ float out_tensor_scale(const GemmArgs& g, int64_t grp) {
+  float St = g.q_amax[grp] / (g.q_fos ? 1792.0f : 2688.0f);
+  if (!(St >= kFltMin && St <= 3.40282347e38f)) St = 1.0f;
+  return St;
+}
+
+// Quantized output: a wave quantizes rows row0 + [0, NR) of a round's staged
+// blocks (as store_staged_rows joins them), one 16-value unit per lane with
+// consecutive lanes along the row, so an MXFP4 block is a lane pair (xor 1).
+// The unit is quantized as fp4_quantize quantizes a row-major matrix holding
+// C (with the Hadamard transform, 4/6 and stochastic rounding as set; the
+// stochastic-rounding index of element (m, n) of group grp is
+// (grp M + m) N + n); every lane takes part, stores only for valid units.
+template <int WN, int NWN, int NR, bool QNV>
+__device__ __forceinline__ void store_staged_rows_q(const GemmArgs& g, const uint8_t* reg0, int reg_stride, int row0,
+                                                    int64_t grp, int64_t m_base, int64_t m_end, int64_t n0,
+                                                    int lane, const NvConsts& nc) {
+  using E = Epi<WN>;
+  constexpr int kUPR = WN / 16;  // units per row per block
+#pragma unroll 1
+  for (int c0 = 0; c0 < NR * NWN * kUPR; c0 += 64) {
+    const int c = c0 + lane;
+    const int row = row0 + c / (NWN * kUPR), k = c % (NWN * kUPR);
+    const int wn = k / kUPR, u = k % kUPR;
+    const uint8_t* rp = reg0 + wn * reg_stride + row * E::kRowB;
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const float4 f = *reinterpret_cast<const float4*>(rp + (((4 * u + q) ^ (row & E::kSwz)) * 16));
+      v[4 * q] = f.x;
+      v[4 * q + 1] = f.y;
+      v[4 * q + 2] = f.z;
+      v[4 * q + 3] = f.w;
+    }
+    const int64_t m = m_base + row;
+    const int64_t n = n0 + wn * WN + u * 16;
+    if (g.q_rht) rht16(v, g.q_signs);
+    const uint64_t L0 = (uint64_t)((grp * g.M + m) * g.N + n);
+    uint32_t w0, w1, sbyte;
+    if constexpr (QNV) {
+      if (g.q_fos) {
+        if (g.q_sr) quantize_unit<true, true, false, true, false>(v, nc, L0, g.q_seed, g.q_offset, w0, w1, sbyte);
+        else quantize_unit<true, true, false, false, false>(v, nc, L0, g.q_seed, g.q_offset, w0, w1, sbyte);
+      } else {
+        if (g.q_sr) quantize_unit<true, false, false, true, false>(v, nc, L0, g.q_seed, g.q_offset, w0, w1, sbyte);
+        else quantize_unit<true, false, false, false, false>(v, nc, L0, g.q_seed, g.q_offset, w0, w1, sbyte);
+      }
+    } else {
+      if (g.q_sr) quantize_unit<false, false, false, true, false>(v, nc, L0, g.q_seed, g.q_offset, w0, w1, sbyte);
+      else quantize_unit<false, false, false, false, false>(v, nc, L0, g.q_seed, g.q_offset, w0, w1, sbyte);
+    }
+    if (m < m_end && n < g.N) {
+      *reinterpret_cast<uint2*>(g.qc + grp * g.qc_gs + m * g.ldqc + n / 2) = make_uint2(w0, w1);
+      if constexpr (QNV) g.qs[grp * g.qs_gs + m * g.ldqs + n / 16] = (uint8_t)sbyte;
+      else if ((u & 1) == 0) g.qs[grp * g.qs_gs + m * g.ldqs + n / 32] = (uint8_t)sbyte;
+    }
+  }
+}
+
+template <bool NV, int BN, int WAVES, int OUT, bool VAR>
 __global__ __launch_bounds__(WAVES * 64, 1) void gemm_fp4_kernel(GemmArgs g) {
   using T = Tile<NV, BN, WAVES>;
   constexpr int NJ = T::kNJ;
@@ -402,6 +469,11 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_fp4_kernel(GemmArgs g) {
 
   using Walk = typename std::conditional<VAR, VarWalk, DenseWalk>::type;
   const Walk walk(g, BN);
+  if constexpr (OUT == kOutNV) {
+    // the output tensor scales, written once for every group
+    if (blockIdx.x == 0)
+      for (int64_t i = threadIdx.x; i < g.groups; i += blockDim.x) g.q_ts[i] = out_tensor_scale(g, i);
+  }
   TilePos pos;
   if (!walk.get(0, &pos)) return;
 
@@ -687,6 +759,12 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_fp4_kernel(GemmArgs g) {
     lds_barrier();
     float alpha = 1.0f;
     if constexpr (NV) alpha = scalar_load_f32(g.a_ts + cgrp * g.a_ts_gs) * scalar_load_f32(g.b_ts + cgrp);
+    NvConsts nc_out{};
+    if constexpr (OUT == kOutNV) {
+      nc_out.St = out_tensor_scale(g, cgrp);
+      nc_out.k6 = 1.0f / (6.0f * nc_out.St);
+      nc_out.k4 = 1.0f / (4.0f * nc_out.St);
+    }
     {
       // wave w = wm + 2 wn stages into region(w): slot w / kWPS, part w % kWPS
       using E = Epi<T::kWN>;
@@ -701,9 +779,16 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_fp4_kernel(GemmArgs g) {
         wait_lgkm0();
         lds_barrier();
         // wave s: rows (s >> 1) * kNR + [0, kNR) of the blocks of the waves with wm = s & 1
-        store_staged_rows<T::kWN, WAVES / 2, kNR, OUT_BF16>(g, region(sm), (int)(region(sm + 2) - region(sm)),
-                                                              sh * kNR, cgrp, m0 + sm * 128 + round * RR, mend, n0,
-                                                              lane);
+        if constexpr (OUT == kOutF32 || OUT == kOutBF16) {
+          store_staged_rows<T::kWN, WAVES / 2, kNR, OUT == kOutBF16>(g, region(sm),
+                                                                    (int)(region(sm + 2) - region(sm)), sh * kNR,
+                                                                    cgrp, m0 + sm * 128 + round * RR, mend, n0, lane);
+        } else {
+          store_staged_rows_q<T::kWN, WAVES / 2, kNR, OUT == kOutNV>(g, region(sm),
+                                                                    (int)(region(sm + 2) - region(sm)), sh * kNR,
+                                                                    cgrp, m0 + sm * 128 + round * RR, mend, n0, lane,
+                                                                    nc_out);
+        }
         wait_lgkm0();
         lds_barrier();
       }
@@ -739,8 +824,15 @@ static void launch_tiles_v(const GemmArgs& g, hipStream_t s) {
   const int64_t cus = device_cu_count();
   if (wgs > cus) wgs = cus - cus % 8;
   dim3 grid((unsigned)wgs);
-  if (g.c_bf16) hipLaunchKernelGGL((gemm_fp4_kernel<NV, BN, WAVES, true, VAR>), grid, dim3(WAVES * 64), 0, s, g);
-  else hipLaunchKernelGGL((gemm_fp4_kernel<NV, BN, WAVES, false, VAR>), grid, dim3(WAVES * 64), 0, s, g);
+  if constexpr (!VAR && BN == 128) {
+    if (g.qc) {
+      if (g.q_nv) hipLaunchKernelGGL((gemm_fp4_kernel<NV, BN, WAVES, kOutNV, false>), grid, dim3(WAVES * 64), 0, s, g);
+      else hipLaunchKernelGGL((gemm_fp4_kernel<NV, BN, WAVES, kOutMX, false>), grid, dim3(WAVES * 64), 0, s, g);
+      return;
+    }
+  }
+  if (g.c_bf16) hipLaunchKernelGGL((gemm_fp4_kernel<NV, BN, WAVES, kOutBF16, VAR>), grid, dim3(WAVES * 64), 0, s, g);
+  else hipLaunchKernelGGL((gemm_fp4_kernel<NV, BN, WAVES, kOutF32, VAR>), grid, dim3(WAVES * 64), 0, s, g);
 }
 template <bool NV, int BN, int WAVES>
 static void launch_tiles(const GemmArgs& g, hipStream_t s) {
@@ -763,7 +855,9 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
     // fit beside 256 accumulators
     launch_tiles<true, 128, kWavesNv>(g, s);
   } else {
-    if (wide) launch_tiles<false, 256, kWavesMx>(g, s);
+    // a quantized output keeps the 128-wide tile: beside 256 accumulators
+    // the quantizer's temporaries would spill
+    if (wide && !g.qc) launch_tiles<false, 256, kWavesMx>(g, s);
     else launch_tiles<false, 128, kWavesMx>(g, s);
   }
   return hipGetLastError();

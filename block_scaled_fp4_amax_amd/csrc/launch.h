@@ -78,6 +78,19 @@ struct GemmArgs {
   // int32[groups + 1]: group g is rows [offs[g], offs[g + 1]) of one A and
   // one C of M rows (group strides of A and C zero).
   const int32_t* offs;
+  // Quantized output instead of C (qc non-NULL; equal groups only): C_g
+  // quantized along its rows into codes qc [M, N/2] and scales qs
+  // [M, N/blk] per group; NVFP4 (q_nv) takes S_t from q_amax[g] and writes
+  // it to q_ts[g].
+  uint8_t* qc;
+  int64_t ldqc, qc_gs;
+  uint8_t* qs;
+  int64_t ldqs, qs_gs;
+  float* q_ts;
+  const float* q_amax;
+  bool q_nv, q_fos, q_sr, q_rht;
+  uint32_t q_signs;
+  uint64_t q_seed, q_offset;
 };
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream);

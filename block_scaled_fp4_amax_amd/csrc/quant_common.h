@@ -38,6 +38,9 @@ struct NvConsts {
   const float* rtab;
 };
 
+// TAB false: no table; the reciprocal is divided out (the same correctly
+// rounded value the table holds).
+template <bool TAB = true>
 __device__ __forceinline__ NvCand nv_candidate(float amax, float k, const NvConsts& nc) {
   NvCand c;
   float s = amax * k;
@@ -45,7 +48,8 @@ __device__ __forceinline__ NvCand nv_candidate(float amax, float k, const NvCons
   c.code = e4m3_encode(s);
   c.eff = e4m3_decode(c.code) * nc.St;
   c.zero = !(c.eff >= kFltMin);
-  c.r = nc.rtab[c.code & 127u];
+  if constexpr (TAB) c.r = nc.rtab[c.code & 127u];
+  else c.r = c.zero ? 0.0f : 1.0f / c.eff;
   return c;
 }
 
@@ -106,6 +110,75 @@ __device__ __forceinline__ void sr16(const float q[16], uint64_t L0, uint64_t se
     uint32_t r16b = (i & 1) ? (wb >> 16) : (wb & 0xffffu);
     w0 |= e2m1_sr(q[i], r16a) << (4 * i);
     w1 |= e2m1_sr(q[8 + i], r16b) << (4 * i);
+  }
+}
+
+// Quantize the 16 consecutive values v of one lane (a 16-value unit of an
+// output row, after the Hadamard transform if any) whose first element has
+// linear output index L0: packed codes w0 (elements 0..7), w1 (8..15) and
+// the scale byte. Lanes exchange data, so every lane of a wave calls this
+// together: MXFP4 units pair with the xor-1 lane into one 32-value block;
+// under B2D the 16 lanes xor 1..8 hold the 16 rows of one 16 x 16 tile.
+template <bool NV, bool FOS, bool B2D, bool SR, bool TAB = true>
+__device__ __forceinline__ void quantize_unit(const float v[16], const NvConsts& nc, uint64_t L0, uint64_t seed,
+                                              uint64_t offset, uint32_t& w0, uint32_t& w1, uint32_t& sbyte) {
+  float amax = max_abs16(v);
+  if constexpr (!NV) {
+    amax = __builtin_fmaxf(amax, xor_shfl<1>(amax));
+    sbyte = e8m0_from_amax(amax);
+    if constexpr (SR) {
+      float q[16];
+#pragma unroll
+      for (int i = 0; i < 16; i++) q[i] = __builtin_ldexpf(v[i], 127 - (int)sbyte);
+      sr16(q, L0, seed, offset, w0, w1);
+    } else {
+      float sc = e8m0_scale_operand(sbyte);
+      w0 = e2m1_pack2_scaled<0>(0u, v[0], v[1], sc);
+      w0 = e2m1_pack2_scaled<1>(w0, v[2], v[3], sc);
+      w0 = e2m1_pack2_scaled<2>(w0, v[4], v[5], sc);
+      w0 = e2m1_pack2_scaled<3>(w0, v[6], v[7], sc);
+      w1 = e2m1_pack2_scaled<0>(0u, v[8], v[9], sc);
+      w1 = e2m1_pack2_scaled<1>(w1, v[10], v[11], sc);
+      w1 = e2m1_pack2_scaled<2>(w1, v[12], v[13], sc);
+      w1 = e2m1_pack2_scaled<3>(w1, v[14], v[15], sc);
+    }
+  } else {
+    if constexpr (B2D) {
+      amax = __builtin_fmaxf(amax, xor_shfl<1>(amax));
+      amax = __builtin_fmaxf(amax, xor_shfl<2>(amax));
+      amax = __builtin_fmaxf(amax, xor_shfl<4>(amax));
+      amax = __builtin_fmaxf(amax, xor_shfl<8>(amax));
+    }
+    NvCand c = nv_candidate<TAB>(amax, nc.k6, nc);
+    float q[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) q[i] = v[i] * c.r;
+    pack16(q, w0, w1);
+    if constexpr (FOS) {
+      NvCand c4 = nv_candidate<TAB>(amax, nc.k4, nc);
+      float q4[16];
+#pragma unroll
+      for (int i = 0; i < 16; i++) q4[i] = v[i] * c4.r;
+      uint32_t x0, x1;
+      pack16(q4, x0, x1);
+      float s6 = sq_sum16(q, w0, w1), s4 = sq_sum16(q4, x0, x1);
+      if constexpr (B2D) {
+        // pairwise tree over the tile's 16 rows (lanes), adjacent rows first
+        s6 = s6 + xor_shfl<1>(s6); s4 = s4 + xor_shfl<1>(s4);
+        s6 = s6 + xor_shfl<2>(s6); s4 = s4 + xor_shfl<2>(s4);
+        s6 = s6 + xor_shfl<4>(s6); s4 = s4 + xor_shfl<4>(s4);
+        s6 = s6 + xor_shfl<8>(s6); s4 = s4 + xor_shfl<8>(s4);
+      }
+      if (cand_error(c4, s4) < cand_error(c, s6)) {
+        c = c4;
+        w0 = x0;
+        w1 = x1;
+#pragma unroll
+        for (int i = 0; i < 16; i++) q[i] = q4[i];
+      }
+    }
+    if constexpr (SR) sr16(q, L0, seed, offset, w0, w1);
+    sbyte = c.code;
   }
 }
 

@@ -170,67 +170,9 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(QuantArgs a) {
   raw.unpack(v);
   if constexpr (RHT) rht16(v, a.signs);
 
-  float amax = max_abs16(v);
   uint32_t w0, w1, sbyte;
   const uint64_t L0 = ((uint64_t)b * (uint64_t)a.R + (uint64_t)row) * (uint64_t)a.C + (uint64_t)cu * 16;
-
-  if constexpr (!NV) {
-    amax = __builtin_fmaxf(amax, xor_shfl<1>(amax));
-    sbyte = e8m0_from_amax(amax);
-    if constexpr (SR) {
-      float q[16];
-#pragma unroll
-      for (int i = 0; i < 16; i++) q[i] = __builtin_ldexpf(v[i], 127 - (int)sbyte);
-      sr16(q, L0, a.seed, a.offset, w0, w1);
-    } else {
-      float sc = e8m0_scale_operand(sbyte);
-      w0 = e2m1_pack2_scaled<0>(0u, v[0], v[1], sc);
-      w0 = e2m1_pack2_scaled<1>(w0, v[2], v[3], sc);
-      w0 = e2m1_pack2_scaled<2>(w0, v[4], v[5], sc);
-      w0 = e2m1_pack2_scaled<3>(w0, v[6], v[7], sc);
-      w1 = e2m1_pack2_scaled<0>(0u, v[8], v[9], sc);
-      w1 = e2m1_pack2_scaled<1>(w1, v[10], v[11], sc);
-      w1 = e2m1_pack2_scaled<2>(w1, v[12], v[13], sc);
-      w1 = e2m1_pack2_scaled<3>(w1, v[14], v[15], sc);
-    }
-  } else {
-    if constexpr (B2D) {
-      amax = __builtin_fmaxf(amax, xor_shfl<1>(amax));
-      amax = __builtin_fmaxf(amax, xor_shfl<2>(amax));
-      amax = __builtin_fmaxf(amax, xor_shfl<4>(amax));
-      amax = __builtin_fmaxf(amax, xor_shfl<8>(amax));
-    }
-    NvCand c = nv_candidate(amax, nc.k6, nc);
-    float q[16];
-#pragma unroll
-    for (int i = 0; i < 16; i++) q[i] = v[i] * c.r;
-    pack16(q, w0, w1);
-    if constexpr (FOS) {
-      NvCand c4 = nv_candidate(amax, nc.k4, nc);
-      float q4[16];
-#pragma unroll
-      for (int i = 0; i < 16; i++) q4[i] = v[i] * c4.r;
-      uint32_t x0, x1;
-      pack16(q4, x0, x1);
-      float s6 = sq_sum16(q, w0, w1), s4 = sq_sum16(q4, x0, x1);
-      if constexpr (B2D) {
-        // pairwise tree over the tile's 16 rows (lanes), adjacent rows first
-        s6 = s6 + xor_shfl<1>(s6); s4 = s4 + xor_shfl<1>(s4);
-        s6 = s6 + xor_shfl<2>(s6); s4 = s4 + xor_shfl<2>(s4);
-        s6 = s6 + xor_shfl<4>(s6); s4 = s4 + xor_shfl<4>(s4);
-        s6 = s6 + xor_shfl<8>(s6); s4 = s4 + xor_shfl<8>(s4);
-      }
-      if (cand_error(c4, s4) < cand_error(c, s6)) {
-        c = c4;
-        w0 = x0;
-        w1 = x1;
-#pragma unroll
-        for (int i = 0; i < 16; i++) q[i] = q4[i];
-      }
-    }
-    if constexpr (SR) sr16(q, L0, a.seed, a.offset, w0, w1);
-    sbyte = c.code;
-  }
+  quantize_unit<NV, FOS, B2D, SR>(v, nc, L0, a.seed, a.offset, w0, w1, sbyte);
 
   uint8_t* cp = a.codes + b * a.bs_c + row * a.ld_c + cu * 8;
   *reinterpret_cast<uint2*>(cp) = make_uint2(w0, w1);

@@ -193,6 +193,43 @@ fp4_status fp4_gemm(int32_t format, int64_t groups, int64_t M, int64_t N, int64_
                     void* c, int32_t c_dtype, int64_t ldc, int64_t c_group_stride, void* stream);
 
 /*
+ * fp4_gemm_quantize_output -- fp4_gemm whose epilogue quantizes the product
+ * instead of storing it, so that a W4A4 layer hands the next one FP4
+ * activations without a round trip of C through HBM ("FP4", section
+ * "Inferencia e Treinamento FP4": activations quantized to FP4 for FP4
+ * matrix products). Operands, groups, strides and their errors as for
+ * fp4_gemm. Each C_g [M, N], as fp4_gemm computes it in fp32 (after the
+ * tensor scales), is quantized along its rows exactly as fp4_quantize
+ * quantizes a row-major [M, N] fp32 matrix with out_opts:
+ *   out_opts     format MXFP4 or NVFP4 (either, whatever the operands'
+ *                format); flags FP4_FOUR_OVER_SIX (NVFP4), FP4_STOCHASTIC
+ *                (index of element (m, n) of group g: (g M + m) N + n, as in
+ *                a batched fp4_quantize), FP4_HADAMARD; FP4_BLOCK2D and
+ *                FP4_TRANSPOSE -> FP4_ERR_UNSUPPORTED. NVFP4 needs amax_in:
+ *                device float[groups], the tensor amax to derive S_t from
+ *                (the amax of C is only known once C is complete, so the
+ *                caller supplies it, e.g. from a previous step or a
+ *                calibration; values above it saturate).
+ *   out_codes    device [groups][M, N/2] bytes, row pitch ld_out_codes
+ *                (>= N/2, a multiple of 8; 8-byte aligned base and group
+ *                stride).
+ *   out_scales   device [groups][M, N/blk] bytes, row pitch ld_out_scales.
+ *   out_tensor_scale  NVFP4: device float[groups], receives S_t.
+ * N must be a multiple of the output block (16 or 32), else
+ * FP4_ERR_INVALID.
+ */
+fp4_status fp4_gemm_quantize_output(int32_t format, int64_t groups, int64_t M, int64_t N, int64_t K,
+                                    const uint8_t* a_codes, int64_t lda, int64_t a_group_stride,
+                                    const uint8_t* a_scales, int64_t lda_scales, int64_t a_scales_group_stride,
+                                    const float* a_tensor_scale,
+                                    const uint8_t* b_codes, int64_t ldb, int64_t b_group_stride,
+                                    const uint8_t* b_scales, int64_t ldb_scales, int64_t b_scales_group_stride,
+                                    const float* b_tensor_scale, const fp4_quant_opts* out_opts,
+                                    uint8_t* out_codes, int64_t ld_out_codes, int64_t out_codes_group_stride,
+                                    uint8_t* out_scales, int64_t ld_out_scales, int64_t out_scales_group_stride,
+                                    float* out_tensor_scale, void* stream);
+
+/*
  * fp4_gemm_grouped -- the grouped GEMM of a mixture-of-experts layer, where
  * a router decides how many rows (tokens) each group (expert) gets ("FP4",
  * section "Inferencia e Treinamento FP4": MoE weights in MXFP4, FP4 matrix
