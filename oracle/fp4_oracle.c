@@ -201,7 +201,8 @@ enum {
   OR_BLOCK2D = 2u,
   OR_TRANSPOSE = 4u,
   OR_STOCHASTIC = 8u,
-  OR_HADAMARD = 16u
+  OR_HADAMARD = 16u,
+  OR_SCALE_SEARCH = 32u
 };
 
 static float load_elem(const void* x, int dtype, int64_t idx) {
@@ -285,6 +286,16 @@ static nv_cand nv_candidate(float a, float M, float S_t) {
   return c;
 }
 
+/* The candidate whose E4M3 code is `code` (the scale search below). */
+static nv_cand nv_code_candidate(uint8_t code, float S_t) {
+  nv_cand c;
+  c.code = code;
+  c.eff = or_e4m3_value(code) * S_t;
+  c.zero = !(c.eff >= FLT_MIN);
+  c.r = c.zero ? 0.0f : 1.0f / c.eff;
+  return c;
+}
+
 static uint8_t quant_rne_nv(float x, const nv_cand* c) {
   if (c->zero) return signbit(x) ? 8 : 0;
   return or_e2m1_rne(x * c->r);
@@ -306,6 +317,23 @@ static float row16_sq_err(const float* x, int64_t stride, const nv_cand* c) {
     half[hf] = acc;
   }
   return half[0] + half[1];
+}
+
+/* The 4/6 error of one candidate for the block at (r0, c0): eff^2 times the
+ * row16_sq_err sum, over the 16 source rows of a 16x16 tile combined by a
+ * pairwise tree over adjacent rows; infinite for a zero-block candidate. */
+static float nv_block_sse(const float* w, int64_t C, int64_t r0, int64_t c0, int b2d, int tr, const nv_cand* c) {
+  if (c->zero) return INFINITY;
+  float part[16];
+  if (!b2d) {
+    part[0] = row16_sq_err(&w[r0 * C + c0], 1, c);
+  } else {
+    for (int s = 0; s < 16; s++)
+      part[s] = tr ? row16_sq_err(&w[r0 * C + c0 + s], C, c) : row16_sq_err(&w[(r0 + s) * C + c0], 1, c);
+    for (int width = 1; width < 16; width <<= 1)
+      for (int s = 0; s < 16; s += 2 * width) part[s] = part[s] + part[s + width];
+  }
+  return (c->eff * c->eff) * part[0];
 }
 
 typedef struct {
@@ -332,10 +360,11 @@ int or_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld
                 uint64_t L0, uint8_t* codes, uint8_t* scales, float* tensor_scale, float* amax_out) {
   int nv = o->format == OR_NVFP4;
   int blk = nv ? 16 : 32;
+  int search = nv && (o->flags & OR_SCALE_SEARCH);
   int fos = nv && (o->flags & OR_FOUR_OVER_SIX);
   int b2d = nv && (o->flags & OR_BLOCK2D);
   int sr = (o->flags & OR_STOCHASTIC) != 0;
-  if (!nv && (o->flags & (OR_FOUR_OVER_SIX | OR_BLOCK2D))) return -1;
+  if (!nv && (o->flags & (OR_BLOCK2D | OR_SCALE_SEARCH))) return -1;
   int64_t R, C;
   float* w = working_matrix(x, dtype, rows, cols, ld, o->flags, o->rht_signs, &R, &C);
   if (!w) return -1;
@@ -356,6 +385,34 @@ int or_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld
         for (int i = 0; i < blk; i++)
           if (fabsf(v[i]) > a) a = fabsf(v[i]);
         int e = or_e8m0_exponent(a);
+        if ((o->flags & OR_FOUR_OVER_SIX) && e < 127) {
+          /* 4/6 carried over to power-of-two scales (a reading; the pages
+           * define 4/6 for NVFP4 only): the block max lands in [4, 8) under
+           * e, in [2, 4) under e + 1, which clips nothing. Keep the exponent
+           * with the smaller squared error SSE_e = 4^e * S_e, S_e the sum of
+           * (val - q)^2 over the block with q = x * 2^-e, taken per 16-value
+           * half as in row16_sq_err and the halves added; e + 1 wins iff
+           * 4 * S_{e+1} < S_e (the 4^e factor cancels exactly). */
+          float S[2];
+          for (int k = 0; k < 2; k++) {
+            float half[2];
+            for (int hf = 0; hf < 2; hf++) {
+              float part[2];
+              for (int p8 = 0; p8 < 2; p8++) {
+                float acc = 0.0f;
+                for (int i = 16 * hf + 8 * p8; i < 16 * hf + 8 * p8 + 8; i++) {
+                  float q = ldexpf(v[i], -(e + k));
+                  float d = or_e2m1_value(or_e2m1_rne(q)) - q;
+                  acc = fmaf(d, d, acc);
+                }
+                part[p8] = acc;
+              }
+              half[hf] = part[0] + part[1];
+            }
+            S[k] = half[0] + half[1];
+          }
+          if (4.0f * S[1] < S[0]) e = e + 1;
+        }
         scales[r * nb + b] = (uint8_t)(e + 127);
         for (int i = 0; i < blk; i++) {
           int64_t col = b * blk + i;
@@ -379,7 +436,7 @@ int or_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld
     for (int64_t i = 0; i < R * C; i++)
       if (fabsf(w[i]) > T) T = fabsf(w[i]);
   }
-  float S_t = or_nvfp4_tensor_scale(T, fos);
+  float S_t = or_nvfp4_tensor_scale(T, fos || search);
   if (tensor_scale) *tensor_scale = S_t;
   if (amax_out) *amax_out = T;
 
@@ -395,7 +452,24 @@ int or_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld
 
       nv_cand c6 = nv_candidate(a, 6.0f, S_t);
       nv_cand chosen = c6;
-      if (fos) {
+      if (search) {
+        /* The 4/6 choice widened to every E4M3 scale between the two: the
+         * candidates are the codes from the M = 6 candidate's up to the
+         * M = 4 candidate's, so the block max maps to each representable
+         * point between 6 and 4 (a reading of "more candidate maxima"; the
+         * tensor scale is the 4/6 one). Each candidate's error is the 4/6
+         * error below; the smallest wins, ties keep the smaller code. */
+        uint8_t hi = nv_candidate(a, 4.0f, S_t).code;
+        float best = nv_block_sse(w, C, r0, c0, b2d, (o->flags & OR_TRANSPOSE) != 0, &c6);
+        for (int code = c6.code + 1; code <= hi; code++) {
+          nv_cand c = nv_code_candidate((uint8_t)code, S_t);
+          float e = nv_block_sse(w, C, r0, c0, b2d, (o->flags & OR_TRANSPOSE) != 0, &c);
+          if (e < best) {
+            best = e;
+            chosen = c;
+          }
+        }
+      } else if (fos) {
         /* [4o6] introduction: each block's max maps to 4 or to 6, keeping the
          * lower-error choice. Reading: error = sum of squared errors,
          * SSE_M = eff_M^2 * sum_i (val_i - q_i)^2 with q_i = x_i * r_M, the
@@ -405,28 +479,8 @@ int or_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld
          * tree over adjacent rows. Pick 4 iff SSE_4 < SSE_6 (ties keep 6). A
          * zero-block candidate has infinite error. */
         nv_cand c4 = nv_candidate(a, 4.0f, S_t);
-        float sse[2];
-        nv_cand* cs[2] = {&c6, &c4};
-        for (int k = 0; k < 2; k++) {
-          nv_cand* c = cs[k];
-          if (c->zero) {
-            sse[k] = INFINITY;
-            continue;
-          }
-          float part[16];
-          int tr = (o->flags & OR_TRANSPOSE) != 0;
-          if (!b2d) {
-            part[0] = row16_sq_err(&w[r0 * C + c0], 1, c);
-          } else {
-            /* source row s of the tile is output row s (as-is) or output
-             * column s (transposed); its 16 elements in source-column order */
-            for (int s = 0; s < 16; s++)
-              part[s] = tr ? row16_sq_err(&w[r0 * C + c0 + s], C, c) : row16_sq_err(&w[(r0 + s) * C + c0], 1, c);
-            for (int width = 1; width < 16; width <<= 1)
-              for (int s = 0; s < 16; s += 2 * width) part[s] = part[s] + part[s + width];
-          }
-          sse[k] = (c->eff * c->eff) * part[0];
-        }
+        int tr = (o->flags & OR_TRANSPOSE) != 0;
+        float sse[2] = {nv_block_sse(w, C, r0, c0, b2d, tr, &c6), nv_block_sse(w, C, r0, c0, b2d, tr, &c4)};
         if (sse[1] < sse[0]) chosen = c4;
       }
 

@@ -42,7 +42,7 @@ LIB = HERE / "liboracle.so"
 
 MXFP4, NVFP4 = 0, 1
 F32, BF16 = 0, 1
-FOUR_OVER_SIX, BLOCK2D, TRANSPOSE, STOCHASTIC, HADAMARD = 1, 2, 4, 8, 16
+FOUR_OVER_SIX, BLOCK2D, TRANSPOSE, STOCHASTIC, HADAMARD, SCALE_SEARCH = 1, 2, 4, 8, 16, 32
 
 CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
 

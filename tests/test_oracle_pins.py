@@ -345,6 +345,103 @@ def test_four_over_six_never_worse_on_worked_example(oracle):
     assert ((d46 - x) ** 2).sum() <= ((d6 - x) ** 2).sum() * 1.01
 
 
+def test_mxfp4_four_over_six_picks_lower_exact_error(oracle):
+    """MXFP4 under 4/6: the scale exponent is the standard one e or e + 1,
+    whichever gives the smaller exact squared error (brute force over both,
+    in exact rationals); codes are then the nearest grid points of
+    x / 2^e'."""
+    rng = np.random.default_rng(31)
+    x = (rng.standard_normal((24, 96)) * np.exp(rng.uniform(-3, 3, (24, 1)))).astype(np.float32)
+    x[3, :32] *= 0.01
+    x[3, 5] = 7.5  # a block whose max clips under e (to 6; under e + 1 it rounds to 4 * 2)
+    q = oracle.quantize(x, oracle.MXFP4, flags=oracle.FOUR_OVER_SIX)
+    plain = oracle.quantize(x, oracle.MXFP4)
+    codes = unpack_codes(q["codes"])
+    picked = 0
+    for r in range(24):
+        for b in range(3):
+            blk = x[r, 32 * b: 32 * b + 32]
+            e0 = int(plain["scales"][r, b]) - 127
+            sse = {}
+            for e in (e0, e0 + 1):
+                cc = brute_e2m1((blk.astype(np.float64) * 2.0 ** -e).astype(np.float32))
+                sse[e] = (_exact_sse(blk, cc, 2.0 ** e), cc)
+            e = int(q["scales"][r, b]) - 127
+            assert e in (e0, e0 + 1)
+            np.testing.assert_array_equal(codes[r, 32 * b: 32 * b + 32], sse[e][1])
+            s0, s1 = sse[e0][0], sse[e0 + 1][0]
+            if abs(s1 - s0) > Fraction(1, 10 ** 4) * s0:
+                assert e == (e0 + 1 if s1 < s0 else e0), (r, b)
+            picked += e == e0 + 1
+    assert 0 < picked < 72  # both exponents occur on this input
+    assert q["scales"][3, 0] - 127 == plain["scales"][3, 0] - 127 + 1  # the clipped block moves up
+
+
+def test_mxfp4_four_over_six_never_worse(oracle):
+    x = inputs.worked_example().numpy().reshape(128, 32)
+    d = oracle.dequantize(oracle.MXFP4, **_qmx(oracle, x, 0))
+    d46 = oracle.dequantize(oracle.MXFP4, **_qmx(oracle, x, oracle.FOUR_OVER_SIX))
+    blk = ((d46 - x).astype(np.float64) ** 2).sum(axis=1)
+    blk0 = ((d - x).astype(np.float64) ** 2).sum(axis=1)
+    assert (blk <= blk0 * (1 + 1e-6)).all()
+    assert blk.sum() < blk0.sum()
+
+
+def _qmx(oracle, x, flags):
+    q = oracle.quantize(x, oracle.MXFP4, flags=flags)
+    return {"codes": q["codes"], "scales": q["scales"]}
+
+
+@pytest.mark.parametrize("flags", [0, 2, 6])
+def test_scale_search_is_argmin_over_the_codes_between_4_and_6(oracle, flags):
+    """NVFP4 scale search: the chosen E4M3 code lies between the M = 6 and
+    M = 4 candidates' codes and has the smallest exact squared error among
+    all of them (brute force in exact rationals, skipping near-ties); the
+    search is never worse than 4/6, which is never worse than plain."""
+    rng = np.random.default_rng(32 + flags)
+    x = (rng.standard_normal((32, 64)) * np.exp(rng.uniform(-2, 2, (32, 64)))).astype(np.float32)
+    fl = oracle.SCALE_SEARCH | flags
+    q = oracle.quantize(x, oracle.NVFP4, flags=fl)
+    q46 = oracle.quantize(x, oracle.NVFP4, flags=oracle.FOUR_OVER_SIX | flags)
+    St = q["tensor_scale"]
+    assert St == q46["tensor_scale"]
+    tr = bool(flags & oracle.TRANSPOSE)
+    xs = x.T if tr else x  # the quantized orientation
+    codes = unpack_codes(q["codes"])
+    tile = 16 if flags & oracle.BLOCK2D else 1
+    widened = 0
+    for r0 in range(0, xs.shape[0], tile):
+        for b in range(xs.shape[1] // 16):
+            blk = xs[r0:r0 + tile, 16 * b: 16 * b + 16]
+            a = float(np.abs(blk).max())
+            lo = int(torch_e4m3(np.array([min(a / (6 * St), 448.0)], np.float32))[0])
+            hi = int(torch_e4m3(np.array([min(a / (4 * St), 448.0)], np.float32))[0])
+            chosen = int(q["scales"][r0, b])
+            assert lo <= chosen <= hi
+            sse = {}
+            for c in range(lo, hi + 1):
+                eff = np.float32(torch_e4m3_value(np.array([c]))[0]) * np.float32(St)
+                flat = blk.reshape(-1)
+                cc = brute_e2m1((flat.astype(np.float64) / float(eff)).astype(np.float32))
+                sse[c] = _exact_sse(flat, cc, eff)
+            best = min(sse.values())
+            runner = sorted(sse.values())[1] if len(sse) > 1 else None
+            if runner is None or runner - best > Fraction(1, 10 ** 4) * best:
+                assert sse[chosen] == best, (r0, b)
+            widened += chosen not in (lo, hi)
+            c46 = int(q46["scales"][r0, b])
+            assert sse[chosen] <= sse[c46] * (1 + Fraction(1, 10 ** 4))
+            for rr in range(r0, r0 + tile):
+                eff = np.float32(torch_e4m3_value(np.array([chosen]))[0]) * np.float32(St)
+                want = brute_e2m1((xs[rr, 16 * b: 16 * b + 16].astype(np.float64) / float(eff)).astype(np.float32))
+                got = codes[rr, 16 * b: 16 * b + 16]
+                mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+                qq = np.abs(xs[rr, 16 * b: 16 * b + 16].astype(np.float64) / float(eff))
+                near = np.min(np.abs(qq[:, None] - mids[None, :]), axis=1) < 1e-6 * qq
+                assert ((got == want) | near).all()
+    assert widened > 0  # candidates strictly between 4 and 6 do win
+
+
 def _q(oracle, x, flags):
     q = oracle.quantize(x, oracle.NVFP4, flags=flags)
     return {"codes": q["codes"], "scales": q["scales"], "tensor_scale": q["tensor_scale"]}
