@@ -64,8 +64,9 @@ def quant_bytes(elems_in, in_bytes, blk, nv, batch=1):
 class QuantCall:
     """Preallocated fp4_quantize call over `sets` input copies."""
 
-    def __init__(self, F, xs, fmt, flags=0, signs=0, seed=0, offset=0):
+    def __init__(self, F, xs, fmt, flags=0, signs=0, seed=0, offset=0, amax=None):
         self.F, self.xs = F, xs
+        self.amax = amax  # device float[batch] or None (kept alive here)
         x = xs[0]
         x3 = x if x.dim() == 3 else x.unsqueeze(0)
         self.batch, self.rows, self.cols = x3.shape
@@ -74,7 +75,7 @@ class QuantCall:
         self.R, self.C = R, C
         self.blk = 16 if fmt == F.FP4_NVFP4 else 32
         dev = x.device
-        self.opts = F.make_opts(fmt, flags, signs, seed, offset)
+        self.opts = F.make_opts(fmt, flags, signs, seed, offset, amax.data_ptr() if amax is not None else 0)
         self.codes = torch.empty((self.batch, R, C // 2), dtype=torch.uint8, device=dev)
         self.lds = F.scale_pitch(C // self.blk)  # scale rows padded to 16 bytes, as the GEMM reads them
         self.scales_buf = torch.empty((self.batch, R, self.lds), dtype=torch.uint8, device=dev)
@@ -330,6 +331,54 @@ def wl_w4a4_fused(F, inputs):
     return ops, cfg, "fp4 e2m1 codes (nvfp4); f16 MFMA, f32 accumulate", None
 
 
+def wl_w4a4_unfused_chain(F, inputs):
+    """The same hand-over as w4a4_fused done the unfused way, for
+    comparison: the GEMM stores bf16 C, then C is quantized to NVFP4 4/6
+    with the same supplied amax."""
+    d = inputs.w4a4_linear(device="cuda")
+    n = n_sets(d["a"].numel() * 2 + d["w"].numel() * 2)
+    qa = QuantCall(F, copies(d["a"], n), F.FP4_NVFP4, F.FP4_FOUR_OVER_SIX)
+    qw = QuantCall(F, copies(d["w"], n), F.FP4_NVFP4, F.FP4_FOUR_OVER_SIX)
+    qa(0)
+    qw(0)
+    gm = GemmCall(F, qa, qw, torch.bfloat16)
+    gm(0)
+    amax = gm.c.float().abs().amax().reshape(1)
+    qc = QuantCall(F, [gm.c], F.FP4_NVFP4, F.FP4_FOUR_OVER_SIX, amax=amax)
+    ops = [Op("quantize A nvfp4 4/6 (amax pre-pass + quantize)", "amax_kernel+quant_rows_kernel", "hbm", qa.bytes(),
+              PEAK_HBM_GBS, qa, "GB/s"),
+           Op("quantize W nvfp4 4/6 (amax pre-pass + quantize)", "amax_kernel+quant_rows_kernel", "hbm", qw.bytes(),
+              PEAK_HBM_GBS, qw, "GB/s"),
+           Op("gemm nvfp4 (exact fp16 dequant + fp16 MFMA)", "gemm_fp4_kernel<true, 128, 4, 1, false>", "mfma",
+              gm.flops(), PEAK_TFLOPS["f16"], gm, "TFLOP/s"),
+           Op("quantize C nvfp4 4/6 (amax supplied)", "quant_rows_kernel", "hbm", qc.bytes(), PEAK_HBM_GBS, qc,
+              "GB/s")]
+    cfg = {"workload": "w4a4_linear_nvfp4_unfused_output_quantize", "M": 2048, "N": 4096, "K": 4096,
+           "activations": "2048x4096 bf16 N(0,1), 1% columns x30", "weight": "4096x4096 bf16 N(0,0.02)",
+           "output": "bf16 C, then nvfp4 4/6 codes + scales, amax supplied", "input_sets_rotated": n}
+    return ops, cfg, "fp4 e2m1 codes (nvfp4); f16 MFMA, f32 accumulate", None
+
+
+def wl_scale_search(F, inputs):
+    """The error-searched scale options on the training weight (8192^2 bf16):
+    NVFP4 with the scale search over every E4M3 code between the 4 and 6
+    candidates, 1D and 2D, and MXFP4 with the 4/6 exponent pair."""
+    d = inputs.training(device="cuda")
+    n = n_sets(d["w"].numel() * 2)
+    ws = copies(d["w"], n)
+    qs = QuantCall(F, ws, F.FP4_NVFP4, F.FP4_SCALE_SEARCH)
+    q2 = QuantCall(F, ws, F.FP4_NVFP4, F.FP4_SCALE_SEARCH | F.FP4_BLOCK2D)
+    qm = QuantCall(F, ws, F.FP4_MXFP4, F.FP4_FOUR_OVER_SIX)
+    ops = [Op("quantize W nvfp4 scale search (amax pre-pass + quantize)", "amax_kernel+quant_rows_kernel", "hbm",
+              qs.bytes(), PEAK_HBM_GBS, qs, "GB/s"),
+           Op("quantize W nvfp4 2D scale search (amax pre-pass + quantize)", "amax_kernel+quant_rows_kernel", "hbm",
+              q2.bytes(), PEAK_HBM_GBS, q2, "GB/s"),
+           Op("quantize W mxfp4 4/6 exponent pair", "quant_rows_kernel", "hbm", qm.bytes(), PEAK_HBM_GBS, qm, "GB/s")]
+    cfg = {"workload": "scale_search_8192", "shape": [8192, 8192], "weight": "8192x8192 bf16 N(0,0.02)",
+           "input_sets_rotated": n}
+    return ops, cfg, "fp4 e2m1 codes, f32 scale arithmetic", None
+
+
 def wl_moe_routed(F, inputs):
     """MoE layer with router-decided rows per expert: 4096 tokens top-4 over
     32 experts (16384 rows, 60 to 1709 per expert), one MXFP4 quantize of the
@@ -352,7 +401,8 @@ def wl_moe_routed(F, inputs):
 
 
 WORKLOADS = {"w4a4_linear": wl_w4a4_linear, "moe": wl_moe, "training": wl_training, "rht": wl_rht,
-             "training_backward": wl_training_backward, "moe_routed": wl_moe_routed, "w4a4_fused": wl_w4a4_fused}
+             "training_backward": wl_training_backward, "moe_routed": wl_moe_routed, "w4a4_fused": wl_w4a4_fused,
+             "w4a4_unfused_chain": wl_w4a4_unfused_chain, "scale_search": wl_scale_search}
 
 
 # ---------------------------------------------------------------------------

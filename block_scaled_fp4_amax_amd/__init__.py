@@ -45,6 +45,7 @@ FP4_BLOCK2D = 2
 FP4_TRANSPOSE = 4
 FP4_STOCHASTIC = 8
 FP4_HADAMARD = 16
+FP4_SCALE_SEARCH = 32
 
 EXPORTED_SYMBOLS = ("fp4_quantize_workspace", "fp4_quantize", "fp4_dequantize", "fp4_gemm", "fp4_gemm_grouped",
                     "fp4_gemm_quantize_output", "fp4_status_str")
@@ -227,7 +228,8 @@ def _check(status: int, where: str):
 
 
 def quantize(x, fmt="nvfp4", *, four_over_six=False, block2d=False, transpose=False, stochastic=False,
-             hadamard=False, rht_signs=0, seed=0, offset=0, amax=None, stream=None) -> Quantized:
+             hadamard=False, scale_search=False, rht_signs=0, seed=0, offset=0, amax=None,
+             stream=None) -> Quantized:
     """Quantize a [rows, cols] or [batch, rows, cols] bf16/fp32 device tensor."""
     import torch
     fmt = _fmt(fmt)
@@ -240,7 +242,7 @@ def quantize(x, fmt="nvfp4", *, four_over_six=False, block2d=False, transpose=Fa
     dt = {torch.bfloat16: FP4_BF16, torch.float32: FP4_F32}[x3.dtype]
     flags = ((FP4_FOUR_OVER_SIX if four_over_six else 0) | (FP4_BLOCK2D if block2d else 0)
              | (FP4_TRANSPOSE if transpose else 0) | (FP4_STOCHASTIC if stochastic else 0)
-             | (FP4_HADAMARD if hadamard else 0))
+             | (FP4_HADAMARD if hadamard else 0) | (FP4_SCALE_SEARCH if scale_search else 0))
     amax_t = None
     if amax is not None:
         amax_t = torch.as_tensor(amax, dtype=torch.float32, device=x3.device).reshape(-1).contiguous()
@@ -319,7 +321,8 @@ def gemm(a: Quantized, b: Quantized, out_dtype=None, stream=None):
 
 
 def gemm_quantize_output(a: Quantized, b: Quantized, fmt="nvfp4", *, four_over_six=False, stochastic=False,
-                         hadamard=False, rht_signs=0, seed=0, offset=0, amax=None, stream=None) -> Quantized:
+                         hadamard=False, scale_search=False, rht_signs=0, seed=0, offset=0, amax=None,
+                         stream=None) -> Quantized:
     """deq(A[g]) @ deq(B[g])^T quantized along its rows in the GEMM's epilogue
     (format `fmt`, options as for quantize); NVFP4 needs `amax`, the tensor
     amax per group that S_t derives from."""
@@ -336,7 +339,7 @@ def gemm_quantize_output(a: Quantized, b: Quantized, fmt="nvfp4", *, four_over_s
         raise ValueError("operand shapes do not match")
     qfmt = _fmt(fmt)
     flags = ((FP4_FOUR_OVER_SIX if four_over_six else 0) | (FP4_STOCHASTIC if stochastic else 0)
-             | (FP4_HADAMARD if hadamard else 0))
+             | (FP4_HADAMARD if hadamard else 0) | (FP4_SCALE_SEARCH if scale_search else 0))
     amax_t = None
     if amax is not None:
         amax_t = torch.as_tensor(amax, dtype=torch.float32, device=ac.device).reshape(-1).contiguous()

@@ -14,7 +14,8 @@ using namespace fp4impl;
 
 namespace {
 
-constexpr uint32_t kKnownFlags = FP4_FOUR_OVER_SIX | FP4_BLOCK2D | FP4_TRANSPOSE | FP4_STOCHASTIC | FP4_HADAMARD;
+constexpr uint32_t kKnownFlags =
+    FP4_FOUR_OVER_SIX | FP4_BLOCK2D | FP4_TRANSPOSE | FP4_STOCHASTIC | FP4_HADAMARD | FP4_SCALE_SEARCH;
 constexpr int64_t kMaxGridYZ = 65535;
 constexpr int64_t kMaxGridX = 2147483647;
 // fp4_gemm_grouped: every tile scans the group offsets 64 at a time
@@ -80,7 +81,7 @@ fp4_status plan_quantize(int64_t batch, int64_t rows, int64_t cols, const fp4_qu
   if (o->flags & ~kKnownFlags) return FP4_ERR_INVALID;
   if (batch < 0 || rows < 0 || cols < 0) return FP4_ERR_INVALID;
   const bool nv = o->format == FP4_NVFP4;
-  if (!nv && (o->flags & (FP4_FOUR_OVER_SIX | FP4_BLOCK2D))) return FP4_ERR_UNSUPPORTED;
+  if (!nv && (o->flags & (FP4_BLOCK2D | FP4_SCALE_SEARCH))) return FP4_ERR_UNSUPPORTED;
   if ((o->flags & FP4_BLOCK2D) && (o->flags & FP4_HADAMARD) && (o->flags & FP4_TRANSPOSE)) return FP4_ERR_UNSUPPORTED;
   const bool tr = o->flags & FP4_TRANSPOSE;
   p->blk = nv ? 16 : 32;
@@ -347,7 +348,7 @@ fp4_status fp4_gemm_quantize_output(int32_t format, int64_t groups, int64_t M, i
   if (out_opts->flags & ~kKnownFlags) return FP4_ERR_INVALID;
   const bool qnv = out_opts->format == FP4_NVFP4;
   if (out_opts->flags & (FP4_BLOCK2D | FP4_TRANSPOSE)) return FP4_ERR_UNSUPPORTED;
-  if (!qnv && (out_opts->flags & FP4_FOUR_OVER_SIX)) return FP4_ERR_UNSUPPORTED;
+  if (!qnv && (out_opts->flags & FP4_SCALE_SEARCH)) return FP4_ERR_UNSUPPORTED;
   if (groups < 0 || M < 0 || N < 0 || K < 0) return FP4_ERR_INVALID;
   const int64_t qblk = qnv ? 16 : 32;
   if (K % 64 != 0 || N % qblk != 0) return FP4_ERR_INVALID;
@@ -377,7 +378,7 @@ fp4_status fp4_gemm_quantize_output(int32_t format, int64_t groups, int64_t M, i
   g.q_ts = out_tensor_scale;
   g.q_amax = out_opts->amax_in;
   g.q_nv = qnv;
-  g.q_fos = (out_opts->flags & FP4_FOUR_OVER_SIX) != 0;
+  g.q_sel = (out_opts->flags & FP4_SCALE_SEARCH) ? 2 : (out_opts->flags & FP4_FOUR_OVER_SIX) ? 1 : 0;
   g.q_sr = (out_opts->flags & FP4_STOCHASTIC) != 0;
   g.q_rht = (out_opts->flags & FP4_HADAMARD) != 0;
   g.q_signs = out_opts->rht_signs;

@@ -402,7 +402,7 @@ __device__ __forceinline__ void store_staged_rows(const GemmArgs& g, const uint8
 // caller's amax of C exactly as fp4_quantize forms it, the candidate
 // multipliers, and no reciprocal table (a block divides instead).
 __device__ __forceinline__ float out_tensor_scale(const GemmArgs& g, int64_t grp) {
-  float St = g.q_amax[grp] / (g.q_fos ? 1792.0f : 2688.0f);
+  float St = g.q_amax[grp] / (g.q_sel ? 1792.0f : 2688.0f);
   if (!(St >= kFltMin && St <= 3.40282347e38f)) St = 1.0f;
   return St;
 }
@@ -440,18 +440,20 @@ __device__ __forceinline__ void store_staged_rows_q(const GemmArgs& g, const uin
     if (g.q_rht) rht16(v, g.q_signs);
     const uint64_t L0 = (uint64_t)((grp * g.M + m) * g.N + n);
     uint32_t w0, w1, sbyte;
-    if constexpr (QNV) {
-      if (g.q_fos) {
-        if (g.q_sr) quantize_unit<true, true, false, true, false>(v, nc, L0, g.q_seed, g.q_offset, w0, w1, sbyte);
-        else quantize_unit<true, true, false, false, false>(v, nc, L0, g.q_seed, g.q_offset, w0, w1, sbyte);
-      } else {
-        if (g.q_sr) quantize_unit<true, false, false, true, false>(v, nc, L0, g.q_seed, g.q_offset, w0, w1, sbyte);
-        else quantize_unit<true, false, false, false, false>(v, nc, L0, g.q_seed, g.q_offset, w0, w1, sbyte);
-      }
+#define G_QUNIT(SEL, SR) quantize_unit<QNV, SEL, false, SR, false>(v, nc, L0, g.q_seed, g.q_offset, w0, w1, sbyte)
+    if (g.q_sel == 0) {
+      if (g.q_sr) G_QUNIT(0, true);
+      else G_QUNIT(0, false);
+    } else if (g.q_sel == 1 || !QNV) {
+      if (g.q_sr) G_QUNIT(1, true);
+      else G_QUNIT(1, false);
     } else {
-      if (g.q_sr) quantize_unit<false, false, false, true, false>(v, nc, L0, g.q_seed, g.q_offset, w0, w1, sbyte);
-      else quantize_unit<false, false, false, false, false>(v, nc, L0, g.q_seed, g.q_offset, w0, w1, sbyte);
+      if constexpr (QNV) {
+        if (g.q_sr) G_QUNIT(2, true);
+        else G_QUNIT(2, false);
+      }
     }
+#undef G_QUNIT
     if (m < m_end && n < g.N) {
       *reinterpret_cast<uint2*>(g.qc + grp * g.qc_gs + m * g.ldqc + n / 2) = make_uint2(w0, w1);
       if constexpr (QNV) g.qs[grp * g.qs_gs + m * g.ldqs + n / 16] = (uint8_t)sbyte;

@@ -13,6 +13,7 @@ enum Flags : uint32_t {
   kTranspose = 4u,
   kStochastic = 8u,
   kHadamard = 16u,
+  kScaleSearch = 32u,
 };
 
 struct QuantArgs {
@@ -88,7 +89,8 @@ struct GemmArgs {
   int64_t ldqs, qs_gs;
   float* q_ts;
   const float* q_amax;
-  bool q_nv, q_fos, q_sr, q_rht;
+  bool q_nv, q_sr, q_rht;
+  int q_sel;  // scale selection: 0 plain, 1 4/6, 2 search (NVFP4)
   uint32_t q_signs;
   uint64_t q_seed, q_offset;
 };

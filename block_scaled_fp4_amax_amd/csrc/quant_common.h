@@ -10,6 +10,13 @@
 //   4/6    also try M = 4 and keep the candidate with the smaller squared
 //          error; the error of a 16-slice is eff^2 * (FMA chain over elements
 //          0..7 of (val - q)^2 + FMA chain over elements 8..15).
+// Scale selection modes (template parameter SEL):
+//   0  the plain scale;
+//   1  4/6: NVFP4 M = 6 or 4; MXFP4 exponent e or e + 1 (block max in
+//      [4, 8) or in [2, 4)), by the same squared error with the 4^e factor
+//      cancelled (e + 1 wins iff 4 S_{e+1} < S_e);
+//   2  NVFP4 scale search: every E4M3 code from the M = 6 candidate's to the
+//      M = 4 candidate's, smallest error wins, ties keep the smaller code.
 #pragma once
 
 #include "fp4_device.h"
@@ -84,6 +91,45 @@ __device__ __forceinline__ float sq_sum16(const float q[16], uint32_t w0, uint32
   return sq_chain8(q, w0) + sq_chain8(q + 8, w1);
 }
 
+// The NVFP4 candidate with E4M3 code `code`.
+template <bool TAB = true>
+__device__ __forceinline__ NvCand nv_code_candidate(uint32_t code, const NvConsts& nc) {
+  NvCand c;
+  c.code = code;
+  c.eff = e4m3_decode(code) * nc.St;
+  c.zero = !(c.eff >= kFltMin);
+  if constexpr (TAB) c.r = nc.rtab[code & 127u];
+  else c.r = c.zero ? 0.0f : 1.0f / c.eff;
+  return c;
+}
+
+// MXFP4 under 4/6: the exponent e (scale byte sbyte, shared by the lane pair
+// xor 1 that holds the 32-value block) or e + 1, by the squared error of the
+// nearest-even codes; returns the chosen byte and that exponent's codes of
+// this lane's 16 values. Both lanes of the pair call it together.
+__device__ __forceinline__ uint32_t mx_pair_choice(const float v[16], uint32_t sbyte, uint32_t& w0, uint32_t& w1) {
+  const int e = (int)sbyte - 127;
+  float q0[16];
+#pragma unroll
+  for (int i = 0; i < 16; i++) q0[i] = __builtin_ldexpf(v[i], -e);
+  pack16(q0, w0, w1);
+  if (e >= 127) return sbyte;  // e + 1 has no E8M0 byte
+  float q1[16];
+#pragma unroll
+  for (int i = 0; i < 16; i++) q1[i] = __builtin_ldexpf(v[i], -e - 1);
+  uint32_t x0, x1;
+  pack16(q1, x0, x1);
+  float s0 = sq_sum16(q0, w0, w1), s1 = sq_sum16(q1, x0, x1);
+  s0 = s0 + xor_shfl<1>(s0);
+  s1 = s1 + xor_shfl<1>(s1);
+  if (4.0f * s1 < s0) {
+    w0 = x0;
+    w1 = x1;
+    return sbyte + 1;
+  }
+  return sbyte;
+}
+
 // Candidate error eff^2 * partial sum; a zero block never wins.
 __device__ __forceinline__ float cand_error(const NvCand& c, float sum) {
   return c.zero ? kInf : (c.eff * c.eff) * sum;
@@ -119,19 +165,20 @@ __device__ __forceinline__ void sr16(const float q[16], uint64_t L0, uint64_t se
 // the scale byte. Lanes exchange data, so every lane of a wave calls this
 // together: MXFP4 units pair with the xor-1 lane into one 32-value block;
 // under B2D the 16 lanes xor 1..8 hold the 16 rows of one 16 x 16 tile.
-template <bool NV, bool FOS, bool B2D, bool SR, bool TAB = true>
+template <bool NV, int SEL, bool B2D, bool SR, bool TAB = true>
 __device__ __forceinline__ void quantize_unit(const float v[16], const NvConsts& nc, uint64_t L0, uint64_t seed,
                                               uint64_t offset, uint32_t& w0, uint32_t& w1, uint32_t& sbyte) {
   float amax = max_abs16(v);
   if constexpr (!NV) {
     amax = __builtin_fmaxf(amax, xor_shfl<1>(amax));
     sbyte = e8m0_from_amax(amax);
+    if constexpr (SEL == 1) sbyte = mx_pair_choice(v, sbyte, w0, w1);
     if constexpr (SR) {
       float q[16];
 #pragma unroll
       for (int i = 0; i < 16; i++) q[i] = __builtin_ldexpf(v[i], 127 - (int)sbyte);
       sr16(q, L0, seed, offset, w0, w1);
-    } else {
+    } else if constexpr (SEL == 0) {
       float sc = e8m0_scale_operand(sbyte);
       w0 = e2m1_pack2_scaled<0>(0u, v[0], v[1], sc);
       w0 = e2m1_pack2_scaled<1>(w0, v[2], v[3], sc);
@@ -154,7 +201,7 @@ __device__ __forceinline__ void quantize_unit(const float v[16], const NvConsts&
 #pragma unroll
     for (int i = 0; i < 16; i++) q[i] = v[i] * c.r;
     pack16(q, w0, w1);
-    if constexpr (FOS) {
+    if constexpr (SEL == 1) {
       NvCand c4 = nv_candidate<TAB>(amax, nc.k4, nc);
       float q4[16];
 #pragma unroll
@@ -176,6 +223,41 @@ __device__ __forceinline__ void quantize_unit(const float v[16], const NvConsts&
 #pragma unroll
         for (int i = 0; i < 16; i++) q[i] = q4[i];
       }
+    } else if constexpr (SEL == 2) {
+      float s6 = sq_sum16(q, w0, w1);
+      if constexpr (B2D) {
+        s6 = s6 + xor_shfl<1>(s6);
+        s6 = s6 + xor_shfl<2>(s6);
+        s6 = s6 + xor_shfl<4>(s6);
+        s6 = s6 + xor_shfl<8>(s6);
+      }
+      float best = cand_error(c, s6);
+      // under B2D the 16 lanes of a tile share amax, hence the loop bounds
+      const uint32_t hi = nv_candidate<TAB>(amax, nc.k4, nc).code;
+      for (uint32_t code = c.code + 1; code <= hi; code++) {
+        const NvCand cc = nv_code_candidate<TAB>(code, nc);
+        float qq[16];
+#pragma unroll
+        for (int i = 0; i < 16; i++) qq[i] = v[i] * cc.r;
+        uint32_t x0, x1;
+        pack16(qq, x0, x1);
+        float sc = sq_sum16(qq, x0, x1);
+        if constexpr (B2D) {
+          sc = sc + xor_shfl<1>(sc);
+          sc = sc + xor_shfl<2>(sc);
+          sc = sc + xor_shfl<4>(sc);
+          sc = sc + xor_shfl<8>(sc);
+        }
+        const float err = cand_error(cc, sc);
+        if (err < best) {
+          best = err;
+          c = cc;
+          w0 = x0;
+          w1 = x1;
+#pragma unroll
+          for (int i = 0; i < 16; i++) q[i] = qq[i];
+        }
+      }
     }
     if constexpr (SR) sr16(q, L0, seed, offset, w0, w1);
     sbyte = c.code;
@@ -184,8 +266,9 @@ __device__ __forceinline__ void quantize_unit(const float v[16], const NvConsts&
 
 // NVFP4 tensor scale for batch item b, computed identically by every
 // workgroup: T from amax_in or the max of the pre-pass partials; S_t = T / D
-// with D = 6 * 448 (4 * 448 under 4/6), replaced by 1 when zero, denormal or
-// not finite. The item's first workgroup (first) stores S_t.
+// with D = 6 * 448 (4 * 448 under 4/6 and the scale search: FOS), replaced
+// by 1 when zero, denormal or not finite. The item's first workgroup (first)
+// stores S_t.
 template <bool FOS>
 __device__ __forceinline__ float tensor_scale_prologue(const QuantArgs& a, int64_t b, bool first) {
   __shared__ float red[4];

@@ -144,7 +144,7 @@ struct Raw16<float> {
   }
 };
 
-template <typename TIn, bool NV, bool FOS, bool B2D, bool SR, bool RHT>
+template <typename TIn, bool NV, int SEL, bool B2D, bool SR, bool RHT>
 __global__ __launch_bounds__(256) void quant_rows_kernel(QuantArgs a) {
   const int64_t b = blockIdx.z;
   const int64_t upr = a.C >> 4;  // 16-value units per row
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(QuantArgs a) {
   if (valid) raw.load(reinterpret_cast<const TIn*>(a.x) + b * a.bs_x + row * a.ld_x + cu * 16);
 
   NvConsts nc{};
-  if constexpr (NV) nc = nv_prologue<FOS>(a, b, blockIdx.x == 0 && blockIdx.y == 0);  // every lane takes part
+  if constexpr (NV) nc = nv_prologue<SEL != 0>(a, b, blockIdx.x == 0 && blockIdx.y == 0);  // every lane takes part
   if (!valid) return;
 
   float v[16];
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(QuantArgs a) {
 
   uint32_t w0, w1, sbyte;
   const uint64_t L0 = ((uint64_t)b * (uint64_t)a.R + (uint64_t)row) * (uint64_t)a.C + (uint64_t)cu * 16;
-  quantize_unit<NV, FOS, B2D, SR>(v, nc, L0, a.seed, a.offset, w0, w1, sbyte);
+  quantize_unit<NV, SEL, B2D, SR>(v, nc, L0, a.seed, a.offset, w0, w1, sbyte);
 
   uint8_t* cp = a.codes + b * a.bs_c + row * a.ld_c + cu * 8;
   *reinterpret_cast<uint2*>(cp) = make_uint2(w0, w1);
@@ -227,7 +227,7 @@ struct Patch16x8<float> {
   }
 };
 
-template <typename TIn, bool NV, bool FOS, bool B2D, bool SR, bool RHT>
+template <typename TIn, bool NV, int SEL, bool B2D, bool SR, bool RHT>
 __global__ __launch_bounds__(256) void quant_cols_kernel(QuantArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t cst[kColsN * kColsPitch];
   __shared__ __attribute__((aligned(16))) uint8_t sst[kColsN * kColsScales];
@@ -255,7 +255,7 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(QuantArgs a) {
   Patch16x8<TIn> t;
   if (valid) t.load(reinterpret_cast<const TIn*>(a.x) + b * a.bs_x + k0 * a.ld_x + n0, a.ld_x);
   NvConsts nc{};
-  if constexpr (NV) nc = nv_prologue<FOS>(a, b, nb == 0 && kb == 0);  // while the loads are in flight
+  if constexpr (NV) nc = nv_prologue<SEL != 0>(a, b, nb == 0 && kb == 0);  // while the loads are in flight
   if (valid) {
     const uint64_t Lrow = (uint64_t)b * (uint64_t)a.R;
     uint8_t* crow = cst + nl * kColsPitch + (kl >> 1);
@@ -270,41 +270,45 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(QuantArgs a) {
         for (int j = 0; j < 8; j++) amax = __builtin_fmaxf(amax, __builtin_fabsf(t.get(i, j)));
       amax = __builtin_fmaxf(amax, xor_shfl<2>(amax));
       NvCand c = nv_candidate(amax, nc.k6, nc);
-      if constexpr (FOS) {
-        NvCand c4 = nv_candidate(amax, nc.k4, nc);
-        // per source row: FMA chain over this lane's 8 columns, plus the
-        // partner's chain over the other 8 columns; then a pairwise tree over
-        // the 16 source rows
-        float p6[16], p4[16];
+      // a candidate's error sum: per source row, the FMA chain over this
+      // lane's 8 columns plus the partner's over the other 8, then a
+      // pairwise tree over the 16 source rows
+      auto tile_sum = [&](const NvCand& cc) {
+        float p[16];
 #pragma unroll
         for (int i = 0; i < 16; i++) {
-          float q6[8], q4[8];
+          float qq[8];
 #pragma unroll
-          for (int j = 0; j < 8; j++) {
-            q6[j] = t.get(i, j) * c.r;
-            q4[j] = t.get(i, j) * c4.r;
-          }
-          uint32_t w6 = e2m1_pack2<0>(0u, q6[0], q6[1]);
-          w6 = e2m1_pack2<1>(w6, q6[2], q6[3]);
-          w6 = e2m1_pack2<2>(w6, q6[4], q6[5]);
-          w6 = e2m1_pack2<3>(w6, q6[6], q6[7]);
-          uint32_t w4 = e2m1_pack2<0>(0u, q4[0], q4[1]);
-          w4 = e2m1_pack2<1>(w4, q4[2], q4[3]);
-          w4 = e2m1_pack2<2>(w4, q4[4], q4[5]);
-          w4 = e2m1_pack2<3>(w4, q4[6], q4[7]);
-          p6[i] = sq_chain8(q6, w6);
-          p4[i] = sq_chain8(q4, w4);
-          p6[i] = p6[i] + xor_shfl<2>(p6[i]);
-          p4[i] = p4[i] + xor_shfl<2>(p4[i]);
+          for (int j = 0; j < 8; j++) qq[j] = t.get(i, j) * cc.r;
+          uint32_t ww = e2m1_pack2<0>(0u, qq[0], qq[1]);
+          ww = e2m1_pack2<1>(ww, qq[2], qq[3]);
+          ww = e2m1_pack2<2>(ww, qq[4], qq[5]);
+          ww = e2m1_pack2<3>(ww, qq[6], qq[7]);
+          p[i] = sq_chain8(qq, ww);
+          p[i] = p[i] + xor_shfl<2>(p[i]);
         }
 #pragma unroll
         for (int width = 1; width < 16; width <<= 1)
 #pragma unroll
-          for (int i = 0; i < 16; i += 2 * width) {
-            p6[i] = p6[i] + p6[i + width];
-            p4[i] = p4[i] + p4[i + width];
+          for (int i = 0; i < 16; i += 2 * width) p[i] = p[i] + p[i + width];
+        return p[0];
+      };
+      if constexpr (SEL == 1) {
+        NvCand c4 = nv_candidate(amax, nc.k4, nc);
+        const float s6 = tile_sum(c), s4 = tile_sum(c4);
+        if (cand_error(c4, s4) < cand_error(c, s6)) c = c4;
+      } else if constexpr (SEL == 2) {
+        // the lane pair shares amax, hence the loop bounds
+        float best = cand_error(c, tile_sum(c));
+        const uint32_t hi = nv_candidate(amax, nc.k4, nc).code;
+        for (uint32_t code = c.code + 1; code <= hi; code++) {
+          const NvCand cc = nv_code_candidate(code, nc);
+          const float err = cand_error(cc, tile_sum(cc));
+          if (err < best) {
+            best = err;
+            c = cc;
           }
-        if (cand_error(c4, p4[0]) < cand_error(c, p6[0])) c = c4;
+        }
       }
 #pragma unroll
       for (int j = 0; j < 8; j++) {
@@ -326,53 +330,12 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(QuantArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; i++) v[i] = t.get(i, j);
         if constexpr (RHT) rht16(v, a.signs);
-        float amax = max_abs16(v);
         const uint64_t L0 = (Lrow + (uint64_t)(n0 + j)) * (uint64_t)a.C + (uint64_t)k0;
-        uint32_t w0, w1;
-        if constexpr (!NV) {
-          amax = __builtin_fmaxf(amax, xor_shfl<1>(amax));  // vertical lane pair = 32 rows
-          const uint32_t sbyte = e8m0_from_amax(amax);
-          if constexpr (SR) {
-            float q[16];
-#pragma unroll
-            for (int i = 0; i < 16; i++) q[i] = __builtin_ldexpf(v[i], 127 - (int)sbyte);
-            sr16(q, L0, a.seed, a.offset, w0, w1);
-          } else {
-            const float sc = e8m0_scale_operand(sbyte);
-            w0 = e2m1_pack2_scaled<0>(0u, v[0], v[1], sc);
-            w0 = e2m1_pack2_scaled<1>(w0, v[2], v[3], sc);
-            w0 = e2m1_pack2_scaled<2>(w0, v[4], v[5], sc);
-            w0 = e2m1_pack2_scaled<3>(w0, v[6], v[7], sc);
-            w1 = e2m1_pack2_scaled<0>(0u, v[8], v[9], sc);
-            w1 = e2m1_pack2_scaled<1>(w1, v[10], v[11], sc);
-            w1 = e2m1_pack2_scaled<2>(w1, v[12], v[13], sc);
-            w1 = e2m1_pack2_scaled<3>(w1, v[14], v[15], sc);
-          }
-          if (h == 0) srow[j * kColsScales + (kl >> 5)] = (uint8_t)sbyte;
-        } else {
-          NvCand c = nv_candidate(amax, nc.k6, nc);
-          float q[16];
-#pragma unroll
-          for (int i = 0; i < 16; i++) q[i] = v[i] * c.r;
-          pack16(q, w0, w1);
-          if constexpr (FOS) {
-            NvCand c4 = nv_candidate(amax, nc.k4, nc);
-            float q4[16];
-#pragma unroll
-            for (int i = 0; i < 16; i++) q4[i] = v[i] * c4.r;
-            uint32_t x0, x1;
-            pack16(q4, x0, x1);
-            if (cand_error(c4, sq_sum16(q4, x0, x1)) < cand_error(c, sq_sum16(q, w0, w1))) {
-              c = c4;
-              w0 = x0;
-              w1 = x1;
-#pragma unroll
-              for (int i = 0; i < 16; i++) q[i] = q4[i];
-            }
-          }
-          if constexpr (SR) sr16(q, L0, a.seed, a.offset, w0, w1);
-          srow[j * kColsScales + (kl >> 4)] = (uint8_t)c.code;
-        }
+        uint32_t w0, w1, sbyte;
+        // an MXFP4 block is the vertical lane pair (lanes xor 1, 32 rows)
+        quantize_unit<NV, SEL, false, SR>(v, nc, L0, a.seed, a.offset, w0, w1, sbyte);
+        if constexpr (NV) srow[j * kColsScales + (kl >> 4)] = (uint8_t)sbyte;
+        else if (h == 0) srow[j * kColsScales + (kl >> 5)] = (uint8_t)sbyte;
         *reinterpret_cast<uint2*>(crow + j * kColsPitch) = make_uint2(w0, w1);
       }
     }
@@ -402,7 +365,7 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(QuantArgs a) {
 // ------------------------------------------------------------------------
 // dispatch
 // ------------------------------------------------------------------------
-template <typename TIn, bool NV, bool FOS, bool B2D, bool SR, bool RHT>
+template <typename TIn, bool NV, int SEL, bool B2D, bool SR, bool RHT>
 static void launch_one(const QuantArgs& a, hipStream_t s) {
   if (a.flags & kTranspose) {
     if constexpr (B2D && RHT) {
@@ -412,34 +375,41 @@ static void launch_one(const QuantArgs& a, hipStream_t s) {
       const int64_t strips = a.batch * ((a.src_cols + kColsN - 1) / kColsN);
       const int64_t nkb = (a.src_rows + kColsK - 1) / kColsK;
       dim3 grid((unsigned)(8 * ((strips + 7) / 8) * nkb));
-      hipLaunchKernelGGL((quant_cols_kernel<TIn, NV, FOS, B2D, SR, RHT>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((quant_cols_kernel<TIn, NV, SEL, B2D, SR, RHT>), grid, dim3(256), 0, s, a);
     }
   } else if (B2D) {
     dim3 grid((unsigned)(((a.C >> 4) + 15) / 16), (unsigned)(a.R / 16), (unsigned)a.batch);
-    hipLaunchKernelGGL((quant_rows_kernel<TIn, NV, FOS, B2D, SR, RHT>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((quant_rows_kernel<TIn, NV, SEL, B2D, SR, RHT>), grid, dim3(256), 0, s, a);
   } else {
     int64_t units = a.R * (a.C >> 4);
     dim3 grid((unsigned)((units + 255) / 256), 1, (unsigned)a.batch);
-    hipLaunchKernelGGL((quant_rows_kernel<TIn, NV, FOS, B2D, SR, RHT>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((quant_rows_kernel<TIn, NV, SEL, B2D, SR, RHT>), grid, dim3(256), 0, s, a);
   }
 }
 
-template <typename TIn, bool NV, bool FOS, bool B2D>
+template <typename TIn, bool NV, int SEL, bool B2D>
 static void launch_sr_rht(const QuantArgs& a, hipStream_t s) {
   const bool sr = a.flags & kStochastic, rht = a.flags & kHadamard;
   if (sr) {
-    if (rht) launch_one<TIn, NV, FOS, B2D, true, true>(a, s);
-    else launch_one<TIn, NV, FOS, B2D, true, false>(a, s);
+    if (rht) launch_one<TIn, NV, SEL, B2D, true, true>(a, s);
+    else launch_one<TIn, NV, SEL, B2D, true, false>(a, s);
   } else {
-    if (rht) launch_one<TIn, NV, FOS, B2D, false, true>(a, s);
-    else launch_one<TIn, NV, FOS, B2D, false, false>(a, s);
+    if (rht) launch_one<TIn, NV, SEL, B2D, false, true>(a, s);
+    else launch_one<TIn, NV, SEL, B2D, false, false>(a, s);
   }
+}
+
+template <typename TIn, int SEL>
+static void launch_nv_sel(const QuantArgs& a, hipStream_t s) {
+  if (a.flags & kBlock2D) launch_sr_rht<TIn, true, SEL, true>(a, s);
+  else launch_sr_rht<TIn, true, SEL, false>(a, s);
 }
 
 template <typename TIn>
 static void launch_typed(const QuantArgs& a, hipStream_t s) {
   if (!a.nvfp4) {
-    launch_sr_rht<TIn, false, false, false>(a, s);
+    if (a.flags & kFourOverSix) launch_sr_rht<TIn, false, 1, false>(a, s);
+    else launch_sr_rht<TIn, false, 0, false>(a, s);
     return;
   }
   if (!a.amax_in) {
@@ -449,14 +419,9 @@ static void launch_typed(const QuantArgs& a, hipStream_t s) {
     else if (mode == kAmaxRhtRows) hipLaunchKernelGGL((amax_kernel<TIn, kAmaxRhtRows>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((amax_kernel<TIn, kAmaxRhtCols>), grid, dim3(256), 0, s, a);
   }
-  const bool fos = a.flags & kFourOverSix, b2d = a.flags & kBlock2D;
-  if (fos) {
-    if (b2d) launch_sr_rht<TIn, true, true, true>(a, s);
-    else launch_sr_rht<TIn, true, true, false>(a, s);
-  } else {
-    if (b2d) launch_sr_rht<TIn, true, false, true>(a, s);
-    else launch_sr_rht<TIn, true, false, false>(a, s);
-  }
+  if (a.flags & kScaleSearch) launch_nv_sel<TIn, 2>(a, s);
+  else if (a.flags & kFourOverSix) launch_nv_sel<TIn, 1>(a, s);
+  else launch_nv_sel<TIn, 0>(a, s);
 }
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {

@@ -64,9 +64,12 @@ typedef enum { FP4_F32 = 0, FP4_BF16 = 1 } fp4_dtype;
 
 /* fp4_quant_opts.flags */
 enum {
-  /* NVFP4 only. Each block is scaled so its max maps to 4 and to 6; the
+  /* NVFP4: each block is scaled so its max maps to 4 and to 6; the
    * candidate with the smaller sum of squared errors is kept (ties keep 6).
-   * ("Four Over Six", introduction.) */
+   * ("Four Over Six", introduction.) MXFP4: the same choice between the
+   * power-of-two scales that put the block max in [4, 8) (the standard
+   * exponent e, values above 6 clip) and in [2, 4) (e + 1); e + 1 is kept
+   * iff its squared error is smaller. */
   FP4_FOUR_OVER_SIX = 1u,
   /* NVFP4 only. One scale per 16x16 tile instead of per 1x16 row slice.
    * ("Four Over Six", option list: 2D block scaling.) */
@@ -83,7 +86,14 @@ enum {
    * before quantization: sign flip by rht_signs, 16-point Walsh-Hadamard,
    * times 1/4. The same signs applied to both GEMM operands cancel in the
    * product. ("FP4", "Inferencia e Treinamento FP4"; "Four Over Six".) */
-  FP4_HADAMARD = 16u
+  FP4_HADAMARD = 16u,
+  /* NVFP4 only. The 4/6 choice widened to every E4M3 scale code from the
+   * M = 6 candidate's to the M = 4 candidate's: the block max may map to
+   * any representable point between 6 and 4; the smallest squared error
+   * wins, ties keep the smaller code. Tensor scale as under 4/6 (D = 4 *
+   * 448); takes precedence over FP4_FOUR_OVER_SIX. (The pages' theme of
+   * choosing the scale by error, "Four Over Six", introduction.) */
+  FP4_SCALE_SEARCH = 32u
 };
 
 typedef struct fp4_quant_opts {
@@ -127,11 +137,12 @@ size_t fp4_quantize_workspace(int64_t batch, int64_t rows, int64_t cols, const f
  * Shape rules (else FP4_ERR_INVALID): C % blk == 0; under FP4_TRANSPOSE the
  * source column count (= R) is a multiple of 8; under FP4_BLOCK2D also
  * R % 16 == 0.
- * FP4_FOUR_OVER_SIX or FP4_BLOCK2D with MXFP4 -> FP4_ERR_UNSUPPORTED.
+ * FP4_BLOCK2D or FP4_SCALE_SEARCH with MXFP4 -> FP4_ERR_UNSUPPORTED.
  *
  * NVFP4 tensor scale: T = max |x| over the batch item (after the Hadamard
  * transform, if on) or amax_in[b]; S_t = T / (6 * 448), or T / (4 * 448)
- * under FP4_FOUR_OVER_SIX; S_t = 1 when that is zero, denormal or not finite.
+ * under FP4_FOUR_OVER_SIX or FP4_SCALE_SEARCH; S_t = 1 when that is zero,
+ * denormal or not finite.
  */
 fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t batch, int64_t rows, int64_t cols,
                         int64_t ld_x, int64_t batch_stride_x, const fp4_quant_opts* opts,
@@ -202,7 +213,8 @@ fp4_status fp4_gemm(int32_t format, int64_t groups, int64_t M, int64_t N, int64_
  * tensor scales), is quantized along its rows exactly as fp4_quantize
  * quantizes a row-major [M, N] fp32 matrix with out_opts:
  *   out_opts     format MXFP4 or NVFP4 (either, whatever the operands'
- *                format); flags FP4_FOUR_OVER_SIX (NVFP4), FP4_STOCHASTIC
+ *                format); flags FP4_FOUR_OVER_SIX, FP4_SCALE_SEARCH
+ *                (NVFP4), FP4_STOCHASTIC
  *                (index of element (m, n) of group g: (g M + m) N + n, as in
  *                a batched fp4_quantize), FP4_HADAMARD; FP4_BLOCK2D and
  *                FP4_TRANSPOSE -> FP4_ERR_UNSUPPORTED. NVFP4 needs amax_in:

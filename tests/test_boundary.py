@@ -59,7 +59,7 @@ def test_quantize_option_errors(fp4):
     assert q(fp4, bad) == fp4.FP4_ERR_INVALID
     assert q(fp4, fp4.make_opts(7)) == fp4.FP4_ERR_INVALID
     assert q(fp4, fp4.make_opts(fp4.FP4_NVFP4, flags=64)) == fp4.FP4_ERR_INVALID
-    assert q(fp4, fp4.make_opts(fp4.FP4_MXFP4, flags=fp4.FP4_FOUR_OVER_SIX)) == fp4.FP4_ERR_UNSUPPORTED
+    assert q(fp4, fp4.make_opts(fp4.FP4_MXFP4, flags=fp4.FP4_SCALE_SEARCH)) == fp4.FP4_ERR_UNSUPPORTED
     assert q(fp4, fp4.make_opts(fp4.FP4_MXFP4, flags=fp4.FP4_BLOCK2D)) == fp4.FP4_ERR_UNSUPPORTED
     f = fp4.FP4_BLOCK2D | fp4.FP4_HADAMARD | fp4.FP4_TRANSPOSE
     assert q(fp4, fp4.make_opts(fp4.FP4_NVFP4, flags=f)) == fp4.FP4_ERR_UNSUPPORTED
@@ -178,6 +178,64 @@ def test_gemm_errors(fp4):
 def test_valid_gemm_without_gfx950_reports_device(fp4):
     assert g(fp4) == fp4.FP4_ERR_DEVICE
     assert g(fp4, fmt=1) == fp4.FP4_ERR_DEVICE
+
+
+def gq(fp4, opts, N=64, oc=FAKE, ldoc=32, os_=FAKE, ldos=16, ots=FAKE, groups=1, ocgs=0, osgs=0, **kw):
+    """fp4_gemm_quantize_output with the operand arguments of g()."""
+    a = dict(fmt=0, M=64, K=128, a=FAKE, lda=64, ags=0, asc=FAKE, ldas=16, asgs=0, ats=FAKE, b=FAKE, ldb=64, bgs=0,
+             bsc=FAKE, ldbs=16, bsgs=0, bts=FAKE)
+    a.update(kw)
+    return fp4.fp4_gemm_quantize_output(a["fmt"], groups, a["M"], N, a["K"], a["a"], a["lda"], a["ags"], a["asc"],
+                                        a["ldas"], a["asgs"], a["ats"], a["b"], a["ldb"], a["bgs"], a["bsc"],
+                                        a["ldbs"], a["bsgs"], a["bts"], opts, oc, ldoc, ocgs, os_, ldos, osgs, ots,
+                                        None)
+
+
+def test_gemm_quantize_output_errors(fp4):
+    mx = fp4.make_opts(fp4.FP4_MXFP4)
+    nv_amax = fp4.make_opts(fp4.FP4_NVFP4, amax_in=FAKE)
+    assert gq(fp4, fp4.make_opts(fp4.FP4_NVFP4)) == fp4.FP4_ERR_INVALID            # NVFP4 output needs amax_in
+    assert gq(fp4, nv_amax, ots=0) == fp4.FP4_ERR_INVALID                          # and a tensor-scale output
+    assert gq(fp4, mx, N=48, ldoc=24) == fp4.FP4_ERR_INVALID                       # N % 32
+    assert gq(fp4, mx, ldoc=16) == fp4.FP4_ERR_INVALID                             # pitch < N / 2
+    assert gq(fp4, mx, oc=FAKE + 4) == fp4.FP4_ERR_ALIGN
+    assert gq(fp4, mx, ldoc=36) == fp4.FP4_ERR_ALIGN
+    for f in (fp4.FP4_BLOCK2D, fp4.FP4_TRANSPOSE):
+        assert gq(fp4, fp4.make_opts(fp4.FP4_NVFP4, flags=f, amax_in=FAKE)) == fp4.FP4_ERR_UNSUPPORTED
+    assert gq(fp4, fp4.make_opts(fp4.FP4_MXFP4, flags=fp4.FP4_SCALE_SEARCH)) == fp4.FP4_ERR_UNSUPPORTED
+    assert gq(fp4, fp4.make_opts(fp4.FP4_NVFP4, flags=64, amax_in=FAKE)) == fp4.FP4_ERR_INVALID
+    assert gq(fp4, mx, fmt=3) == fp4.FP4_ERR_INVALID                               # operand format
+    assert gq(fp4, mx, M=0) == fp4.FP4_OK
+
+
+@cpu_only
+def test_valid_gemm_quantize_output_without_gfx950_reports_device(fp4):
+    assert gq(fp4, fp4.make_opts(fp4.FP4_MXFP4, flags=fp4.FP4_FOUR_OVER_SIX)) == fp4.FP4_ERR_DEVICE
+    assert gq(fp4, fp4.make_opts(fp4.FP4_NVFP4, flags=fp4.FP4_SCALE_SEARCH, amax_in=FAKE), fmt=1) == \
+        fp4.FP4_ERR_DEVICE
+
+
+def gg(fp4, groups=2, offs=FAKE, M=64, N=64, K=128, a=FAKE, lda=64, asc=FAKE, ldas=16, ats=FAKE, b=FAKE, ldb=64,
+       bgs=4096, bsc=FAKE, ldbs=16, bsgs=1024, bts=FAKE, c=FAKE, ct=0, ldc=64, fmt=0):
+    return fp4.fp4_gemm_grouped(fmt, groups, offs, M, N, K, a, lda, asc, ldas, ats, b, ldb, bgs, bsc, ldbs, bsgs,
+                                bts, c, ct, ldc, None)
+
+
+def test_gemm_grouped_errors(fp4):
+    assert gg(fp4, offs=0) == fp4.FP4_ERR_INVALID
+    assert gg(fp4, offs=FAKE + 2) == fp4.FP4_ERR_ALIGN
+    assert gg(fp4, groups=5000) == fp4.FP4_ERR_UNSUPPORTED
+    assert gg(fp4, K=96, lda=48, ldb=48, ldas=3, ldbs=3) == fp4.FP4_ERR_INVALID
+    assert gg(fp4, ldc=32) == fp4.FP4_ERR_INVALID
+    assert gg(fp4, fmt=1, ats=0) == fp4.FP4_ERR_INVALID
+    assert gg(fp4, bgs=4104) == fp4.FP4_ERR_ALIGN
+    assert gg(fp4, groups=0, offs=0) == fp4.FP4_OK
+    assert gg(fp4, M=0) == fp4.FP4_OK
+
+
+@cpu_only
+def test_valid_gemm_grouped_without_gfx950_reports_device(fp4):
+    assert gg(fp4) == fp4.FP4_ERR_DEVICE
 
 
 def test_product_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -23,14 +23,15 @@ from gpu_util import assert_codes_equal, flag_str, oracle_operand, oracle_quanti
 pytestmark = pytest.mark.gpu
 
 MX, NV = 0, 1
-FOS, SR, RHT = 1, 8, 16
+FOS, SR, RHT, SEARCH = 1, 8, 16, 32
 SIGNS = 0xA5C3
 SEED, OFFSET = 21, 5
 
 # (operand format, operand flags, output format, output flags)
 CASES = [(MX, 0, MX, 0), (MX, 0, MX, SR), (MX, 0, MX, RHT), (NV, FOS, MX, SR | RHT),
          (NV, 0, NV, 0), (NV, FOS, NV, FOS), (NV, FOS, NV, SR), (NV, FOS, NV, FOS | SR),
-         (MX, 0, NV, FOS | RHT), (NV, FOS, NV, FOS | SR | RHT)]
+         (MX, 0, NV, FOS | RHT), (NV, FOS, NV, FOS | SR | RHT), (MX, 0, MX, FOS), (NV, FOS, MX, FOS | SR),
+         (NV, FOS, NV, SEARCH), (MX, 0, NV, SEARCH | SR | RHT)]
 IDS = [f"{'nv' if a == NV else 'mx'}-{flag_str(fa)}->{'nv' if o == NV else 'mx'}-{flag_str(fo)}"
        for a, fa, o, fo in CASES]
 
@@ -62,8 +63,8 @@ def lsb_exponent(v):
 
 def run_fused(qa, qb, fo_fmt, fo, amax):
     return F.gemm_quantize_output(qa, qb, "nvfp4" if fo_fmt == NV else "mxfp4", four_over_six=bool(fo & FOS),
-                                  stochastic=bool(fo & SR), hadamard=bool(fo & RHT), rht_signs=SIGNS, seed=SEED,
-                                  offset=OFFSET, amax=amax)
+                                  stochastic=bool(fo & SR), hadamard=bool(fo & RHT), scale_search=bool(fo & SEARCH),
+                                  rht_signs=SIGNS, seed=SEED, offset=OFFSET, amax=amax)
 
 
 def compare(got, codes, scales, ts, fo_fmt, what):
@@ -123,8 +124,8 @@ def test_matches_unfused_path(oracle, fa_fmt, fa, fo_fmt, fo):
     c = F.gemm(qa, qb, torch.float32)
     amax = c.abs().reshape(2, -1).amax(dim=1) if fo_fmt == NV else None
     ref = F.quantize(c, "nvfp4" if fo_fmt == NV else "mxfp4", four_over_six=bool(fo & FOS),
-                     stochastic=bool(fo & SR), hadamard=bool(fo & RHT), rht_signs=SIGNS, seed=SEED, offset=OFFSET,
-                     amax=amax)
+                     stochastic=bool(fo & SR), hadamard=bool(fo & RHT), scale_search=bool(fo & SEARCH),
+                     rht_signs=SIGNS, seed=SEED, offset=OFFSET, amax=amax)
     got = run_fused(qa, qb, fo_fmt, fo, amax)
     torch.cuda.synchronize()
     compare(got, ref.codes.cpu().numpy(), ref.scales.cpu().numpy(),

@@ -12,16 +12,20 @@ from gpu_util import (assert_codes_equal, flag_str, gpu_quantize, mixed_matrix, 
 pytestmark = pytest.mark.gpu
 
 MX, NV = 0, 1
-FOS, B2D, TR, SR, RHT = 1, 2, 4, 8, 16
+FOS, B2D, TR, SR, RHT, SEARCH = 1, 2, 4, 8, 16, 32
 
 
 def valid_combos():
+    """Every flag set the API accepts: MXFP4 without 2D or the scale search;
+    NVFP4 without 2D + Hadamard + transpose; the search in place of 4/6."""
     out = []
     for f in range(32):
-        if f & (FOS | B2D) == 0:
+        if f & B2D == 0:
             out.append((MX, f))
         if not (f & B2D and f & RHT and f & TR):
             out.append((NV, f))
+            if f & FOS == 0:
+                out.append((NV, f | SEARCH))
     return out
 
 
