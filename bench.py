@@ -247,10 +247,12 @@ def wl_moe(F, inputs):
 def wl_training(F, inputs):
     d = inputs.training(device="cuda")
     n = n_sets(d["w"].numel() * 4)
-    ws, gs = copies(d["w"], n), copies(d["grad"], n)
+    # W and W^T read their own copies: a second read of the same tensor right
+    # after the first would be served from the 256 MB Infinity Cache
+    ws, ws2, gs = copies(d["w"], n), copies(d["w"], n), copies(d["grad"], n)
     f = F.FP4_FOUR_OVER_SIX | F.FP4_BLOCK2D
     q1 = QuantCall(F, ws, F.FP4_NVFP4, f)
-    q2 = QuantCall(F, ws, F.FP4_NVFP4, f | F.FP4_TRANSPOSE)
+    q2 = QuantCall(F, ws2, F.FP4_NVFP4, f | F.FP4_TRANSPOSE)
     q3 = QuantCall(F, gs, F.FP4_NVFP4, F.FP4_FOUR_OVER_SIX | F.FP4_STOCHASTIC, seed=d["sr_seed"])
     ops = [Op("quantize W nvfp4 2D 4/6", "quant_rows_kernel", "hbm", q1.bytes(), PEAK_HBM_GBS, q1, "GB/s"),
            Op("quantize W^T nvfp4 2D 4/6", "quant_cols_kernel", "hbm", q2.bytes(), PEAK_HBM_GBS, q2, "GB/s"),
@@ -282,12 +284,13 @@ def wl_training_backward(F, inputs):
     Philox offset for each of the two quantizations of dY)."""
     d = inputs.training_backward(device="cuda")
     n = n_sets(d["w"].numel() * 2 + d["grad"].numel() * 2 + d["x"].numel() * 2)
-    gs, ws, xs = copies(d["grad"], n), copies(d["w"], n), copies(d["x"], n)
+    # the two quantizations of dY read separate copies (no cache-served re-read)
+    gs, gs2, ws, xs = copies(d["grad"], n), copies(d["grad"], n), copies(d["w"], n), copies(d["x"], n)
     fos, sr, tr = F.FP4_FOUR_OVER_SIX, F.FP4_STOCHASTIC, F.FP4_TRANSPOSE
     qg = QuantCall(F, gs, F.FP4_NVFP4, fos | sr, seed=d["sr_seed"], offset=0)
     qwt = QuantCall(F, ws, F.FP4_NVFP4, fos | F.FP4_BLOCK2D | tr)
     gd = GemmCall(F, qg, qwt, torch.bfloat16)
-    qgt = QuantCall(F, gs, F.FP4_NVFP4, fos | sr | tr, seed=d["sr_seed"], offset=1 << 40)
+    qgt = QuantCall(F, gs2, F.FP4_NVFP4, fos | sr | tr, seed=d["sr_seed"], offset=1 << 40)
     qxt = QuantCall(F, xs, F.FP4_NVFP4, fos | tr)
     gw = GemmCall(F, qgt, qxt, torch.bfloat16)
     ops = [Op("quantize dY nvfp4 4/6 stochastic", "quant_rows_kernel", "hbm", qg.bytes(), PEAK_HBM_GBS, qg, "GB/s"),
@@ -365,10 +368,10 @@ def wl_scale_search(F, inputs):
     candidates, 1D and 2D, and MXFP4 with the 4/6 exponent pair."""
     d = inputs.training(device="cuda")
     n = n_sets(d["w"].numel() * 2)
-    ws = copies(d["w"], n)
-    qs = QuantCall(F, ws, F.FP4_NVFP4, F.FP4_SCALE_SEARCH)
-    q2 = QuantCall(F, ws, F.FP4_NVFP4, F.FP4_SCALE_SEARCH | F.FP4_BLOCK2D)
-    qm = QuantCall(F, ws, F.FP4_MXFP4, F.FP4_FOUR_OVER_SIX)
+    # one set of copies per op, so no op reads what the previous one just read
+    qs = QuantCall(F, copies(d["w"], n), F.FP4_NVFP4, F.FP4_SCALE_SEARCH)
+    q2 = QuantCall(F, copies(d["w"], n), F.FP4_NVFP4, F.FP4_SCALE_SEARCH | F.FP4_BLOCK2D)
+    qm = QuantCall(F, copies(d["w"], n), F.FP4_MXFP4, F.FP4_FOUR_OVER_SIX)
     ops = [Op("quantize W nvfp4 scale search (amax pre-pass + quantize)", "amax_kernel+quant_rows_kernel", "hbm",
               qs.bytes(), PEAK_HBM_GBS, qs, "GB/s"),
            Op("quantize W nvfp4 2D scale search (amax pre-pass + quantize)", "amax_kernel+quant_rows_kernel", "hbm",
