@@ -310,6 +310,11 @@ __device__ __forceinline__ f16x8 nv_dequant8(uint32_t w, const NvScale& s) {
   return f16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
+// The dword of a lane's 16-byte fragment that sub-step kt (0..3) reads.
+__device__ __forceinline__ uint32_t nv_word(const uint4& c, int kt) {
+  return kt == 0 ? c.x : kt == 1 ? c.y : kt == 2 ? c.z : c.w;
+}
+
 }  // namespace
 
 // Output staging. A wave's 128 x WN block of C goes, in fp32, to its own
@@ -629,36 +634,45 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_fp4_kernel(GemmArgs g) {
         }                                                                               \
       }                                                                                 \
     } else {                                                                            \
+      /* software-pipelined: sub-step kt's MFMAs run while the fp16 fragments \
+         of kt + 1 are dequantized, one fragment after each MFMA */         \
       constexpr int nm_ = 16 * NJ;                                                      \
       uint32_t pa_[4], pb_[NJ];                                                         \
       _Pragma("unroll") for (int i = 0; i < 4; i++) pa_[i] = SA[i][(KB) & (NV ? 1 : 0)] >> (16 * h); \
       _Pragma("unroll") for (int j = 0; j < NJ; j++) pb_[j] = SB[j][(KB) & (NV ? 1 : 0)] >> (16 * h); \
       NvScale na[4], nb[NJ];                                                            \
-      _Pragma("unroll") for (int kt = (P0) & ~1; kt < (P1); kt++) {                     \
-        if ((kt & 1) == 0) {                                                            \
-          _Pragma("unroll") for (int i = 0; i < 4; i++)                                 \
-            na[i] = nv_scale(kt == 0 ? (pa_[i] & 0xffu) : ((pa_[i] >> 8) & 0xffu));     \
-          _Pragma("unroll") for (int j = 0; j < NJ; j++)                                \
-            nb[j] = nv_scale(kt == 0 ? (pb_[j] & 0xffu) : ((pb_[j] >> 8) & 0xffu));     \
-        }                                                                               \
-        f16x8 ha[4], hb[NJ];                                                            \
-        _Pragma("unroll") for (int i = 0; i < 4; i++) {                                 \
-          const uint32_t wa = kt == 0 ? CA[i].x : kt == 1 ? CA[i].y : kt == 2 ? CA[i].z : CA[i].w; \
-          ha[i] = nv_dequant8(wa, na[i]);                                               \
-        }                                                                               \
-        _Pragma("unroll") for (int j = 0; j < NJ; j++) {                                \
-          const uint32_t wb = kt == 0 ? CB[j].x : kt == 1 ? CB[j].y : kt == 2 ? CB[j].z : CB[j].w; \
-          hb[j] = nv_dequant8(wb, nb[j]);                                               \
-        }                                                                               \
+      f16x8 ha[4], hb[NJ], ha2[4], hb2[NJ];                                             \
+      _Pragma("unroll") for (int i = 0; i < 4; i++) {                                   \
+        na[i] = nv_scale(((P0) < 2) ? (pa_[i] & 0xffu) : ((pa_[i] >> 8) & 0xffu));      \
+        ha[i] = nv_dequant8(nv_word(CA[i], (P0)), na[i]);                                \
+      }                                                                                 \
+      _Pragma("unroll") for (int j = 0; j < NJ; j++) {                                  \
+        nb[j] = nv_scale(((P0) < 2) ? (pb_[j] & 0xffu) : ((pb_[j] >> 8) & 0xffu));      \
+        hb[j] = nv_dequant8(nv_word(CB[j], (P0)), nb[j]);                                \
+      }                                                                                 \
+      _Pragma("unroll") for (int kt = (P0); kt < (P1); kt++) {                          \
+        const int kn_ = kt + 1;                                                         \
         _Pragma("unroll") for (int i = 0; i < 4; i++)                                   \
         _Pragma("unroll") for (int j = 0; j < NJ; j++) {                                \
+          const int m_ = i * NJ + j;                                                    \
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(hb[j], ha[i], acc[i][j], 0, 0, 0); \
+          if (kn_ < (P1)) {                                                             \
+            if (m_ < 4) {                                                               \
+              if ((kn_ & 1) == 0) na[m_] = nv_scale((pa_[m_] >> 8) & 0xffu);            \
+              ha2[m_] = nv_dequant8(nv_word(CA[m_], kn_), na[m_]);                      \
+            } else if (m_ - 4 < NJ) {                                                   \
+              if ((kn_ & 1) == 0) nb[m_ - 4] = nv_scale((pb_[m_ - 4] >> 8) & 0xffu);    \
+              hb2[m_ - 4] = nv_dequant8(nv_word(CB[m_ - 4], kn_), nb[m_ - 4]);          \
+            }                                                                           \
+          }                                                                             \
           if constexpr (CP) {                                                           \
             _Pragma("unroll") for (int c = 0; c < nc_; c++)                             \
               if ((c * nm_) / nc_ == (kt * 4 + i) * NJ + j) G_COPY(LSLOT, LCHUNK, yo_, yos_, (WC), c); \
-            __builtin_amdgcn_sched_barrier(0);                                          \
           }                                                                             \
+          __builtin_amdgcn_sched_barrier(0);                                            \
         }                                                                               \
+        _Pragma("unroll") for (int i = 0; i < 4; i++) ha[i] = ha2[i];                   \
+        _Pragma("unroll") for (int j = 0; j < NJ; j++) hb[j] = hb2[j];                  \
       }                                                                                 \
     }                                                                                   \
   } while (0)
@@ -698,13 +712,20 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_fp4_kernel(GemmArgs g) {
     const bool next_ = x_ + 1 < S;                                                      \
     G_READ(slot_, 1, ca1, cb1);                                                         \
     __builtin_amdgcn_sched_barrier(0);                                                  \
-    G_MFMAS(ca0, cb0, sa_c, sb_c, 0, 0, 2);                                             \
-    if (((U) + 1) % CS != 0) {                                                          \
+    if constexpr (NV) {                                                                 \
+      /* one pipelined run over the half-stage */                                      \
+      if (((U) + 1) % CS != 0) G_READ_SCALES(nchunk_, (U) + 1, sa_n, sb_n);             \
       __builtin_amdgcn_sched_barrier(0);                                                \
-      G_READ_SCALES(nchunk_, (U) + 1, sa_n, sb_n);                                      \
-      __builtin_amdgcn_sched_barrier(0);                                                \
+      G_MFMAS(ca0, cb0, sa_c, sb_c, 0, 0, 4);                                           \
+    } else {                                                                            \
+      G_MFMAS(ca0, cb0, sa_c, sb_c, 0, 0, 2);                                           \
+      if (((U) + 1) % CS != 0) {                                                        \
+        __builtin_amdgcn_sched_barrier(0);                                              \
+        G_READ_SCALES(nchunk_, (U) + 1, sa_n, sb_n);                                    \
+        __builtin_amdgcn_sched_barrier(0);                                              \
+      }                                                                                 \
+      G_MFMAS(ca0, cb0, sa_c, sb_c, 0, 2, 4);                                           \
     }                                                                                   \
-    G_MFMAS(ca0, cb0, sa_c, sb_c, 0, 2, 4);                                             \
     __builtin_amdgcn_sched_barrier(0);                                                  \
     wait_lgkm0();                                                                       \
     if (next_)                                                                          \
