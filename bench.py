@@ -76,7 +76,8 @@ class QuantCall:
         self.blk = 16 if fmt == F.FP4_NVFP4 else 32
         dev = x.device
         self.opts = F.make_opts(fmt, flags, signs, seed, offset, amax.data_ptr() if amax is not None else 0)
-        self.codes = torch.empty((self.batch, R, C // 2), dtype=torch.uint8, device=dev)
+        self.ldc = F.code_pitch(C // 2)  # code rows on whole 128-byte lines
+        self.codes = torch.empty((self.batch, R, self.ldc), dtype=torch.uint8, device=dev)[:, :, : C // 2]
         self.lds = F.scale_pitch(C // self.blk)  # scale rows padded to 16 bytes, as the GEMM reads them
         self.scales_buf = torch.empty((self.batch, R, self.lds), dtype=torch.uint8, device=dev)
         self.scales = self.scales_buf[:, :, : C // self.blk]
@@ -93,8 +94,8 @@ class QuantCall:
     def __call__(self, i):
         x = self.xs[i % len(self.xs)]
         st = self.lib.fp4_quantize(x.data_ptr(), self.dt, self.batch, self.rows, self.cols, self.cols,
-                                   self.rows * self.cols, self.opts_ref, self.codes.data_ptr(), self.C // 2,
-                                   self.R * (self.C // 2), self.scales_buf.data_ptr(), self.lds,
+                                   self.rows * self.cols, self.opts_ref, self.codes.data_ptr(), self.ldc,
+                                   self.R * self.ldc, self.scales_buf.data_ptr(), self.lds,
                                    self.R * self.lds, self.ts.data_ptr(), self.ws.data_ptr(),
                                    self.ws_bytes, self.stream)
         if st != 0:
@@ -119,11 +120,12 @@ class GemmCall:
         self.ct = F.FP4_BF16 if out_dtype == torch.bfloat16 else F.FP4_F32
         self.stream = torch.cuda.current_stream().cuda_stream
         a, b = self.a, self.b
-        self.args = (a.fmt, self.G, self.M, self.N, self.K, a.codes.data_ptr(), half, self.M * half,
-                     a.scales.data_ptr(), a.scales.stride(1), a.scales.stride(0),
+        self.args = (a.fmt, self.G, self.M, self.N, self.K, a.codes.data_ptr(), a.codes.stride(1),
+                     a.codes.stride(0), a.scales.data_ptr(), a.scales.stride(1), a.scales.stride(0),
                      a.tensor_scale.data_ptr() if a.tensor_scale is not None else None,
-                     b.codes.data_ptr(), half, self.N * half, b.scales.data_ptr(), b.scales.stride(1),
-                     b.scales.stride(0), b.tensor_scale.data_ptr() if b.tensor_scale is not None else None,
+                     b.codes.data_ptr(), b.codes.stride(1), b.codes.stride(0), b.scales.data_ptr(),
+                     b.scales.stride(1), b.scales.stride(0),
+                     b.tensor_scale.data_ptr() if b.tensor_scale is not None else None,
                      self.c.data_ptr(), self.ct, self.N, self.M * self.N)
 
     def __call__(self, i):
@@ -153,11 +155,12 @@ class GemmQuantizeOutputCall:
         self.lds = F.scale_pitch(self.N // 16)
         self.scales = torch.empty((self.G, self.M, self.lds), dtype=torch.uint8, device=dev)
         self.ts = torch.empty((self.G,), dtype=torch.float32, device=dev)
-        self.args = (a.fmt, self.G, self.M, self.N, self.K, a.codes.data_ptr(), half, self.M * half,
-                     a.scales.data_ptr(), a.scales.stride(1), a.scales.stride(0),
+        self.args = (a.fmt, self.G, self.M, self.N, self.K, a.codes.data_ptr(), a.codes.stride(1),
+                     a.codes.stride(0), a.scales.data_ptr(), a.scales.stride(1), a.scales.stride(0),
                      a.tensor_scale.data_ptr() if a.tensor_scale is not None else None,
-                     b.codes.data_ptr(), half, self.N * half, b.scales.data_ptr(), b.scales.stride(1),
-                     b.scales.stride(0), b.tensor_scale.data_ptr() if b.tensor_scale is not None else None,
+                     b.codes.data_ptr(), b.codes.stride(1), b.codes.stride(0), b.scales.data_ptr(),
+                     b.scales.stride(1), b.scales.stride(0),
+                     b.tensor_scale.data_ptr() if b.tensor_scale is not None else None,
                      ctypes.byref(self.opts), self.codes.data_ptr(), self.N // 2, self.M * (self.N // 2),
                      self.scales.data_ptr(), self.lds, self.M * self.lds, self.ts.data_ptr())
         self.stream = torch.cuda.current_stream().cuda_stream
@@ -184,11 +187,12 @@ class GroupedGemmCall:
         self.offsets = offsets.to(device=a.codes.device, dtype=torch.int32)
         self.c = torch.empty((self.M, self.N), dtype=out_dtype, device=a.codes.device)
         ct = F.FP4_BF16 if out_dtype == torch.bfloat16 else F.FP4_F32
-        self.args = (a.fmt, self.G, self.offsets.data_ptr(), self.M, self.N, self.K, a.codes.data_ptr(), half,
-                     a.scales.data_ptr(), a.scales.stride(1),
+        self.args = (a.fmt, self.G, self.offsets.data_ptr(), self.M, self.N, self.K, a.codes.data_ptr(),
+                     a.codes.stride(1), a.scales.data_ptr(), a.scales.stride(1),
                      a.tensor_scale.data_ptr() if a.tensor_scale is not None else None,
-                     b.codes.data_ptr(), half, self.N * half, b.scales.data_ptr(), b.scales.stride(1),
-                     b.scales.stride(0), b.tensor_scale.data_ptr() if b.tensor_scale is not None else None,
+                     b.codes.data_ptr(), b.codes.stride(1), b.codes.stride(0), b.scales.data_ptr(),
+                     b.scales.stride(1), b.scales.stride(0),
+                     b.tensor_scale.data_ptr() if b.tensor_scale is not None else None,
                      self.c.data_ptr(), ct, self.N)
         self.stream = torch.cuda.current_stream().cuda_stream
 

@@ -191,12 +191,20 @@ def scale_pitch(n_blocks: int) -> int:
     return (n_blocks + 15) // 16 * 16
 
 
+def code_pitch(n_bytes: int) -> int:
+    """Code-row pitch in bytes: rounded up to 128 (one cache line), so that
+    every row starts on a line and no store of a row shares a line with the
+    next row (rows of 1440 bytes otherwise straddle lines)."""
+    return (n_bytes + 127) // 128 * 128
+
+
 @dataclass
 class Quantized:
     """Packed FP4 tensor as written by fp4_quantize. Shapes carry an optional
     leading batch dimension: codes [.., R, C/2], scales [.., R, C/blk],
-    tensor_scale [batch] (NVFP4) or None. `scales` may be a view whose row
-    pitch (stride(-2)) exceeds C/blk; quantize() pads it to scale_pitch()."""
+    tensor_scale [batch] (NVFP4) or None. `codes` and `scales` may be views
+    whose row pitch (stride(-2)) exceeds C/2 or C/blk: quantize() pads code
+    rows to code_pitch() and scale rows to scale_pitch()."""
     fmt: int
     codes: "torch.Tensor"
     scales: "torch.Tensor"
@@ -250,15 +258,16 @@ def quantize(x, fmt="nvfp4", *, four_over_six=False, block2d=False, transpose=Fa
     R, C = (cols, rows) if transpose else (rows, cols)
     blk = 16 if fmt == FP4_NVFP4 else 32
     dev = x3.device
-    codes = torch.empty((batch, R, C // 2), dtype=torch.uint8, device=dev)
+    ldc = code_pitch(C // 2)
+    codes = torch.empty((batch, R, ldc), dtype=torch.uint8, device=dev)[:, :, : C // 2]
     lds = scale_pitch(C // blk)
     scales_buf = torch.empty((batch, R, lds), dtype=torch.uint8, device=dev)
     scales = scales_buf[:, :, : C // blk]
     ts = torch.empty((batch,), dtype=torch.float32, device=dev) if fmt == FP4_NVFP4 else None
     ws_bytes = fp4_quantize_workspace(batch, rows, cols, opts)
     ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev) if ws_bytes else None
-    st = fp4_quantize(x3.data_ptr(), dt, batch, rows, cols, cols, rows * cols, opts, codes.data_ptr(), C // 2,
-                      R * (C // 2), scales_buf.data_ptr(), lds, R * lds,
+    st = fp4_quantize(x3.data_ptr(), dt, batch, rows, cols, cols, rows * cols, opts, codes.data_ptr(), ldc,
+                      R * ldc, scales_buf.data_ptr(), lds, R * lds,
                       ts.data_ptr() if ts is not None else None, ws.data_ptr() if ws is not None else None,
                       ws_bytes, _stream(stream))
     _check(st, "fp4_quantize")
@@ -274,6 +283,12 @@ def _check_scales(scales):
         raise ValueError("scale rows must be contiguous")
 
 
+def _check_codes(codes):
+    """Codes likewise: dense rows, any row / batch pitch."""
+    if codes.stride(-1) != 1:
+        raise ValueError("code rows must be contiguous")
+
+
 def dequantize(q: Quantized, dtype=None, stream=None):
     import torch
     dtype = dtype or torch.float32
@@ -284,7 +299,9 @@ def dequantize(q: Quantized, dtype=None, stream=None):
     y = torch.empty((batch, rows, cols), dtype=dtype, device=codes.device)
     dt = {torch.bfloat16: FP4_BF16, torch.float32: FP4_F32}[dtype]
     _check_scales(scales)
-    st = fp4_dequantize(q.fmt, batch, rows, cols, codes.data_ptr(), half, rows * half, scales.data_ptr(),
+    _check_codes(codes)
+    st = fp4_dequantize(q.fmt, batch, rows, cols, codes.data_ptr(), codes.stride(1), codes.stride(0),
+                        scales.data_ptr(),
                         scales.stride(1), scales.stride(0),
                         q.tensor_scale.data_ptr() if q.tensor_scale is not None else None, y.data_ptr(), dt, cols,
                         rows * cols, _stream(stream))
@@ -311,9 +328,11 @@ def gemm(a: Quantized, b: Quantized, out_dtype=None, stream=None):
     ct = {torch.bfloat16: FP4_BF16, torch.float32: FP4_F32}[out_dtype]
     _check_scales(asc)
     _check_scales(bsc)
-    st = fp4_gemm(a.fmt, G, M, N, K, ac.data_ptr(), half, M * half, asc.data_ptr(), asc.stride(1),
+    _check_codes(ac)
+    _check_codes(bc)
+    st = fp4_gemm(a.fmt, G, M, N, K, ac.data_ptr(), ac.stride(1), ac.stride(0), asc.data_ptr(), asc.stride(1),
                   asc.stride(0), a.tensor_scale.data_ptr() if a.tensor_scale is not None else None,
-                  bc.data_ptr(), half, N * half, bsc.data_ptr(), bsc.stride(1), bsc.stride(0),
+                  bc.data_ptr(), bc.stride(1), bc.stride(0), bsc.data_ptr(), bsc.stride(1), bsc.stride(0),
                   b.tensor_scale.data_ptr() if b.tensor_scale is not None else None, c.data_ptr(), ct, N, M * N,
                   _stream(stream))
     _check(st, "fp4_gemm")
@@ -346,18 +365,21 @@ def gemm_quantize_output(a: Quantized, b: Quantized, fmt="nvfp4", *, four_over_s
     opts = make_opts(qfmt, flags, rht_signs, seed, offset, amax_t.data_ptr() if amax_t is not None else 0)
     blk = 16 if qfmt == FP4_NVFP4 else 32
     dev = ac.device
-    codes = torch.empty((G, M, N // 2), dtype=torch.uint8, device=dev)
+    ldq = code_pitch(N // 2)
+    codes = torch.empty((G, M, ldq), dtype=torch.uint8, device=dev)[:, :, : N // 2]
     lds = scale_pitch(N // blk)
     scales_buf = torch.empty((G, M, lds), dtype=torch.uint8, device=dev)
     ts = torch.empty((G,), dtype=torch.float32, device=dev) if qfmt == FP4_NVFP4 else None
     _check_scales(asc)
     _check_scales(bsc)
-    st = fp4_gemm_quantize_output(a.fmt, G, M, N, half * 2, ac.data_ptr(), half, M * half, asc.data_ptr(),
-                                  asc.stride(1), asc.stride(0),
+    _check_codes(ac)
+    _check_codes(bc)
+    st = fp4_gemm_quantize_output(a.fmt, G, M, N, half * 2, ac.data_ptr(), ac.stride(1), ac.stride(0),
+                                  asc.data_ptr(), asc.stride(1), asc.stride(0),
                                   a.tensor_scale.data_ptr() if a.tensor_scale is not None else None,
-                                  bc.data_ptr(), half, N * half, bsc.data_ptr(), bsc.stride(1), bsc.stride(0),
-                                  b.tensor_scale.data_ptr() if b.tensor_scale is not None else None, opts,
-                                  codes.data_ptr(), N // 2, M * (N // 2), scales_buf.data_ptr(), lds, M * lds,
+                                  bc.data_ptr(), bc.stride(1), bc.stride(0), bsc.data_ptr(), bsc.stride(1),
+                                  bsc.stride(0), b.tensor_scale.data_ptr() if b.tensor_scale is not None else None,
+                                  opts, codes.data_ptr(), ldq, M * ldq, scales_buf.data_ptr(), lds, M * lds,
                                   ts.data_ptr() if ts is not None else None, _stream(stream))
     _check(st, "fp4_gemm_quantize_output")
     scales = scales_buf[:, :, : N // blk]
@@ -389,10 +411,12 @@ def gemm_grouped(a: Quantized, b: Quantized, offsets, out_dtype=None, stream=Non
     ct = {torch.bfloat16: FP4_BF16, torch.float32: FP4_F32}[out_dtype]
     _check_scales(a.scales.unsqueeze(0))
     _check_scales(bsc)
-    st = fp4_gemm_grouped(a.fmt, G, offsets.data_ptr(), M, N, half * 2, a.codes.data_ptr(), half,
+    _check_codes(a.codes)
+    _check_codes(bc)
+    st = fp4_gemm_grouped(a.fmt, G, offsets.data_ptr(), M, N, half * 2, a.codes.data_ptr(), a.codes.stride(0),
                           a.scales.data_ptr(), a.scales.stride(0),
                           a.tensor_scale.data_ptr() if a.tensor_scale is not None else None,
-                          bc.data_ptr(), half, N * half, bsc.data_ptr(), bsc.stride(1), bsc.stride(0),
+                          bc.data_ptr(), bc.stride(1), bc.stride(0), bsc.data_ptr(), bsc.stride(1), bsc.stride(0),
                           b.tensor_scale.data_ptr() if b.tensor_scale is not None else None, c.data_ptr(), ct, N,
                           _stream(stream))
     _check(st, "fp4_gemm_grouped")
