@@ -670,8 +670,8 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the multi-GPU sharding is described in DESIGN.md but not built", file=sys.stderr)
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "sharding the path over several GPUs is designed but not built", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
