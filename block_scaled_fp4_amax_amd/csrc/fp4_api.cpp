@@ -102,7 +102,8 @@ fp4_status plan_quantize(int64_t batch, int64_t rows, int64_t cols, const fp4_qu
   }
   if (nv && !o->amax_in && batch > 0 && rows > 0 && cols > 0) {
     p->nparts = amax_partials(rows, cols, o->flags);
-    p->ws = (size_t)batch * (size_t)p->nparts * sizeof(float);
+    // the partial maxima of every item, then each item's folded amax
+    p->ws = (size_t)batch * (size_t)(p->nparts + 1) * sizeof(float);
   }
   return FP4_OK;
 }

@@ -103,6 +103,29 @@ __global__ __launch_bounds__(256) void amax_kernel(QuantArgs a) {
         __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
 }
 
+// Folds batch item b's nparts partial maxima into T, written after all the
+// items' partials (workspace word batch * nparts + b), so that the quantizer
+// reads one word instead of every workgroup folding the partials again.
+constexpr int64_t kFoldOnceElems = int64_t(1) << 25;
+__global__ __launch_bounds__(256) void amax_finalize_kernel(QuantArgs a) {
+  const int64_t b = blockIdx.x;
+  const float* p = a.partials + b * a.nparts;
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < a.nparts; i += 256) m = __builtin_fmaxf(m, p[i]);
+  m = __builtin_fmaxf(m, xor_shfl<32>(m));
+  m = __builtin_fmaxf(m, xor_shfl<16>(m));
+  m = __builtin_fmaxf(m, xor_shfl<8>(m));
+  m = __builtin_fmaxf(m, xor_shfl<4>(m));
+  m = __builtin_fmaxf(m, xor_shfl<2>(m));
+  m = __builtin_fmaxf(m, xor_shfl<1>(m));
+  __shared__ float red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    a.partials[a.batch * a.nparts + b] =
+        __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+}
+
 // ------------------------------------------------------------------------
 // Row-major quantization
 // ------------------------------------------------------------------------
@@ -419,9 +442,17 @@ static void launch_typed(const QuantArgs& a, hipStream_t s) {
     else if (mode == kAmaxRhtRows) hipLaunchKernelGGL((amax_kernel<TIn, kAmaxRhtRows>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((amax_kernel<TIn, kAmaxRhtCols>), grid, dim3(256), 0, s, a);
   }
-  if (a.flags & kScaleSearch) launch_nv_sel<TIn, 2>(a, s);
-  else if (a.flags & kFourOverSix) launch_nv_sel<TIn, 1>(a, s);
-  else launch_nv_sel<TIn, 0>(a, s);
+  QuantArgs q = a;
+  // Large items: fold the partials once (one more small launch) rather than
+  // in every one of the quantizer's many workgroups; small ones keep the
+  // fold in the quantizer's prologue, where it costs less than a launch.
+  if (!a.amax_in && a.src_rows * a.src_cols >= kFoldOnceElems) {
+    hipLaunchKernelGGL(amax_finalize_kernel, dim3((unsigned)a.batch), dim3(256), 0, s, a);
+    q.amax_in = q.partials + q.batch * q.nparts;
+  }
+  if (q.flags & kScaleSearch) launch_nv_sel<TIn, 2>(q, s);
+  else if (q.flags & kFourOverSix) launch_nv_sel<TIn, 1>(q, s);
+  else launch_nv_sel<TIn, 0>(q, s);
 }
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
