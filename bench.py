@@ -46,11 +46,14 @@ ROTATE_BYTES = 600 << 20
 
 
 class Op:
-    """One library call in the step: `launch(i)` enqueues it for input set i."""
+    """One library call in the step: `launch(i)` enqueues it for input set i.
+    lane 0: on the step's stream, after every op before it; lane k > 0: on
+    side stream k, after the last lane-0 op before it (independent of the
+    other lanes' ops since then)."""
 
-    def __init__(self, name, kernel, bound, work, peak, launch, unit):
+    def __init__(self, name, kernel, bound, work, peak, launch, unit, lane=0):
         self.name, self.kernel, self.bound, self.work, self.peak = name, kernel, bound, work, peak
-        self.launch, self.unit = launch, unit
+        self.launch, self.unit, self.lane = launch, unit, lane
         self.durations = []
 
     def roofline_seconds(self):
@@ -240,8 +243,10 @@ def wl_moe(F, inputs):
     qw = QuantCall(F, copies(d["w"], n), F.FP4_MXFP4, F.FP4_TRANSPOSE)
     qx = QuantCall(F, copies(d["x"], n), F.FP4_MXFP4, 0)
     gm = GemmCall(F, qx, qw, torch.bfloat16)
-    ops = [Op("quantize W^T mxfp4 32x[2880x5760]", "quant_cols_kernel", "hbm", qw.bytes(), PEAK_HBM_GBS, qw, "GB/s"),
-           Op("quantize X mxfp4 32x[512x2880]", "quant_rows_kernel", "hbm", qx.bytes(), PEAK_HBM_GBS, qx, "GB/s"),
+    ops = [Op("quantize W^T mxfp4 32x[2880x5760]", "quant_cols_kernel", "hbm", qw.bytes(),
+              PEAK_HBM_GBS, qw, "GB/s"),
+           Op("quantize X mxfp4 32x[512x2880]", "quant_rows_kernel", "hbm", qx.bytes(),
+              PEAK_HBM_GBS, qx, "GB/s"),
            Op("grouped gemm mxfp4 (scaled FP4 MFMA)", "gemm_fp4_kernel<false, 256, 4, 1, false>", "mfma",
               gm.flops(), PEAK_TFLOPS["fp4"], gm, "TFLOP/s")]
     cfg = {"workload": "moe_mxfp4_grouped", "experts": 32, "M": 512, "N": 5760, "K": 2880, "output": "bf16",
@@ -259,9 +264,10 @@ def wl_training(F, inputs):
     q1 = QuantCall(F, ws, F.FP4_NVFP4, f)
     q2 = QuantCall(F, ws2, F.FP4_NVFP4, f | F.FP4_TRANSPOSE)
     q3 = QuantCall(F, gs, F.FP4_NVFP4, F.FP4_FOUR_OVER_SIX | F.FP4_STOCHASTIC, seed=d["sr_seed"])
-    ops = [Op("quantize W nvfp4 2D 4/6", "quant_rows_kernel", "hbm", q1.bytes(), PEAK_HBM_GBS, q1, "GB/s"),
-           Op("quantize W^T nvfp4 2D 4/6", "quant_cols_kernel", "hbm", q2.bytes(), PEAK_HBM_GBS, q2, "GB/s"),
-           Op("quantize G nvfp4 4/6 stochastic", "quant_rows_kernel", "hbm", q3.bytes(), PEAK_HBM_GBS, q3, "GB/s")]
+    ops = [Op("quantize W nvfp4 2D 4/6", "quant_rows_kernel", "hbm", q1.bytes(), PEAK_HBM_GBS, q1, "GB/s", lane=1),
+           Op("quantize W^T nvfp4 2D 4/6", "quant_cols_kernel", "hbm", q2.bytes(), PEAK_HBM_GBS, q2, "GB/s", lane=2),
+           Op("quantize G nvfp4 4/6 stochastic", "quant_rows_kernel", "hbm", q3.bytes(),
+              PEAK_HBM_GBS, q3, "GB/s", lane=3)]
     cfg = {"workload": "training_quantize_8192", "shape": [8192, 8192], "input_sets_rotated": n}
     return ops, cfg, "fp4 e2m1 codes (nvfp4), f32 scale arithmetic", None
 
@@ -273,8 +279,8 @@ def wl_rht(F, inputs):
     qx = QuantCall(F, copies(d["x"], n), F.FP4_NVFP4, f, signs=d["signs"])
     qw = QuantCall(F, copies(d["w"], n), F.FP4_NVFP4, f | F.FP4_TRANSPOSE, signs=d["signs"])
     gm = GemmCall(F, qx, qw, torch.bfloat16)
-    ops = [Op("quantize X nvfp4 4/6 RHT", "quant_rows_kernel", "hbm", qx.bytes(), PEAK_HBM_GBS, qx, "GB/s"),
-           Op("quantize W^T nvfp4 4/6 RHT", "quant_cols_kernel", "hbm", qw.bytes(), PEAK_HBM_GBS, qw, "GB/s"),
+    ops = [Op("quantize X nvfp4 4/6 RHT", "quant_rows_kernel", "hbm", qx.bytes(), PEAK_HBM_GBS, qx, "GB/s", lane=1),
+           Op("quantize W^T nvfp4 4/6 RHT", "quant_cols_kernel", "hbm", qw.bytes(), PEAK_HBM_GBS, qw, "GB/s", lane=2),
            Op("gemm nvfp4 (exact fp16 dequant + fp16 MFMA)", "gemm_fp4_kernel<true, 128, 4, 1, false>", "mfma",
               gm.flops(), PEAK_TFLOPS["f16"], gm, "TFLOP/s")]
     cfg = {"workload": "rht_activation_nvfp4", "M": 16384, "N": 12288, "K": 4096, "input_sets_rotated": n}
@@ -298,13 +304,14 @@ def wl_training_backward(F, inputs):
     qgt = QuantCall(F, gs2, F.FP4_NVFP4, fos | sr | tr, seed=d["sr_seed"], offset=1 << 40)
     qxt = QuantCall(F, xs, F.FP4_NVFP4, fos | tr)
     gw = GemmCall(F, qgt, qxt, torch.bfloat16)
-    ops = [Op("quantize dY nvfp4 4/6 stochastic", "quant_rows_kernel", "hbm", qg.bytes(), PEAK_HBM_GBS, qg, "GB/s"),
-           Op("quantize W^T nvfp4 2D 4/6", "quant_cols_kernel", "hbm", qwt.bytes(), PEAK_HBM_GBS, qwt, "GB/s"),
+    ops = [Op("quantize dY nvfp4 4/6 stochastic", "quant_rows_kernel", "hbm", qg.bytes(),
+              PEAK_HBM_GBS, qg, "GB/s", lane=1),
+           Op("quantize W^T nvfp4 2D 4/6", "quant_cols_kernel", "hbm", qwt.bytes(), PEAK_HBM_GBS, qwt, "GB/s", lane=2),
            Op("dgrad gemm nvfp4 dX = dY W", "gemm_fp4_kernel<true, 128, 4, 1, false>", "mfma", gd.flops(),
               PEAK_TFLOPS["f16"], gd, "TFLOP/s"),
            Op("quantize dY^T nvfp4 4/6 stochastic", "quant_cols_kernel", "hbm", qgt.bytes(), PEAK_HBM_GBS, qgt,
-              "GB/s"),
-           Op("quantize X^T nvfp4 4/6", "quant_cols_kernel", "hbm", qxt.bytes(), PEAK_HBM_GBS, qxt, "GB/s"),
+              "GB/s", lane=1),
+           Op("quantize X^T nvfp4 4/6", "quant_cols_kernel", "hbm", qxt.bytes(), PEAK_HBM_GBS, qxt, "GB/s", lane=2),
            Op("wgrad gemm nvfp4 dW = dY^T X", "gemm_fp4_kernel<true, 128, 4, 1, false>", "mfma", gw.flops(),
               PEAK_TFLOPS["f16"], gw, "TFLOP/s")]
     cfg = {"workload": "training_backward_nvfp4_8192", "M": 8192, "N": 8192, "K": 8192,
@@ -378,10 +385,11 @@ def wl_scale_search(F, inputs):
     q2 = QuantCall(F, copies(d["w"], n), F.FP4_NVFP4, F.FP4_SCALE_SEARCH | F.FP4_BLOCK2D)
     qm = QuantCall(F, copies(d["w"], n), F.FP4_MXFP4, F.FP4_FOUR_OVER_SIX)
     ops = [Op("quantize W nvfp4 scale search (amax pre-pass + quantize)", "amax_kernel+quant_rows_kernel", "hbm",
-              qs.bytes(), PEAK_HBM_GBS, qs, "GB/s"),
+              qs.bytes(), PEAK_HBM_GBS, qs, "GB/s", lane=1),
            Op("quantize W nvfp4 2D scale search (amax pre-pass + quantize)", "amax_kernel+quant_rows_kernel", "hbm",
-              q2.bytes(), PEAK_HBM_GBS, q2, "GB/s"),
-           Op("quantize W mxfp4 4/6 exponent pair", "quant_rows_kernel", "hbm", qm.bytes(), PEAK_HBM_GBS, qm, "GB/s")]
+              q2.bytes(), PEAK_HBM_GBS, q2, "GB/s", lane=2),
+           Op("quantize W mxfp4 4/6 exponent pair", "quant_rows_kernel", "hbm", qm.bytes(),
+              PEAK_HBM_GBS, qm, "GB/s", lane=3)]
     cfg = {"workload": "scale_search_8192", "shape": [8192, 8192], "weight": "8192x8192 bf16 N(0,0.02)",
            "input_sets_rotated": n}
     return ops, cfg, "fp4 e2m1 codes, f32 scale arithmetic", None
@@ -397,7 +405,8 @@ def wl_moe_routed(F, inputs):
     qw = QuantCall(F, copies(d["w"], n), F.FP4_MXFP4, F.FP4_TRANSPOSE)
     qx = QuantCall(F, copies(d["x"], n), F.FP4_MXFP4, 0)
     gm = GroupedGemmCall(F, qx, qw, d["offsets"], torch.bfloat16)
-    ops = [Op("quantize W^T mxfp4 32x[2880x5760]", "quant_cols_kernel", "hbm", qw.bytes(), PEAK_HBM_GBS, qw, "GB/s"),
+    ops = [Op("quantize W^T mxfp4 32x[2880x5760]", "quant_cols_kernel", "hbm", qw.bytes(),
+              PEAK_HBM_GBS, qw, "GB/s"),
            Op("quantize routed X mxfp4 [16384x2880]", "quant_rows_kernel", "hbm", qx.bytes(), PEAK_HBM_GBS, qx,
               "GB/s"),
            Op("grouped gemm mxfp4, router row counts", "gemm_fp4_kernel<false, 256, 4, 1, true>", "mfma",
@@ -560,19 +569,34 @@ def graph_step_ms(ops, steps, warmup):
     """Average step time with each step replayed as one captured HIP graph:
     the step's ops are captured once per input set (the ops read rotating
     copies, so each graph holds its own set's pointers) and the graphs are
-    replayed round-robin. Every replay runs every kernel of the step."""
+    replayed round-robin. Every replay runs every kernel of the step; ops on
+    side lanes (independent quantizations) run concurrently in the graph."""
     n = 1 + max(len(getattr(op.launch, "xs", [0])) for op in ops)
     cap = torch.cuda.Stream()
+    sides = {op.lane: torch.cuda.Stream() for op in ops if op.lane > 0}
     saved = [op.launch.stream for op in ops]
     graphs = []
     try:
         for i in range(n):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cap):
-                h = torch.cuda.current_stream().cuda_stream
+                main = torch.cuda.current_stream()
+                forked = set()
                 for op in ops:
-                    op.launch.stream = h
+                    if op.lane > 0:
+                        st = sides[op.lane]
+                        if op.lane not in forked:
+                            st.wait_stream(main)
+                            forked.add(op.lane)
+                        op.launch.stream = st.cuda_stream
+                    else:
+                        for k in forked:
+                            main.wait_stream(sides[k])
+                        forked.clear()
+                        op.launch.stream = main.cuda_stream
                     op.launch(i)
+                for k in forked:
+                    main.wait_stream(sides[k])
             graphs.append(g)
     finally:
         for op, st in zip(ops, saved):

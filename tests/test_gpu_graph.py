@@ -47,10 +47,14 @@ class Step:
                             q["ws"].data_ptr(), q["ws_bytes"], stream)
         assert st == 0, F.fp4_status_str(st)
 
-    def run(self, stream):
+    def run(self, stream, stream_a=None, stream_w=None):
         M, N, K = self.M, self.N, self.K
-        self._quantize(self.xa, self.qa, M, K, stream)
-        self._quantize(self.xw, self.qw, N, K, stream)
+        self._quantize(self.xa, self.qa, M, K, stream_a or stream)
+        self._quantize(self.xw, self.qw, N, K, stream_w or stream)
+        self.gemms(stream)
+
+    def gemms(self, stream):
+        M, N, K = self.M, self.N, self.K
         a, w = self.qa, self.qw
         st = F.fp4_gemm(F.FP4_NVFP4, 1, M, N, K, a["codes"].data_ptr(), K // 2, 0, a["scales"].data_ptr(),
                         a["lds"], 0, a["ts"].data_ptr(), w["codes"].data_ptr(), K // 2, 0, w["scales"].data_ptr(),
@@ -97,3 +101,41 @@ def test_graph_replays_match_eager():
         for k, (x, y) in enumerate(zip(got, want)):
             assert torch.equal(x, y), f"replay {r}: output {k} differs from the eager call"
         assert float(got[2][0]) != 0.0
+
+
+def test_graph_with_concurrent_quantizations():
+    """The two quantizations captured on two side streams forked from the
+    capture stream and joined before the GEMMs (as the benchmark captures its
+    steps): every replay equals the eager calls."""
+    M, N, K = 320, 256, 384
+    print(f"[graph] fork/join capture, {M}x{N}x{K}", flush=True)
+    step = Step(M, N, K)
+    d = inputs.w4a4_linear(m=M, n=N, k=K, seed=2, device="cuda")
+    step.xa.copy_(d["a"])
+    step.xw.copy_(d["w"])
+    step.run(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    sa, sw = torch.cuda.Stream(), torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        main = torch.cuda.current_stream()
+        sa.wait_stream(main)
+        sw.wait_stream(main)
+        step._quantize(step.xa, step.qa, M, K, sa.cuda_stream)
+        step._quantize(step.xw, step.qw, N, K, sw.cuda_stream)
+        main.wait_stream(sa)
+        main.wait_stream(sw)
+        step.gemms(main.cuda_stream)
+    for r in range(3):
+        d = inputs.w4a4_linear(m=M, n=N, k=K, seed=20 + r, device="cuda")
+        step.xa.copy_(d["a"])
+        step.xw.copy_(d["w"] * (0.5 + r))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = step.outputs()
+        step.run(torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        want = step.outputs()
+        for k, (x, y) in enumerate(zip(got, want)):
+            assert torch.equal(x, y), f"replay {r}: output {k} differs from the eager call"
