@@ -295,11 +295,27 @@ struct NvScale {
   float pow2;
   f16x2 mant;
 };
-__device__ __forceinline__ NvScale nv_scale(uint32_t byte) {
-  const float dec = e4m3_decode(byte);
-  const float m = __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, dec) & 0x007fffffu) | 0x3f800000u);
-  const _Float16 mh = (_Float16)m;
-  return NvScale{dec, f16x2{mh, mh}};
+// The scales of a lane's two blocks of one half-stage (E4M3 bytes 0 and 1 of
+// `pair`), decoded together: one packed fp8 -> fp32 conversion gives both
+// converter operands, and one packed fp16 conversion (exact: 1 + m/8 has 4
+// significant bits) both mantissa factors, block 0's in the low half. The
+// conversion's elements are copied to scalars before their bits are taken:
+// a bit cast of a vector element has been seen to read element 0.
+struct NvScale2 {
+  float pow2[2];
+  f16x2 mant;
+};
+__device__ __forceinline__ NvScale2 nv_scale2(uint32_t pair) {
+  const f32x2 pk = __builtin_amdgcn_cvt_pk_f32_fp8((int)pair, false);
+  const float d0 = pk[0], d1 = pk[1];
+  const float m0 = __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, d0) & 0x007fffffu) | 0x3f800000u);
+  const float m1 = __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, d1) & 0x007fffffu) | 0x3f800000u);
+  return NvScale2{{d0, d1}, __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(m0, m1))};
+}
+// block B's scale (B compile-time) in the form nv_dequant8 takes
+template <int B>
+__device__ __forceinline__ NvScale nv_block(const NvScale2& s) {
+  return NvScale{s.pow2[B], B ? f16x2{s.mant.y, s.mant.y} : f16x2{s.mant.x, s.mant.x}};
 }
 // 8 codes (one dword) -> 8 exact fp16 values of val * scale
 __device__ __forceinline__ f16x8 nv_dequant8(uint32_t w, const NvScale& s) {
@@ -640,15 +656,15 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_fp4_kernel(GemmArgs g) {
       uint32_t pa_[4], pb_[NJ];                                                         \
       _Pragma("unroll") for (int i = 0; i < 4; i++) pa_[i] = SA[i][(KB) & (NV ? 1 : 0)] >> (16 * h); \
       _Pragma("unroll") for (int j = 0; j < NJ; j++) pb_[j] = SB[j][(KB) & (NV ? 1 : 0)] >> (16 * h); \
-      NvScale na[4], nb[NJ];                                                            \
+      NvScale2 na[4], nb[NJ];                                                           \
       f16x8 ha[4], hb[NJ], ha2[4], hb2[NJ];                                             \
       _Pragma("unroll") for (int i = 0; i < 4; i++) {                                   \
-        na[i] = nv_scale(((P0) < 2) ? (pa_[i] & 0xffu) : ((pa_[i] >> 8) & 0xffu));      \
-        ha[i] = nv_dequant8(nv_word(CA[i], (P0)), na[i]);                                \
+        na[i] = nv_scale2(pa_[i]);                                                      \
+        ha[i] = nv_dequant8(nv_word(CA[i], (P0)), nv_block<((P0) >> 1)>(na[i]));         \
       }                                                                                 \
       _Pragma("unroll") for (int j = 0; j < NJ; j++) {                                  \
-        nb[j] = nv_scale(((P0) < 2) ? (pb_[j] & 0xffu) : ((pb_[j] >> 8) & 0xffu));      \
-        hb[j] = nv_dequant8(nv_word(CB[j], (P0)), nb[j]);                                \
+        nb[j] = nv_scale2(pb_[j]);                                                      \
+        hb[j] = nv_dequant8(nv_word(CB[j], (P0)), nv_block<((P0) >> 1)>(nb[j]));         \
       }                                                                                 \
       _Pragma("unroll") for (int kt = (P0); kt < (P1); kt++) {                          \
         const int kn_ = kt + 1;                                                         \
@@ -658,11 +674,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_fp4_kernel(GemmArgs g) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(hb[j], ha[i], acc[i][j], 0, 0, 0); \
           if (kn_ < (P1)) {                                                             \
             if (m_ < 4) {                                                               \
-              if ((kn_ & 1) == 0) na[m_] = nv_scale((pa_[m_] >> 8) & 0xffu);            \
-              ha2[m_] = nv_dequant8(nv_word(CA[m_], kn_), na[m_]);                      \
+              ha2[m_] = nv_dequant8(nv_word(CA[m_], kn_), kn_ < 2 ? nv_block<0>(na[m_]) : nv_block<1>(na[m_])); \
             } else if (m_ - 4 < NJ) {                                                   \
-              if ((kn_ & 1) == 0) nb[m_ - 4] = nv_scale((pb_[m_ - 4] >> 8) & 0xffu);    \
-              hb2[m_ - 4] = nv_dequant8(nv_word(CB[m_ - 4], kn_), nb[m_ - 4]);          \
+              hb2[m_ - 4] = nv_dequant8(nv_word(CB[m_ - 4], kn_), kn_ < 2 ? nv_block<0>(nb[m_ - 4]) : nv_block<1>(nb[m_ - 4])); \
             }                                                                           \
           }                                                                             \
           if constexpr (CP) {                                                           \
