@@ -12,10 +12,10 @@
 //
 // NVFP4: the MFMA scale operand is a power of two per 32 values, which cannot
 // carry an E4M3 scale per 16. Each lane therefore dequantizes its codes
-// exactly to fp16: the converter v_cvt_scalef32_pk_f16_fp4 gives
-// val * 2^E for the power-of-two part 2^E of the block scale, and one packed
-// fp16 multiply applies its mantissa factor 1 + m/8 (the product has at most
-// 6 significant bits and lies in [2^-10, 2688], so fp16 holds it exactly);
+// exactly to fp16: v_cvt_scalef32_pk_f16_fp4 gives the E2M1 values, and one
+// packed fp16 multiply applies the block scale, itself converted to fp16
+// (exact: every E4M3 value is a normal fp16; the product has at most 6
+// significant bits and lies in [2^-10, 2688], so fp16 holds it exactly);
 // v_mfma_f32_32x32x16_f16 multiplies, and the two tensor scales multiply the
 // accumulator in the epilogue. A lane's 32 K values feed four K=16 MFMAs
 // (8 values each); the K order inside the product is permuted identically
@@ -288,41 +288,26 @@ __device__ __forceinline__ i32x8 fp4_operand(const uint4& v) {
   return __builtin_shufflevector(q, q, 0, 1, 2, 3, -1, -1, -1, -1);
 }
 
-// NVFP4 block scale split for the fp16 dequant: the converter's scale operand
-// (only its exponent is used, so the decoded scale itself serves) and the
-// mantissa factor 1 + m/8 as an fp16 pair.
-struct NvScale {
-  float pow2;
-  f16x2 mant;
-};
-// The scales of a lane's two blocks of one half-stage (E4M3 bytes 0 and 1 of
-// `pair`), decoded together: one packed fp8 -> fp32 conversion gives both
-// converter operands, and one packed fp16 conversion (exact: 1 + m/8 has 4
-// significant bits) both mantissa factors, block 0's in the low half. The
-// conversion's elements are copied to scalars before their bits are taken:
-// a bit cast of a vector element has been seen to read element 0.
-struct NvScale2 {
-  float pow2[2];
-  f16x2 mant;
-};
-__device__ __forceinline__ NvScale2 nv_scale2(uint32_t pair) {
-  const f32x2 pk = __builtin_amdgcn_cvt_pk_f32_fp8((int)pair, false);
-  const float d0 = pk[0], d1 = pk[1];
-  const float m0 = __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, d0) & 0x007fffffu) | 0x3f800000u);
-  const float m1 = __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, d1) & 0x007fffffu) | 0x3f800000u);
-  return NvScale2{{d0, d1}, __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(m0, m1))};
+// The E4M3 scales of a lane's two blocks of one half-stage (bytes 0 and 1 of
+// `pair`) as an fp16 pair, block 0's in the low half, in one conversion:
+// every E4M3 value is a normal fp16, so the conversion is exact.
+__device__ __forceinline__ f16x2 nv_scale_pair(uint32_t pair) {
+  return __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pair, 1.0f, false));
 }
-// block B's scale (B compile-time) in the form nv_dequant8 takes
+// block B's scale (B compile-time) in both halves
 template <int B>
-__device__ __forceinline__ NvScale nv_block(const NvScale2& s) {
-  return NvScale{s.pow2[B], B ? f16x2{s.mant.y, s.mant.y} : f16x2{s.mant.x, s.mant.x}};
+__device__ __forceinline__ f16x2 nv_block(f16x2 s) {
+  return B ? f16x2{s.y, s.y} : f16x2{s.x, s.x};
 }
-// 8 codes (one dword) -> 8 exact fp16 values of val * scale
-__device__ __forceinline__ f16x8 nv_dequant8(uint32_t w, const NvScale& s) {
-  f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s.pow2, 0) * s.mant;
-  f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s.pow2, 1) * s.mant;
-  f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s.pow2, 2) * s.mant;
-  f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s.pow2, 3) * s.mant;
+// 8 codes (one dword) -> 8 exact fp16 values of val * scale: the converter
+// gives the E2M1 values, one packed fp16 multiply per two applies the scale
+// s (the product has at most 6 significant bits and lies in [2^-10, 2688],
+// so fp16 holds it exactly).
+__device__ __forceinline__ f16x8 nv_dequant8(uint32_t w, f16x2 s) {
+  f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
+  f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
+  f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
+  f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
   return f16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
@@ -656,14 +641,14 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_fp4_kernel(GemmArgs g) {
       uint32_t pa_[4], pb_[NJ];                                                         \
       _Pragma("unroll") for (int i = 0; i < 4; i++) pa_[i] = SA[i][(KB) & (NV ? 1 : 0)] >> (16 * h); \
       _Pragma("unroll") for (int j = 0; j < NJ; j++) pb_[j] = SB[j][(KB) & (NV ? 1 : 0)] >> (16 * h); \
-      NvScale2 na[4], nb[NJ];                                                           \
+      f16x2 na[4], nb[NJ];                                                               \
       f16x8 ha[4], hb[NJ], ha2[4], hb2[NJ];                                             \
       _Pragma("unroll") for (int i = 0; i < 4; i++) {                                   \
-        na[i] = nv_scale2(pa_[i]);                                                      \
+        na[i] = nv_scale_pair(pa_[i]);                                                      \
         ha[i] = nv_dequant8(nv_word(CA[i], (P0)), nv_block<((P0) >> 1)>(na[i]));         \
       }                                                                                 \
       _Pragma("unroll") for (int j = 0; j < NJ; j++) {                                  \
-        nb[j] = nv_scale2(pb_[j]);                                                      \
+        nb[j] = nv_scale_pair(pb_[j]);                                                      \
         hb[j] = nv_dequant8(nv_word(CB[j], (P0)), nv_block<((P0) >> 1)>(nb[j]));         \
       }                                                                                 \
       _Pragma("unroll") for (int kt = (P0); kt < (P1); kt++) {                          \
