@@ -65,6 +65,43 @@ def test_k_pipeline_depths(oracle, fmt, k):
              what=f"k-sweep K={k}")
 
 
+@pytest.mark.parametrize("fmt", [MX, NV], ids=["mx", "nv"])
+def test_every_block_scale_code(oracle, fmt):
+    """Random codes under block scales that run through every finite E4M3
+    code, zero and the subnormals included (NVFP4), or through 2^-17 .. 2^17
+    (MXFP4), on both operands, against the oracle's dequantize-then-matmul.
+    The codes and scales are set directly, not quantized."""
+    from gpu_util import upload_scales
+    rng = np.random.default_rng(11 + fmt)
+    M, N, K = 127, 96, 512
+    blk = 16 if fmt == NV else 32
+    ca = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
+    cb = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    if fmt == NV:
+        # 37 and 53 are prime to 127: each code appears about equally often
+        sa = (np.arange(M * (K // blk)) * 37 % 127).astype(np.uint8).reshape(M, K // blk)
+        sb = (np.arange(N * (K // blk)) * 53 % 127).astype(np.uint8).reshape(N, K // blk)
+        ts_a, ts_b = 0.125, 4.0
+    else:
+        sa = (110 + np.arange(M * (K // blk)) * 3 % 35).astype(np.uint8).reshape(M, K // blk)
+        sb = (110 + np.arange(N * (K // blk)) * 5 % 35).astype(np.uint8).reshape(N, K // blk)
+        ts_a = ts_b = None
+    da = oracle.dequantize(fmt, ca, sa, ts_a)
+    db = oracle.dequantize(fmt, cb, sb, ts_b)
+
+    def upload(codes, scales, ts):
+        t = torch.tensor([ts], dtype=torch.float32).cuda() if ts is not None else None
+        return F.Quantized(fmt, torch.from_numpy(codes).cuda(), upload_scales(scales), t)
+
+    print(f"[gemm] every-scale-code fmt={fmt} {M}x{N}x{K}", flush=True)
+    c = F.gemm(upload(ca, sa, ts_a), upload(cb, sb, ts_b), torch.float32)
+    torch.cuda.synchronize()
+    c = c if c.dim() == 2 else c[0]
+    ref = oracle.gemm_reference(da, db)
+    absab = np.abs(da).astype(np.float64) @ np.abs(db).astype(np.float64).T
+    check_close(c, ref, absab, K, torch.float32, f"every-scale-code fmt={fmt}")
+
+
 def test_nvfp4_grouped(oracle):
     a = torch.stack([inputs.w4a4_linear(m=33, n=64, k=128, seed=s)["a"] for s in range(3)])
     b = torch.stack([inputs.w4a4_linear(m=33, n=64, k=128, seed=s)["w"] for s in range(3)])
