@@ -311,6 +311,17 @@ __device__ __forceinline__ f16x8 nv_dequant8(uint32_t w, f16x2 s) {
   return f16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
+// Codes pr (0..3, compile-time after unrolling) of w -> one exact fp16 pair
+__device__ __forceinline__ f16x2 nv_dequant2(uint32_t w, int pr, f16x2 s) {
+  const f16x2 p = pr == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0)
+                : pr == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1)
+                : pr == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2)
+                          : __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+  return p * s;
+}
+__device__ __forceinline__ f16x8 join4(const f16x2 (&q)[4]) {
+  return f16x8{q[0].x, q[0].y, q[1].x, q[1].y, q[2].x, q[2].y, q[3].x, q[3].y};
+}
 // The dword of a lane's 16-byte fragment that sub-step kt (0..3) reads.
 __device__ __forceinline__ uint32_t nv_word(const uint4& c, int kt) {
   return kt == 0 ? c.x : kt == 1 ? c.y : kt == 2 ? c.z : c.w;
@@ -636,13 +647,16 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_fp4_kernel(GemmArgs g) {
       }                                                                                 \
     } else {                                                                            \
       /* software-pipelined: sub-step kt's MFMAs run while the fp16 fragments \
-         of kt + 1 are dequantized, one fragment after each MFMA */         \
+         of kt + 1 are dequantized, in equal shares after each MFMA: every \
+         MFMA is followed by (4 + NJ) / NJ converter + multiply pairs, so \
+         that no burst of VALU work outlasts the MFMA it hides behind */     \
       constexpr int nm_ = 16 * NJ;                                                      \
       uint32_t pa_[4], pb_[NJ];                                                         \
       _Pragma("unroll") for (int i = 0; i < 4; i++) pa_[i] = SA[i][(KB) & (NV ? 1 : 0)] >> (16 * h); \
       _Pragma("unroll") for (int j = 0; j < NJ; j++) pb_[j] = SB[j][(KB) & (NV ? 1 : 0)] >> (16 * h); \
       f16x2 na[4], nb[NJ];                                                               \
-      f16x8 ha[4], hb[NJ], ha2[4], hb2[NJ];                                             \
+      f16x8 ha[4], hb[NJ];                                                              \
+      f16x2 qa_[4][4], qb_[NJ][4];                                                      \
       _Pragma("unroll") for (int i = 0; i < 4; i++) {                                   \
         na[i] = nv_scale_pair(pa_[i]);                                                      \
         ha[i] = nv_dequant8(nv_word(CA[i], (P0)), nv_block<((P0) >> 1)>(na[i]));         \
@@ -658,10 +672,13 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_fp4_kernel(GemmArgs g) {
           const int m_ = i * NJ + j;                                                    \
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(hb[j], ha[i], acc[i][j], 0, 0, 0); \
           if (kn_ < (P1)) {                                                             \
-            if (m_ < 4) {                                                               \
-              ha2[m_] = nv_dequant8(nv_word(CA[m_], kn_), kn_ < 2 ? nv_block<0>(na[m_]) : nv_block<1>(na[m_])); \
-            } else if (m_ - 4 < NJ) {                                                   \
-              hb2[m_ - 4] = nv_dequant8(nv_word(CB[m_ - 4], kn_), kn_ < 2 ? nv_block<0>(nb[m_ - 4]) : nv_block<1>(nb[m_ - 4])); \
+            constexpr int qpm_ = (4 + NJ) / NJ;                                         \
+            _Pragma("unroll") for (int qq = 0; qq < qpm_; qq++) {                       \
+              const int q_ = m_ * qpm_ + qq, f_ = q_ >> 2, pr_ = q_ & 3;                \
+              if (f_ < 4)                                                               \
+                qa_[f_][pr_] = nv_dequant2(nv_word(CA[f_], kn_), pr_, kn_ < 2 ? nv_block<0>(na[f_]) : nv_block<1>(na[f_])); \
+              else if (f_ - 4 < NJ)                                                     \
+                qb_[f_ - 4][pr_] = nv_dequant2(nv_word(CB[f_ - 4], kn_), pr_, kn_ < 2 ? nv_block<0>(nb[f_ - 4]) : nv_block<1>(nb[f_ - 4])); \
             }                                                                           \
           }                                                                             \
           if constexpr (CP) {                                                           \
@@ -670,8 +687,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_fp4_kernel(GemmArgs g) {
           }                                                                             \
           __builtin_amdgcn_sched_barrier(0);                                            \
         }                                                                               \
-        _Pragma("unroll") for (int i = 0; i < 4; i++) ha[i] = ha2[i];                   \
-        _Pragma("unroll") for (int j = 0; j < NJ; j++) hb[j] = hb2[j];                  \
+        if (kn_ < (P1)) {                                                               \
+          _Pragma("unroll") for (int i = 0; i < 4; i++) ha[i] = join4(qa_[i]);          \
+          _Pragma("unroll") for (int j = 0; j < NJ; j++) hb[j] = join4(qb_[j]);         \
+        }                                                                               \
       }                                                                                 \
     }                                                                                   \
   } while (0)
