@@ -299,19 +299,11 @@ template <int B>
 __device__ __forceinline__ f16x2 nv_block(f16x2 s) {
   return B ? f16x2{s.y, s.y} : f16x2{s.x, s.x};
 }
-// 8 codes (one dword) -> 8 exact fp16 values of val * scale: the converter
-// gives the E2M1 values, one packed fp16 multiply per two applies the scale
-// s (the product has at most 6 significant bits and lies in [2^-10, 2688],
-// so fp16 holds it exactly).
-__device__ __forceinline__ f16x8 nv_dequant8(uint32_t w, f16x2 s) {
-  f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
-  f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
-  f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
-  f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
-  return f16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
-}
-
-// Codes pr (0..3, compile-time after unrolling) of w -> one exact fp16 pair
+// Codes 2 pr and 2 pr + 1 of w (pr 0..3, compile-time after unrolling) ->
+// their exact fp16 values of val * scale: the converter gives the E2M1
+// values, one packed fp16 multiply applies the block scale s (the product
+// has at most 6 significant bits and lies in [2^-10, 2688], so fp16 holds
+// it exactly).
 __device__ __forceinline__ f16x2 nv_dequant2(uint32_t w, int pr, f16x2 s) {
   const f16x2 p = pr == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0)
                 : pr == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1)
@@ -319,8 +311,14 @@ __device__ __forceinline__ f16x2 nv_dequant2(uint32_t w, int pr, f16x2 s) {
                           : __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
   return p * s;
 }
+// four fp16 pairs, in order, as one 8-value MFMA operand
 __device__ __forceinline__ f16x8 join4(const f16x2 (&q)[4]) {
   return f16x8{q[0].x, q[0].y, q[1].x, q[1].y, q[2].x, q[2].y, q[3].x, q[3].y};
+}
+// all 8 codes of w
+__device__ __forceinline__ f16x8 nv_dequant8(uint32_t w, f16x2 s) {
+  const f16x2 q[4] = {nv_dequant2(w, 0, s), nv_dequant2(w, 1, s), nv_dequant2(w, 2, s), nv_dequant2(w, 3, s)};
+  return join4(q);
 }
 // The dword of a lane's 16-byte fragment that sub-step kt (0..3) reads.
 __device__ __forceinline__ uint32_t nv_word(const uint4& c, int kt) {
