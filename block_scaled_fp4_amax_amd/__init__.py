@@ -4,9 +4,9 @@ W4A4 block-scaled GEMM on AMD MI355X (gfx950).
 The compute lives in ``libfp4.so`` (hand-written HIP kernels behind the C ABI
 of ``include/fp4.h``). This module only marshals arguments:
 
-* ``fp4_quantize``, ``fp4_dequantize``, ``fp4_gemm``, ``fp4_gemm_grouped``,
-  ``fp4_gemm_quantize_output``, ``fp4_quantize_workspace``,
-  ``fp4_status_str`` -- the C entry points with
+* ``fp4_quantize``, ``fp4_quantize_noalloc``, ``fp4_dequantize``,
+  ``fp4_gemm``, ``fp4_gemm_grouped``, ``fp4_gemm_quantize_output``,
+  ``fp4_quantize_workspace``, ``fp4_status_str`` -- the C entry points with
   the same names and argument order (integers for device pointers);
 * ``quantize``, ``dequantize``, ``gemm``, ``gemm_grouped``,
   ``gemm_quantize_output`` -- conveniences over torch device
@@ -34,6 +34,8 @@ FP4_ERR_ALIGN = -3
 FP4_ERR_DEVICE = -4
 FP4_ERR_WORKSPACE = -5
 FP4_ERR_HIP = -6
+FP4_ERR_SCRATCH = -7
+FP4_NOALLOC_SCRATCH_BYTES = 262144
 # fp4_format / fp4_dtype
 FP4_MXFP4 = 0
 FP4_NVFP4 = 1
@@ -47,8 +49,8 @@ FP4_STOCHASTIC = 8
 FP4_HADAMARD = 16
 FP4_SCALE_SEARCH = 32
 
-EXPORTED_SYMBOLS = ("fp4_quantize_workspace", "fp4_quantize", "fp4_dequantize", "fp4_gemm", "fp4_gemm_grouped",
-                    "fp4_gemm_quantize_output", "fp4_status_str")
+EXPORTED_SYMBOLS = ("fp4_quantize_workspace", "fp4_quantize", "fp4_quantize_noalloc", "fp4_dequantize", "fp4_gemm",
+                    "fp4_gemm_grouped", "fp4_gemm_quantize_output", "fp4_status_str")
 
 
 class fp4_quant_opts(ctypes.Structure):
@@ -87,6 +89,10 @@ def lib() -> ctypes.CDLL:
         L.fp4_quantize.argtypes = [
             c_void_p, c_int32, c_int64, c_int64, c_int64, c_int64, c_int64, ctypes.POINTER(fp4_quant_opts),
             c_void_p, c_int64, c_int64, c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_size_t, c_void_p]
+        L.fp4_quantize_noalloc.restype = c_int32
+        L.fp4_quantize_noalloc.argtypes = [
+            c_void_p, c_int32, c_int64, c_int64, c_int64, c_int64, c_int64, ctypes.POINTER(fp4_quant_opts),
+            c_void_p, c_int64, c_int64, c_void_p, c_int64, c_int64, c_void_p, c_void_p]
         L.fp4_dequantize.restype = c_int32
         L.fp4_dequantize.argtypes = [
             c_int32, c_int64, c_int64, c_int64, c_void_p, c_int64, c_int64, c_void_p, c_int64, c_int64,
@@ -146,6 +152,13 @@ def fp4_quantize(x, x_dtype, batch, rows, cols, ld_x, batch_stride_x, opts: fp4_
     return lib().fp4_quantize(x, x_dtype, batch, rows, cols, ld_x, batch_stride_x, ctypes.byref(opts), codes,
                               ld_codes, batch_stride_codes, scales, ld_scales, batch_stride_scales, tensor_scale,
                               workspace, workspace_bytes, stream)
+
+
+def fp4_quantize_noalloc(x, x_dtype, batch, rows, cols, ld_x, batch_stride_x, opts: fp4_quant_opts, codes, ld_codes,
+                         batch_stride_codes, scales, ld_scales, batch_stride_scales, tensor_scale, stream) -> int:
+    return lib().fp4_quantize_noalloc(x, x_dtype, batch, rows, cols, ld_x, batch_stride_x, ctypes.byref(opts), codes,
+                                      ld_codes, batch_stride_codes, scales, ld_scales, batch_stride_scales,
+                                      tensor_scale, stream)
 
 
 def fp4_dequantize(fmt, batch, rows, cols, codes, ld_codes, batch_stride_codes, scales, ld_scales,

@@ -12,6 +12,8 @@
 
 using namespace fp4impl;
 
+static_assert(FP4_NOALLOC_SCRATCH_BYTES == kNoAllocScratchBytes, "the header states the scratch size");
+
 namespace {
 
 constexpr uint32_t kKnownFlags =
@@ -121,6 +123,7 @@ const char* fp4_status_str(int32_t s) {
     case FP4_ERR_DEVICE: return "FP4_ERR_DEVICE: current HIP device is not gfx950";
     case FP4_ERR_WORKSPACE: return "FP4_ERR_WORKSPACE: workspace missing or too small";
     case FP4_ERR_HIP: return "FP4_ERR_HIP: HIP runtime error";
+    case FP4_ERR_SCRATCH: return "FP4_ERR_SCRATCH: needs more than the built-in scratch, or it could not be located";
     default: return "unknown fp4 status";
   }
 }
@@ -131,11 +134,16 @@ size_t fp4_quantize_workspace(int64_t batch, int64_t rows, int64_t cols, const f
   return p.ws;
 }
 
-fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t batch, int64_t rows, int64_t cols,
-                        int64_t ld_x, int64_t batch_stride_x, const fp4_quant_opts* opts,
-                        uint8_t* codes, int64_t ld_codes, int64_t batch_stride_codes,
-                        uint8_t* scales, int64_t ld_scales, int64_t batch_stride_scales,
-                        float* tensor_scale, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+// fp4_quantize and fp4_quantize_noalloc: the amax partials go to the
+// caller's workspace, or (noalloc) to the library's per-GPU scratch array.
+static fp4_status quantize_impl(const void* x, int32_t x_dtype, int64_t batch, int64_t rows, int64_t cols,
+                                int64_t ld_x, int64_t batch_stride_x, const fp4_quant_opts* opts,
+                                uint8_t* codes, int64_t ld_codes, int64_t batch_stride_codes,
+                                uint8_t* scales, int64_t ld_scales, int64_t batch_stride_scales,
+                                float* tensor_scale, void* workspace, size_t workspace_bytes, bool noalloc,
+                                void* stream) {
   QuantPlan p;
   fp4_status st = plan_quantize(batch, rows, cols, opts, &p);
   if (st != FP4_OK) return st;
@@ -155,12 +163,22 @@ fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t batch, int64_t r
   if (!aligned(codes, 8) || ld_codes % 8 != 0 || (batch > 1 && batch_stride_codes % 8 != 0)) return FP4_ERR_ALIGN;
   if (nv && !aligned(tensor_scale, 4)) return FP4_ERR_ALIGN;
   if (nv && opts->amax_in && !aligned(opts->amax_in, 4)) return FP4_ERR_ALIGN;
-  if (p.ws > 0) {
+  if (noalloc) {
+    if (p.ws > kNoAllocScratchBytes) return FP4_ERR_SCRATCH;
+  } else if (p.ws > 0) {
     if (!workspace || workspace_bytes < p.ws) return FP4_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return FP4_ERR_ALIGN;
   }
   st = check_device();
   if (st != FP4_OK) return st;
+  if (noalloc && p.ws > 0) {
+    float* sp = nullptr;
+    if (noalloc_scratch(&sp) != hipSuccess) {
+      (void)hipGetLastError();
+      return FP4_ERR_SCRATCH;
+    }
+    workspace = sp;
+  }
 
   QuantArgs a{};
   a.x = x;
@@ -189,6 +207,28 @@ fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t batch, int64_t r
   a.nparts = p.nparts;
   (void)hipGetLastError();
   return launch_quantize(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FP4_OK : FP4_ERR_HIP;
+}
+
+extern "C" {
+
+fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t batch, int64_t rows, int64_t cols,
+                        int64_t ld_x, int64_t batch_stride_x, const fp4_quant_opts* opts,
+                        uint8_t* codes, int64_t ld_codes, int64_t batch_stride_codes,
+                        uint8_t* scales, int64_t ld_scales, int64_t batch_stride_scales,
+                        float* tensor_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  return quantize_impl(x, x_dtype, batch, rows, cols, ld_x, batch_stride_x, opts, codes, ld_codes,
+                       batch_stride_codes, scales, ld_scales, batch_stride_scales, tensor_scale, workspace,
+                       workspace_bytes, false, stream);
+}
+
+fp4_status fp4_quantize_noalloc(const void* x, int32_t x_dtype, int64_t batch, int64_t rows, int64_t cols,
+                                int64_t ld_x, int64_t batch_stride_x, const fp4_quant_opts* opts,
+                                uint8_t* codes, int64_t ld_codes, int64_t batch_stride_codes,
+                                uint8_t* scales, int64_t ld_scales, int64_t batch_stride_scales,
+                                float* tensor_scale, void* stream) {
+  return quantize_impl(x, x_dtype, batch, rows, cols, ld_x, batch_stride_x, opts, codes, ld_codes,
+                       batch_stride_codes, scales, ld_scales, batch_stride_scales, tensor_scale, nullptr, 0,
+                       true, stream);
 }
 
 fp4_status fp4_dequantize(int32_t format, int64_t batch, int64_t rows, int64_t cols,

@@ -42,6 +42,14 @@ int amax_partials(int64_t src_rows, int64_t src_cols, uint32_t flags);
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 
+// Bytes of the library's own scratch array (one copy per GPU) that
+// fp4_quantize_noalloc puts the NVFP4 amax partials in.
+constexpr size_t kNoAllocScratchBytes = 262144;
+
+// The current device's address of that array, looked up on the first call
+// per device and cached; hipSuccess or the runtime's error.
+hipError_t noalloc_scratch(float** ptr);
+
 struct DequantArgs {
   bool nvfp4;
   int64_t batch, rows, cols;

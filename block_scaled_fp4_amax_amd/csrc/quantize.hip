@@ -14,9 +14,42 @@
 //                      so each output row is written as whole lines.
 //
 // The method is stated in quant_common.h.
+#include <mutex>
+
 #include "quant_common.h"
 
 namespace fp4impl {
+
+// ------------------------------------------------------------------------
+// Scratch of fp4_quantize_noalloc: the NVFP4 amax partials of a call, in an
+// array every GPU holds a copy of until the process ends, so the call needs
+// no workspace and allocates nothing. In host code `scratch` names a host
+// stand-in, not device memory: kernels get the device address that
+// hipGetSymbolAddress reports for the current device, never the name.
+// ------------------------------------------------------------------------
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+hipError_t noalloc_scratch(float** ptr) {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static float* per_dev[kMaxDev] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev < kMaxDev && per_dev[dev]) {
+    *ptr = per_dev[dev];
+    return hipSuccess;
+  }
+  void* p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  if (!p) return hipErrorInvalidSymbol;
+  if (dev < kMaxDev) per_dev[dev] = static_cast<float*>(p);
+  *ptr = static_cast<float*>(p);
+  return hipSuccess;
+}
 
 // ------------------------------------------------------------------------
 // amax pre-pass

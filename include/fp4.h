@@ -55,7 +55,9 @@ typedef enum {
   FP4_ERR_ALIGN = -3,       /* pointer or stride misaligned (see each entry point) */
   FP4_ERR_DEVICE = -4,      /* the current HIP device is not gfx950 */
   FP4_ERR_WORKSPACE = -5,   /* workspace missing or smaller than fp4_quantize_workspace() */
-  FP4_ERR_HIP = -6          /* the HIP runtime reported an error at launch */
+  FP4_ERR_HIP = -6,         /* the HIP runtime reported an error at launch */
+  FP4_ERR_SCRATCH = -7      /* fp4_quantize_noalloc: the call needs more scratch than
+                               FP4_NOALLOC_SCRATCH_BYTES, or the scratch could not be located */
 } fp4_status;
 
 typedef enum { FP4_MXFP4 = 0, FP4_NVFP4 = 1 } fp4_format;
@@ -149,6 +151,33 @@ fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t batch, int64_t r
                         uint8_t* codes, int64_t ld_codes, int64_t batch_stride_codes,
                         uint8_t* scales, int64_t ld_scales, int64_t batch_stride_scales,
                         float* tensor_scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fp4_quantize_noalloc -- fp4_quantize for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc. Same arguments, results and errors as
+ * fp4_quantize, without the workspace: the NVFP4 tensor-amax partials go to
+ * a scratch array inside the library, FP4_NOALLOC_SCRATCH_BYTES per GPU,
+ * held by each GPU the library runs on until the process ends. Nothing is
+ * allocated or freed and no allocating routine is called.
+ *   Limit: a call whose fp4_quantize_workspace() would exceed
+ *   FP4_NOALLOC_SCRATCH_BYTES returns FP4_ERR_SCRATCH with nothing enqueued
+ *   (one NVFP4 item without amax_in needs at most 4100 bytes, so up to 63
+ *   batch items always fit). MXFP4, and NVFP4 with amax_in, need none.
+ *   The first call on a device looks up that device's copy of the array
+ *   (FP4_ERR_SCRATCH if the runtime cannot); later calls reuse the address.
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one
+ *   GPU (different streams, or different host threads without ordering)
+ *   race and may produce wrong tensor scales. Calls ordered on one stream
+ *   are safe. The array keeps the last call's contents; no word of it needs
+ *   to start at zero (the pre-pass writes every word the quantizer reads).
+ */
+#define FP4_NOALLOC_SCRATCH_BYTES 262144
+fp4_status fp4_quantize_noalloc(const void* x, int32_t x_dtype, int64_t batch, int64_t rows, int64_t cols,
+                                int64_t ld_x, int64_t batch_stride_x, const fp4_quant_opts* opts,
+                                uint8_t* codes, int64_t ld_codes, int64_t batch_stride_codes,
+                                uint8_t* scales, int64_t ld_scales, int64_t batch_stride_scales,
+                                float* tensor_scale, void* stream);
 
 /*
  * fp4_dequantize -- y = val(code) * scale, per element ("FP4", section "Como

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_entry_point(fp4):
 
 
 def test_status_strings(fp4):
-    for s in range(-6, 1):
+    for s in range(-7, 1):
         txt = fp4.fp4_status_str(s)
         assert txt.startswith("FP4_")
     assert "unknown" in fp4.fp4_status_str(-99)
@@ -113,6 +113,40 @@ def test_workspace_size_and_errors(fp4):
     assert q(fp4, nv, ws=0, ws_bytes=0) == fp4.FP4_ERR_WORKSPACE
     assert q(fp4, nv, ws_bytes=need - 4) == fp4.FP4_ERR_WORKSPACE
     assert q(fp4, nv, ws=FAKE + 4) == fp4.FP4_ERR_ALIGN
+
+
+def qn(fp4, opts, batch=1, rows=64, cols=64, x=FAKE, codes=FAKE, scales=FAKE, ts=FAKE):
+    tr = opts.flags & fp4.FP4_TRANSPOSE
+    R, C = (cols, rows) if tr else (rows, cols)
+    blk = 16 if opts.format == fp4.FP4_NVFP4 else 32
+    return fp4.fp4_quantize_noalloc(x, 1, batch, rows, cols, cols, rows * cols, opts, codes, C // 2, R * (C // 2),
+                                    scales, C // blk, R * (C // blk), ts, None)
+
+
+def test_noalloc_validation_and_scratch_limit(fp4):
+    nv = fp4.make_opts(fp4.FP4_NVFP4)
+    assert fp4.FP4_NOALLOC_SCRATCH_BYTES == 262144
+    # the same argument checks as fp4_quantize
+    assert qn(fp4, nv, cols=24) == fp4.FP4_ERR_INVALID
+    assert qn(fp4, nv, x=0) == fp4.FP4_ERR_INVALID
+    assert qn(fp4, nv, x=FAKE + 8) == fp4.FP4_ERR_ALIGN
+    assert qn(fp4, fp4.make_opts(fp4.FP4_MXFP4, flags=fp4.FP4_BLOCK2D)) == fp4.FP4_ERR_UNSUPPORTED
+    for kw in ({"rows": 0}, {"batch": 0}):
+        assert qn(fp4, nv, x=0, codes=0, scales=0, ts=0, **kw) == fp4.FP4_OK
+    # an NVFP4 item without amax_in needs at most 1025 words: 63 items fit,
+    # 64 of the largest size do not, and are refused before any HIP call
+    big = (8192, 8192)
+    per_item = fp4.fp4_quantize_workspace(1, *big, nv)
+    assert per_item == 1025 * 4
+    assert 63 * per_item <= fp4.FP4_NOALLOC_SCRATCH_BYTES < 64 * per_item
+    assert qn(fp4, nv, batch=64, rows=big[0], cols=big[1]) == fp4.FP4_ERR_SCRATCH
+
+
+@cpu_only
+def test_valid_noalloc_without_gfx950_reports_device(fp4):
+    assert qn(fp4, fp4.make_opts(fp4.FP4_NVFP4)) == fp4.FP4_ERR_DEVICE
+    assert qn(fp4, fp4.make_opts(fp4.FP4_NVFP4), batch=63, rows=8192, cols=8192) == fp4.FP4_ERR_DEVICE
+    assert qn(fp4, fp4.make_opts(fp4.FP4_MXFP4)) == fp4.FP4_ERR_DEVICE
 
 
 @cpu_only
