@@ -216,8 +216,8 @@ static float load_elem(const void* x, int dtype, int64_t idx) {
 }
 
 /* Materialise the working matrix W [rows_out, cols_out] in fp32: the input,
- * transposed when OR_TRANSPOSE is set ([4o6] "transposed inputs": quantize
- * X^T, blocks running along the rows of X^T), then the RHT on every 16-slice
+ * transposed when OR_TRANSPOSE is set ([4o6] option list: transposed
+ * inputs; quantize X^T, blocks running along the rows of X^T), then the RHT on every 16-slice
  * of each row when OR_HADAMARD is set. Returns malloc'd memory. */
 static float* working_matrix(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
                              unsigned flags, uint32_t signs, int64_t* rows_out, int64_t* cols_out) {
@@ -251,8 +251,8 @@ float or_tensor_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64
   return t;
 }
 
-/* NVFP4 per-tensor FP32 scale ([FP4]: "a second FP32 per-tensor scale").
- * Reading: amax-based, S_t = T / D with D = 6 * 448 so that the block holding
+/* NVFP4 per-tensor FP32 scale ([FP4] "Como funciona FP4": NVFP4 puts one
+ * FP32 scale per tensor on top of its E4M3 block scales). Reading: amax-based, S_t = T / D with D = 6 * 448 so that the block holding
  * the tensor max gets the largest E4M3 scale; under 4/6, D = 4 * 448 so the
  * M = 4 candidate of that block does not saturate. If S_t is zero, denormal or
  * not finite, S_t = 1 (the tensor then quantizes to zeros). */
@@ -456,7 +456,7 @@ int or_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld
         /* The 4/6 choice widened to every E4M3 scale between the two: the
          * candidates are the codes from the M = 6 candidate's up to the
          * M = 4 candidate's, so the block max maps to each representable
-         * point between 6 and 4 (a reading of "more candidate maxima"; the
+         * point between 6 and 4 (a reading of trying more candidate maxima; the
          * tensor scale is the 4/6 one). Each candidate's error is the 4/6
          * error below; the smallest wins, ties keep the smaller code. */
         uint8_t hi = nv_candidate(a, 4.0f, S_t).code;
@@ -536,31 +536,29 @@ int or_dequantize(int format, int64_t R, int64_t C, const uint8_t* codes, const 
 }
 
 /* ------------------------------------------------------------------------ */
-/* The worked example's float-scale mode ([FP4] "Como funciona FP4" snippet):  */
-/* scale = block amax / 6 in fp32, the nearest grid value to |x| / scale      */
-/* (first index on ties, as an argmin does), dequantized as                   */
-/* grid * sign(x) * scale. Writes the dequantized tensor.                     */
+/* Float-scale mode of the worked example ([FP4] "Como funciona FP4"): the    */
+/* plain block scaling the page measures its MAE with, before any scale       */
+/* format. Each block's scale is its largest magnitude over 6, in fp32, so    */
+/* that the block max lands on 6; every value becomes the E2M1 magnitude      */
+/* nearest to t = fl(|x| / scale), carrying the sign of x (zero stays zero),  */
+/* times the scale. Where two magnitudes are equally near, the example keeps  */
+/* the smaller one. That nearest magnitude is found as the number of          */
+/* midpoints between neighbouring magnitudes that t exceeds (strictly, so     */
+/* that a tie keeps the smaller one). Writes the dequantized tensor.          */
 /* ------------------------------------------------------------------------ */
 int or_float_scale_dequant(const float* x, int64_t n, int64_t block, float* deq) {
+  static const float MIDPOINT[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
   if (block <= 0 || n % block != 0) return -1;
-  for (int64_t b0 = 0; b0 < n; b0 += block) {
-    float amax = 0.0f;
-    for (int64_t i = b0; i < b0 + block; i++)
-      if (fabsf(x[i]) > amax) amax = fabsf(x[i]);
-    float scale = amax / 6.0f;
-    for (int64_t i = b0; i < b0 + block; i++) {
-      float t = fabsf(x[i]) / scale;
-      int best = 0;
-      float best_d = fabsf(t - E2M1_MAGNITUDE[0]);
-      for (int j = 1; j < 8; j++) {
-        float d = fabsf(t - E2M1_MAGNITUDE[j]);
-        if (d < best_d) {
-          best_d = d;
-          best = j;
-        }
-      }
-      float sgn = (x[i] > 0.0f) ? 1.0f : (x[i] < 0.0f ? -1.0f : 0.0f);
-      deq[i] = (E2M1_MAGNITUDE[best] * sgn) * scale;
+  for (int64_t start = 0; start < n; start += block) {
+    float largest = 0.0f;
+    for (int64_t i = start; i < start + block; i++) largest = fmaxf(largest, fabsf(x[i]));
+    const float scale = largest / 6.0f;
+    for (int64_t i = start; i < start + block; i++) {
+      const float t = fabsf(x[i]) / scale;
+      int m = 0;
+      while (m < 7 && t > MIDPOINT[m]) m++;
+      const float mag = E2M1_MAGNITUDE[m] * scale;
+      deq[i] = x[i] > 0.0f ? mag : (x[i] < 0.0f ? -mag : 0.0f);
     }
   }
   return 0;

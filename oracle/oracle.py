@@ -16,8 +16,16 @@ other than the oracle itself:
   Philox4x32-10        rocRAND's independent implementation
   stochastic rounding  unbiasedness on exact fractions; brute-force bracket
   Hadamard transform   dense Sylvester matrix (exact rational), orthogonality
-  MXFP4 / NVFP4 / 4/6  brute force over candidate scales on tiny inputs
-                       (exact rationals), invariants (saturation, scale 448)
+  MXFP4 / NVFP4 / 4/6  exact argmin of the candidates' errors on 10^5 blocks
+  and the scale search   each (float64 certified to 1e-13, spot-checked with
+                       fractions), outside a band derived from the float32
+                       evaluation the readings fix; exact nearest E4M3 and
+                       E2M1 codes outside their rounding bands; invariants
+                       (saturation, scale 448)
+  RHT and SR inside    quantize with the transform = quantize of the exactly
+  the quantizer        rotated copy; every SR code = e2m1_sr of the scaled
+                       value with rocRAND's draw of its output index;
+                       unbiased mean over 2^12 offsets
   2D / transpose       transpose symmetry, constant tiles reduce to 1D
   GEMM reference       dequantize + numpy float64 matmul (library routine)
   grouped GEMM         brute-force sum over k per output element; one group

@@ -3,8 +3,6 @@ worked example, brute-force searches on small inputs, torch's OCP FP8 casts,
 rocRAND's Philox, closed forms and invariants. CPU only."""
 import json
 import math
-import shutil
-import subprocess
 from fractions import Fraction
 from pathlib import Path
 
@@ -148,21 +146,6 @@ def test_e8m0_byte_decodes_to_power_of_two():
 # ---------------------------------------------------------------------------
 # Philox4x32-10 and stochastic rounding
 # ---------------------------------------------------------------------------
-@pytest.fixture(scope="module")
-def rocrand_philox(tmp_path_factory):
-    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
-    if not Path(hipcc).exists():
-        pytest.skip("hipcc not available to build the rocRAND reference")
-    exe = tmp_path_factory.mktemp("philox") / "philox_ref"
-    subprocess.run([hipcc, "-O1", str(HERE / "philox_rocrand_ref.cpp"), "-o", str(exe)], check=True,
-                   capture_output=True)
-
-    def run(seed, sub, count):
-        out = subprocess.run([str(exe), str(seed), str(sub), str(count)], check=True, capture_output=True, text=True)
-        return np.array([[int(w, 16) for w in line.split()] for line in out.stdout.splitlines()], np.uint32)
-    return run
-
-
 def test_philox_matches_rocrand(oracle, rocrand_philox):
     for seed, sub in [(0, 0), (4, 0), (0x123456789ABCDEF, 7), (2**64 - 1, 2**40 + 3)]:
         ref = rocrand_philox(seed, sub, 20)
@@ -262,75 +245,18 @@ def test_mxfp4_codes_are_nearest_grid_of_x_over_scale(oracle):
                 np.testing.assert_array_equal(unpack_codes(q["codes"])[r, 32 * b: 32 * b + 32], want)
 
 
-def _exact_sse(x, codes, eff):
-    return sum((Fraction(float(v)) * Fraction(float(eff)) - Fraction(float(xi))) ** 2
-               for v, xi in zip(e2m1_val(codes), x))
-
-
-def test_nvfp4_scale_and_codes(oracle):
+def test_block_holding_the_tensor_max_gets_448(oracle):
+    """S_t = T / (6 * 448) maps the block holding the tensor max to the largest
+    E4M3 scale (0x7E = 448); under 4/6 (T / (4 * 448)) its 4-candidate is
+    448. The scale and code decisions of every block are pinned in
+    test_oracle_decisions.py."""
     rng = np.random.default_rng(7)
     for scale in (1.0, 3e-3, 50.0):
         x = tiny_matrix(rng, 8, 64, scale)
-        q = oracle.quantize(x, oracle.NVFP4)
-        T = np.abs(x).max()
-        St = q["tensor_scale"]
-        assert abs(St * 2688.0 - T) <= 2e-7 * T
-        codes = unpack_codes(q["codes"])
-        for r in range(8):
-            for b in range(4):
-                blk = x[r, 16 * b: 16 * b + 16].astype(np.float64)
-                ideal = min(np.abs(blk).max() / (6.0 * St), 448.0)
-                c = q["scales"][r, b]
-                if c != torch_e4m3(np.array([ideal], np.float32))[0]:
-                    # only possible within float32 rounding of the ideal scale
-                    assert abs(torch_e4m3_value(np.array([c]))[0] - ideal) <= 0.07 * ideal
-                eff = np.float32(torch_e4m3_value(np.array([c]))[0]) * np.float32(St)
-                if eff < np.finfo(np.float32).tiny:
-                    assert (codes[r, 16 * b: 16 * b + 16] & 7 == 0).all()
-                    continue
-                exact_q = blk / float(eff)
-                want = brute_e2m1(exact_q.astype(np.float32))
-                got = codes[r, 16 * b: 16 * b + 16]
-                # fl(x * fl(1/eff)) may sit one rounding away from x / eff: only
-                # where x / eff is within 1e-6 of a rounding midpoint
-                mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
-                near = np.min(np.abs(np.abs(exact_q)[:, None] - mids[None, :]), axis=1) < 1e-6 * np.abs(exact_q)
-                assert ((got == want) | near).all()
-        # the block holding the tensor max gets the largest E4M3 scale
         r, cidx = np.unravel_index(np.argmax(np.abs(x)), x.shape)
-        assert q["scales"][r, cidx // 16] == 0x7E
-
-
-def test_four_over_six_picks_lower_exact_error(oracle):
-    rng = np.random.default_rng(8)
-    x = (rng.standard_normal((16, 64)) * np.exp(rng.uniform(-2, 2, (16, 1)))).astype(np.float32)
-    q46 = oracle.quantize(x, oracle.NVFP4, flags=oracle.FOUR_OVER_SIX)
-    St = q46["tensor_scale"]
-    assert abs(St * 1792.0 - np.abs(x).max()) <= 2e-7 * np.abs(x).max()
-    codes = unpack_codes(q46["codes"])
-    picked4 = 0
-    for r in range(16):
-        for b in range(4):
-            blk = x[r, 16 * b: 16 * b + 16]
-            a = float(np.abs(blk).max())
-            cand = {}
-            for M in (6, 4):
-                c = int(torch_e4m3(np.array([min(a / (M * St), 448.0)], np.float32))[0])
-                eff = np.float32(torch_e4m3_value(np.array([c]))[0]) * np.float32(St)
-                cc = brute_e2m1((blk.astype(np.float64) / float(eff)).astype(np.float32))
-                cand[M] = (c, _exact_sse(blk, cc, eff))
-            chosen = int(q46["scales"][r, b])
-            assert chosen in (cand[6][0], cand[4][0])
-            s4, s6 = cand[4][1], cand[6][1]
-            near_tie = abs(s4 - s6) <= Fraction(1, 10 ** 4) * s6
-            if not near_tie and cand[4][0] != cand[6][0]:
-                assert chosen == (cand[4][0] if s4 < s6 else cand[6][0]), (r, b)
-            picked4 += chosen == cand[4][0] and cand[4][0] != cand[6][0]
-            # the chosen candidate never has a larger error than the 6 candidate
-            eff_ch = np.float32(torch_e4m3_value(np.array([chosen]))[0]) * np.float32(St)
-            s_ch = _exact_sse(blk, codes[r, 16 * b: 16 * b + 16], eff_ch)
-            assert s_ch <= s6 * (1 + Fraction(1, 10 ** 4))
-    assert 0 < picked4 < 64  # both candidates occur on this input
+        assert oracle.quantize(x, oracle.NVFP4)["scales"][r, cidx // 16] == 0x7E
+        q46 = oracle.quantize(x, oracle.NVFP4, flags=oracle.FOUR_OVER_SIX)
+        assert q46["scales"][r, cidx // 16] in (0x7E, torch_e4m3(np.array([448.0 * 4 / 6], np.float32))[0])
 
 
 def test_four_over_six_never_worse_on_worked_example(oracle):
@@ -345,36 +271,15 @@ def test_four_over_six_never_worse_on_worked_example(oracle):
     assert ((d46 - x) ** 2).sum() <= ((d6 - x) ** 2).sum() * 1.01
 
 
-def test_mxfp4_four_over_six_picks_lower_exact_error(oracle):
-    """MXFP4 under 4/6: the scale exponent is the standard one e or e + 1,
-    whichever gives the smaller exact squared error (brute force over both,
-    in exact rationals); codes are then the nearest grid points of
-    x / 2^e'."""
-    rng = np.random.default_rng(31)
-    x = (rng.standard_normal((24, 96)) * np.exp(rng.uniform(-3, 3, (24, 1)))).astype(np.float32)
-    x[3, :32] *= 0.01
-    x[3, 5] = 7.5  # a block whose max clips under e (to 6; under e + 1 it rounds to 4 * 2)
-    q = oracle.quantize(x, oracle.MXFP4, flags=oracle.FOUR_OVER_SIX)
+def test_mxfp4_four_over_six_moves_a_clipped_block_up(oracle):
+    """A block whose max clips under the standard exponent e (7.5 * 2^e -> 6)
+    is better served by e + 1 (7.5 -> 4 * 2^(e+1) = 8 * 2^e); the exponent
+    pair of every block is pinned in test_oracle_decisions.py."""
+    x = np.full((1, 32), 0.01, np.float32)
+    x[0, 5] = 7.5
     plain = oracle.quantize(x, oracle.MXFP4)
-    codes = unpack_codes(q["codes"])
-    picked = 0
-    for r in range(24):
-        for b in range(3):
-            blk = x[r, 32 * b: 32 * b + 32]
-            e0 = int(plain["scales"][r, b]) - 127
-            sse = {}
-            for e in (e0, e0 + 1):
-                cc = brute_e2m1((blk.astype(np.float64) * 2.0 ** -e).astype(np.float32))
-                sse[e] = (_exact_sse(blk, cc, 2.0 ** e), cc)
-            e = int(q["scales"][r, b]) - 127
-            assert e in (e0, e0 + 1)
-            np.testing.assert_array_equal(codes[r, 32 * b: 32 * b + 32], sse[e][1])
-            s0, s1 = sse[e0][0], sse[e0 + 1][0]
-            if abs(s1 - s0) > Fraction(1, 10 ** 4) * s0:
-                assert e == (e0 + 1 if s1 < s0 else e0), (r, b)
-            picked += e == e0 + 1
-    assert 0 < picked < 72  # both exponents occur on this input
-    assert q["scales"][3, 0] - 127 == plain["scales"][3, 0] - 127 + 1  # the clipped block moves up
+    q = oracle.quantize(x, oracle.MXFP4, flags=oracle.FOUR_OVER_SIX)
+    assert int(q["scales"][0, 0]) == int(plain["scales"][0, 0]) + 1
 
 
 def test_mxfp4_four_over_six_never_worse(oracle):
@@ -390,56 +295,6 @@ def test_mxfp4_four_over_six_never_worse(oracle):
 def _qmx(oracle, x, flags):
     q = oracle.quantize(x, oracle.MXFP4, flags=flags)
     return {"codes": q["codes"], "scales": q["scales"]}
-
-
-@pytest.mark.parametrize("flags", [0, 2, 6])
-def test_scale_search_is_argmin_over_the_codes_between_4_and_6(oracle, flags):
-    """NVFP4 scale search: the chosen E4M3 code lies between the M = 6 and
-    M = 4 candidates' codes and has the smallest exact squared error among
-    all of them (brute force in exact rationals, skipping near-ties); the
-    search is never worse than 4/6, which is never worse than plain."""
-    rng = np.random.default_rng(32 + flags)
-    x = (rng.standard_normal((32, 64)) * np.exp(rng.uniform(-2, 2, (32, 64)))).astype(np.float32)
-    fl = oracle.SCALE_SEARCH | flags
-    q = oracle.quantize(x, oracle.NVFP4, flags=fl)
-    q46 = oracle.quantize(x, oracle.NVFP4, flags=oracle.FOUR_OVER_SIX | flags)
-    St = q["tensor_scale"]
-    assert St == q46["tensor_scale"]
-    tr = bool(flags & oracle.TRANSPOSE)
-    xs = x.T if tr else x  # the quantized orientation
-    codes = unpack_codes(q["codes"])
-    tile = 16 if flags & oracle.BLOCK2D else 1
-    widened = 0
-    for r0 in range(0, xs.shape[0], tile):
-        for b in range(xs.shape[1] // 16):
-            blk = xs[r0:r0 + tile, 16 * b: 16 * b + 16]
-            a = float(np.abs(blk).max())
-            lo = int(torch_e4m3(np.array([min(a / (6 * St), 448.0)], np.float32))[0])
-            hi = int(torch_e4m3(np.array([min(a / (4 * St), 448.0)], np.float32))[0])
-            chosen = int(q["scales"][r0, b])
-            assert lo <= chosen <= hi
-            sse = {}
-            for c in range(lo, hi + 1):
-                eff = np.float32(torch_e4m3_value(np.array([c]))[0]) * np.float32(St)
-                flat = blk.reshape(-1)
-                cc = brute_e2m1((flat.astype(np.float64) / float(eff)).astype(np.float32))
-                sse[c] = _exact_sse(flat, cc, eff)
-            best = min(sse.values())
-            runner = sorted(sse.values())[1] if len(sse) > 1 else None
-            if runner is None or runner - best > Fraction(1, 10 ** 4) * best:
-                assert sse[chosen] == best, (r0, b)
-            widened += chosen not in (lo, hi)
-            c46 = int(q46["scales"][r0, b])
-            assert sse[chosen] <= sse[c46] * (1 + Fraction(1, 10 ** 4))
-            for rr in range(r0, r0 + tile):
-                eff = np.float32(torch_e4m3_value(np.array([chosen]))[0]) * np.float32(St)
-                want = brute_e2m1((xs[rr, 16 * b: 16 * b + 16].astype(np.float64) / float(eff)).astype(np.float32))
-                got = codes[rr, 16 * b: 16 * b + 16]
-                mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
-                qq = np.abs(xs[rr, 16 * b: 16 * b + 16].astype(np.float64) / float(eff))
-                near = np.min(np.abs(qq[:, None] - mids[None, :]), axis=1) < 1e-6 * qq
-                assert ((got == want) | near).all()
-    assert widened > 0  # candidates strictly between 4 and 6 do win
 
 
 def _q(oracle, x, flags):
