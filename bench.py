@@ -1,24 +1,35 @@
 #!/usr/bin/env python3
 """Benchmark of the block-scaled FP4 hot path on one MI355X.
 
-A step is one pass of the workload's whole path over one batch of seeded
-synthetic input already resident in HBM. The default workload is the W4A4
-linear layer: NVFP4 four-over-six quantization of the activations
-[2048, 4096] and of the weight [4096, 4096] (each with its tensor-amax
-pre-pass), then the NVFP4 GEMM to a [2048, 4096] bf16 output.
+A step is one pass of a workload's whole path over one batch of seeded
+synthetic input already resident in HBM. The headline step (the default) is
+the random-Hadamard activation workload, the largest configuration:
+NVFP4 four-over-six quantization with the 16-point random Hadamard
+transform of the activations X [16384, 4096] and of the weight W [4096,
+12288] (quantized transposed), each with its tensor-amax pre-pass, then the
+NVFP4 GEMM 16384 x 12288 x 4096 to bf16. The same JSON line carries, under
+"workloads", the mixture-of-experts MXFP4 step (32 experts: W^T and X
+quantize, grouped GEMM 32 x 512 x 5760 x 2880), the training quantize step
+(8192^2 weight with 16 x 16 scales as-is and transposed, gradient with
+stochastic rounding) and the W4A4 linear step (2048 x 4096 x 4096), and under
+"worked_example" the codes, scales and MAE of the 4096-value example in the
+whole-tensor, MXFP4, NVFP4 and four-over-six modes.
 
 Timing: W untimed warm-up steps, then K steps between two device
 synchronisations, with HIP events (torch.cuda.Event on the stream the kernels
-run on) around the whole region and around every op inside it. Inputs rotate
-over enough copies (>= 600 MB) that the 256 MB Infinity Cache cannot serve
-them from one step to the next.
+run on) around every op; the step time is the average over replays of HIP
+graphs of the step. Inputs rotate over enough copies (>= 600 MB) that the
+256 MB Infinity Cache cannot serve them from one step to the next. Every
+NVFP4 quantize is also timed on its own with the tensor amax supplied
+(kernel-only), beside its end-to-end time with the pre-pass.
 
 Output: one JSON line. `value` is the step's roofline time (sum over its ops
 of algorithmic bytes / 8 TB/s for codec scans, flops / dense matrix peak for
 the GEMM) as a percentage of the measured step time. `roofline` describes the
 op that takes most of the step; `kernels` lists every op. `cpu_baseline`
-times the CPU oracle on a bounded sample of the same workload (single
-thread), scaled to the full step.
+times the CPU oracle, as it stands, on a bounded sample of the same workload,
+on one core and on all host cores (rows split over processes), scaled to the
+full step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME|all]
 """
@@ -29,8 +40,11 @@ import ctypes
 import hashlib
 import json
 import os
+import subprocess
 import sys
+import tempfile
 import time
+from dataclasses import dataclass, field
 from pathlib import Path
 
 import numpy as np
@@ -216,14 +230,107 @@ def copies(t, n):
     return [t] + [t.clone() for _ in range(n - 1)]
 
 
+
+
 # ---------------------------------------------------------------------------
 # workloads
 # ---------------------------------------------------------------------------
+@dataclass
+class QuantSample:
+    """A CPU-baseline sample of one quantize op: the oracle quantizes
+    `units` rows (axis 0) or columns (axis 1: a transposed quantize, whose
+    output rows are the source columns) of x; the time scales by
+    full_units / units to the whole op, batch items included."""
+    name: str
+    x: np.ndarray           # bf16 bit patterns (uint16) or float32
+    fmt: int
+    flags: int
+    axis: int
+    full_units: int
+    bytes_full: int
+    one: int                # units timed on one core
+    all: int                # units timed on all cores (split over processes)
+    signs: int = 0
+    seed: int = 0
+    offset: int = 0
+    step: int = 16          # units come in multiples of this (2D tiles, lane pairs)
+
+
+@dataclass
+class GemmSample:
+    """A CPU-baseline sample of one GEMM: the oracle's operands of m_s rows
+    of A and n_s rows of B (quantized untimed), then its dequantize (timed,
+    scaled by (M + N) / (m_s + n_s)) and its float64 matmul (timed, scaled
+    by M N / (m_s n_s)), times `groups`."""
+    name: str
+    a: np.ndarray           # A rows [>= m_s, K] (bf16 bits)
+    b: np.ndarray           # B as [N, K] rows, or [K, N] with b_transposed
+    b_transposed: bool
+    fmt: int
+    fa: int
+    fb: int
+    M: int
+    N: int
+    K: int
+    groups: int
+    one: tuple
+    all: tuple
+    signs: int = 0
+
+
+@dataclass
+class Workload:
+    ops: list
+    cfg: dict
+    dtype: str
+    cpu: list = field(default_factory=list)      # CPU-baseline samples
+    probes: list = field(default_factory=list)   # ops timed on their own, outside the step
+
+
+def sylvester16(device):
+    h = torch.ones(1, 1)
+    for _ in range(4):
+        h = torch.cat([torch.cat([h, h], 1), torch.cat([h, -h], 1)], 0)
+    return h.to(device)
+
+
+def probe_amax(x, hadamard=False, signs=0, along_columns=False):
+    """The tensor amax the quantizer's pre-pass finds (after the random
+    Hadamard transform along the block direction, if on), computed with
+    torch for the kernel-only timing of an NVFP4 quantize (the value only
+    sets the tensor scale; any positive amax does the same work)."""
+    xf = x.float()
+    if not hadamard:
+        return xf.abs().amax().reshape(1)
+    if along_columns:
+        xf = xf.t()
+    d = torch.tensor([-1.0 if (signs >> i) & 1 else 1.0 for i in range(16)], device=x.device)
+    m = (sylvester16(x.device) * d[None, :]) / 4.0
+    best = torch.zeros((), device=x.device)
+    rows = xf.shape[0]
+    for r in range(0, rows, 2048):
+        v = xf[r:r + 2048].contiguous().reshape(-1, 16) @ m.t()
+        best = torch.maximum(best, v.abs().amax())
+    return best.reshape(1)
+
+
+def bits(t):
+    """bf16 device/host tensor -> numpy uint16 bit patterns (host)."""
+    return t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def kernel_only(F, name, kernel, xs, fmt, flags, amax, signs=0, seed=0, offset=0):
+    q = QuantCall(F, xs, fmt, flags, signs=signs, seed=seed, offset=offset, amax=amax)
+    return Op(name + " (kernel only, amax supplied)", kernel, "hbm", q.bytes(), PEAK_HBM_GBS, q, "GB/s")
+
+
 def wl_w4a4_linear(F, inputs):
     d = inputs.w4a4_linear(device="cuda")
     n = n_sets(d["a"].numel() * 2 + d["w"].numel() * 2)
-    qa = QuantCall(F, copies(d["a"], n), F.FP4_NVFP4, F.FP4_FOUR_OVER_SIX)
-    qw = QuantCall(F, copies(d["w"], n), F.FP4_NVFP4, F.FP4_FOUR_OVER_SIX)
+    fos = F.FP4_FOUR_OVER_SIX
+    xa, xw = copies(d["a"], n), copies(d["w"], n)
+    qa = QuantCall(F, xa, F.FP4_NVFP4, fos)
+    qw = QuantCall(F, xw, F.FP4_NVFP4, fos)
     gm = GemmCall(F, qa, qw, torch.bfloat16)
     ops = [Op("quantize A nvfp4 4/6 (amax pre-pass + quantize)", "amax_kernel+quant_rows_kernel", "hbm", qa.bytes(),
               PEAK_HBM_GBS, qa, "GB/s"),
@@ -231,10 +338,16 @@ def wl_w4a4_linear(F, inputs):
               PEAK_HBM_GBS, qw, "GB/s"),
            Op("gemm nvfp4 (exact fp16 dequant + fp16 MFMA)", "gemm_fp4_kernel<true, 128, 4, 1, false>", "mfma",
               gm.flops(), PEAK_TFLOPS["f16"], gm, "TFLOP/s")]
+    probes = [kernel_only(F, "quantize A nvfp4 4/6", "quant_rows_kernel", xa, F.FP4_NVFP4, fos, probe_amax(d["a"])),
+              kernel_only(F, "quantize W nvfp4 4/6", "quant_rows_kernel", xw, F.FP4_NVFP4, fos, probe_amax(d["w"]))]
     cfg = {"workload": "w4a4_linear_nvfp4_four_over_six", "M": 2048, "N": 4096, "K": 4096,
            "activations": "2048x4096 bf16 N(0,1), 1% columns x30", "weight": "4096x4096 bf16 N(0,0.02)",
            "output": "bf16", "input_sets_rotated": n}
-    return ops, cfg, "fp4 e2m1 codes (nvfp4); f16 MFMA, f32 accumulate", lambda: cpu_w4a4(d)
+    a, w = bits(d["a"]), bits(d["w"])
+    cpu = [QuantSample("quantize A nvfp4 4/6", a, F.FP4_NVFP4, fos, 0, 2048, qa.bytes(), 512, 2048),
+           QuantSample("quantize W nvfp4 4/6", w, F.FP4_NVFP4, fos, 0, 4096, qw.bytes(), 512, 4096),
+           GemmSample("gemm nvfp4", a, w, False, F.FP4_NVFP4, fos, fos, 2048, 4096, 4096, 1, (128, 1024), (512, 4096))]
+    return Workload(ops, cfg, "fp4 e2m1 codes (nvfp4); f16 MFMA, f32 accumulate", cpu, probes)
 
 
 def wl_moe(F, inputs):
@@ -249,9 +362,18 @@ def wl_moe(F, inputs):
               PEAK_HBM_GBS, qx, "GB/s"),
            Op("grouped gemm mxfp4 (scaled FP4 MFMA)", "gemm_fp4_kernel<false, 256, 4, 1, false>", "mfma",
               gm.flops(), PEAK_TFLOPS["fp4"], gm, "TFLOP/s")]
-    cfg = {"workload": "moe_mxfp4_grouped", "experts": 32, "M": 512, "N": 5760, "K": 2880, "output": "bf16",
-           "input_sets_rotated": n}
-    return ops, cfg, "fp4 e2m1 codes (mxfp4); fp4 MFMA, f32 accumulate", None
+    cfg = {"workload": "moe_mxfp4_grouped_32x512x5760x2880", "experts": 32, "M": 512, "N": 5760, "K": 2880,
+           "output": "bf16", "input_sets_rotated": n}
+    # four experts' weights side by side as [K, 4 N] (their transposed
+    # quantize is the four experts' stacked), their tokens as [4 * 512, K]
+    w4 = bits(torch.cat([d["w"][e] for e in range(4)], dim=1))
+    x4 = bits(d["x"][:4].reshape(4 * 512, 2880))
+    cpu = [QuantSample("quantize W^T mxfp4", w4, F.FP4_MXFP4, F.FP4_TRANSPOSE, 1, 32 * 5760, qw.bytes(), 5760,
+                       4 * 5760),
+           QuantSample("quantize X mxfp4", x4, F.FP4_MXFP4, 0, 0, 32 * 512, qx.bytes(), 512, 2048),
+           GemmSample("grouped gemm mxfp4", x4[:512], w4[:, :5760], True, F.FP4_MXFP4, 0, F.FP4_TRANSPOSE, 512, 5760,
+                      2880, 32, (512, 2880), (512, 5760))]
+    return Workload(ops, cfg, "fp4 e2m1 codes (mxfp4); fp4 MFMA, f32 accumulate", cpu)
 
 
 def wl_training(F, inputs):
@@ -261,32 +383,60 @@ def wl_training(F, inputs):
     # after the first would be served from the 256 MB Infinity Cache
     ws, ws2, gs = copies(d["w"], n), copies(d["w"], n), copies(d["grad"], n)
     f = F.FP4_FOUR_OVER_SIX | F.FP4_BLOCK2D
+    fg = F.FP4_FOUR_OVER_SIX | F.FP4_STOCHASTIC
     q1 = QuantCall(F, ws, F.FP4_NVFP4, f)
     q2 = QuantCall(F, ws2, F.FP4_NVFP4, f | F.FP4_TRANSPOSE)
-    q3 = QuantCall(F, gs, F.FP4_NVFP4, F.FP4_FOUR_OVER_SIX | F.FP4_STOCHASTIC, seed=d["sr_seed"])
+    q3 = QuantCall(F, gs, F.FP4_NVFP4, fg, seed=d["sr_seed"])
     ops = [Op("quantize W nvfp4 2D 4/6", "quant_rows_kernel", "hbm", q1.bytes(), PEAK_HBM_GBS, q1, "GB/s", lane=1),
            Op("quantize W^T nvfp4 2D 4/6", "quant_cols_kernel", "hbm", q2.bytes(), PEAK_HBM_GBS, q2, "GB/s", lane=2),
            Op("quantize G nvfp4 4/6 stochastic", "quant_rows_kernel", "hbm", q3.bytes(),
               PEAK_HBM_GBS, q3, "GB/s", lane=3)]
-    cfg = {"workload": "training_quantize_8192", "shape": [8192, 8192], "input_sets_rotated": n}
-    return ops, cfg, "fp4 e2m1 codes (nvfp4), f32 scale arithmetic", None
+    aw, ag = probe_amax(d["w"]), probe_amax(d["grad"])
+    probes = [kernel_only(F, "quantize W nvfp4 2D 4/6", "quant_rows_kernel", ws, F.FP4_NVFP4, f, aw),
+              kernel_only(F, "quantize W^T nvfp4 2D 4/6", "quant_cols_kernel", ws2, F.FP4_NVFP4, f | F.FP4_TRANSPOSE,
+                          aw),
+              kernel_only(F, "quantize G nvfp4 4/6 stochastic", "quant_rows_kernel", gs, F.FP4_NVFP4, fg, ag,
+                          seed=d["sr_seed"])]
+    cfg = {"workload": "training_quantize_nvfp4_8192x8192", "shape": [8192, 8192], "input_sets_rotated": n}
+    w, g = bits(d["w"][:, :2048].contiguous()), bits(d["grad"][:1024])
+    wrows = bits(d["w"][:1024])
+    cpu = [QuantSample("quantize W nvfp4 2D 4/6", wrows, F.FP4_NVFP4, f, 0, 8192, q1.bytes(), 128, 1024),
+           QuantSample("quantize W^T nvfp4 2D 4/6", w, F.FP4_NVFP4, f | F.FP4_TRANSPOSE, 1, 8192, q2.bytes(), 128,
+                       2048),
+           QuantSample("quantize G nvfp4 4/6 stochastic", g, F.FP4_NVFP4, fg, 0, 8192, q3.bytes(), 128, 1024,
+                       seed=d["sr_seed"])]
+    return Workload(ops, cfg, "fp4 e2m1 codes (nvfp4), f32 scale arithmetic", cpu, probes)
 
 
 def wl_rht(F, inputs):
     d = inputs.rht_activation(device="cuda")
     n = n_sets(d["x"].numel() * 2 + d["w"].numel() * 2)
     f = F.FP4_FOUR_OVER_SIX | F.FP4_HADAMARD
-    qx = QuantCall(F, copies(d["x"], n), F.FP4_NVFP4, f, signs=d["signs"])
-    qw = QuantCall(F, copies(d["w"], n), F.FP4_NVFP4, f | F.FP4_TRANSPOSE, signs=d["signs"])
+    xs, wsets = copies(d["x"], n), copies(d["w"], n)
+    qx = QuantCall(F, xs, F.FP4_NVFP4, f, signs=d["signs"])
+    qw = QuantCall(F, wsets, F.FP4_NVFP4, f | F.FP4_TRANSPOSE, signs=d["signs"])
     gm = GemmCall(F, qx, qw, torch.bfloat16)
     ops = [Op("quantize X nvfp4 4/6 RHT", "quant_rows_kernel", "hbm", qx.bytes(), PEAK_HBM_GBS, qx, "GB/s", lane=1),
            Op("quantize W^T nvfp4 4/6 RHT", "quant_cols_kernel", "hbm", qw.bytes(), PEAK_HBM_GBS, qw, "GB/s", lane=2),
            Op("gemm nvfp4 (exact fp16 dequant + fp16 MFMA)", "gemm_fp4_kernel<true, 128, 4, 1, false>", "mfma",
               gm.flops(), PEAK_TFLOPS["f16"], gm, "TFLOP/s")]
-    cfg = {"workload": "rht_activation_nvfp4", "M": 16384, "N": 12288, "K": 4096, "input_sets_rotated": n}
-    return ops, cfg, "fp4 e2m1 codes (nvfp4); f16 MFMA, f32 accumulate", None
-
-
+    probes = [kernel_only(F, "quantize X nvfp4 4/6 RHT", "quant_rows_kernel", xs, F.FP4_NVFP4, f,
+                          probe_amax(d["x"], True, d["signs"]), signs=d["signs"]),
+              kernel_only(F, "quantize W^T nvfp4 4/6 RHT", "quant_cols_kernel", wsets, F.FP4_NVFP4,
+                          f | F.FP4_TRANSPOSE, probe_amax(d["w"], True, d["signs"], along_columns=True),
+                          signs=d["signs"])]
+    cfg = {"workload": "rht_activation_nvfp4_16384x12288x4096", "M": 16384, "N": 12288, "K": 4096,
+           "activations": "16384x4096 bf16 N(0,1) + 0.5% Student-t(2)", "weight": "4096x12288 bf16 N(0,0.02) as [K, N]",
+           "transform": "16-point random Hadamard, one sign mask for both operands", "output": "bf16",
+           "input_sets_rotated": n}
+    x, w = bits(d["x"][:8192]), bits(d["w"][:, :6144].contiguous())
+    cpu = [QuantSample("quantize X nvfp4 4/6 RHT", x, F.FP4_NVFP4, f, 0, 16384, qx.bytes(), 2048, 8192,
+                       signs=d["signs"]),
+           QuantSample("quantize W^T nvfp4 4/6 RHT", w, F.FP4_NVFP4, f | F.FP4_TRANSPOSE, 1, 12288, qw.bytes(), 1536,
+                       6144, signs=d["signs"]),
+           GemmSample("gemm nvfp4", x, w, True, F.FP4_NVFP4, f, f | F.FP4_TRANSPOSE, 16384, 12288, 4096, 1,
+                      (512, 1536), (2048, 6144), signs=d["signs"])]
+    return Workload(ops, cfg, "fp4 e2m1 codes (nvfp4); f16 MFMA, f32 accumulate", cpu, probes)
 def wl_training_backward(F, inputs):
     """Backward GEMMs of a quantized linear Y = X W^T (dgrad, wgrad), each with
     its operands' quantization: dX = Q(dY) Q(W^T)^T with the weight's 2D
@@ -317,7 +467,7 @@ def wl_training_backward(F, inputs):
     cfg = {"workload": "training_backward_nvfp4_8192", "M": 8192, "N": 8192, "K": 8192,
            "gradient": "8192x8192 bf16 Laplace(0,1e-3)", "weight": "8192x8192 bf16 N(0,0.02)",
            "activations": "8192x8192 bf16 N(0,1)", "output": "bf16", "input_sets_rotated": n}
-    return ops, cfg, "fp4 e2m1 codes (nvfp4); f16 MFMA, f32 accumulate", None
+    return Workload(ops, cfg, "fp4 e2m1 codes (nvfp4); f16 MFMA, f32 accumulate")
 
 
 def wl_w4a4_fused(F, inputs):
@@ -343,7 +493,7 @@ def wl_w4a4_fused(F, inputs):
     cfg = {"workload": "w4a4_linear_nvfp4_fused_output_quantize", "M": 2048, "N": 4096, "K": 4096,
            "activations": "2048x4096 bf16 N(0,1), 1% columns x30", "weight": "4096x4096 bf16 N(0,0.02)",
            "output": "nvfp4 4/6 codes + scales, amax supplied", "input_sets_rotated": n}
-    return ops, cfg, "fp4 e2m1 codes (nvfp4); f16 MFMA, f32 accumulate", None
+    return Workload(ops, cfg, "fp4 e2m1 codes (nvfp4); f16 MFMA, f32 accumulate")
 
 
 def wl_w4a4_unfused_chain(F, inputs):
@@ -371,7 +521,7 @@ def wl_w4a4_unfused_chain(F, inputs):
     cfg = {"workload": "w4a4_linear_nvfp4_unfused_output_quantize", "M": 2048, "N": 4096, "K": 4096,
            "activations": "2048x4096 bf16 N(0,1), 1% columns x30", "weight": "4096x4096 bf16 N(0,0.02)",
            "output": "bf16 C, then nvfp4 4/6 codes + scales, amax supplied", "input_sets_rotated": n}
-    return ops, cfg, "fp4 e2m1 codes (nvfp4); f16 MFMA, f32 accumulate", None
+    return Workload(ops, cfg, "fp4 e2m1 codes (nvfp4); f16 MFMA, f32 accumulate")
 
 
 def wl_scale_search(F, inputs):
@@ -392,7 +542,7 @@ def wl_scale_search(F, inputs):
               PEAK_HBM_GBS, qm, "GB/s", lane=3)]
     cfg = {"workload": "scale_search_8192", "shape": [8192, 8192], "weight": "8192x8192 bf16 N(0,0.02)",
            "input_sets_rotated": n}
-    return ops, cfg, "fp4 e2m1 codes, f32 scale arithmetic", None
+    return Workload(ops, cfg, "fp4 e2m1 codes, f32 scale arithmetic")
 
 
 def wl_moe_routed(F, inputs):
@@ -414,44 +564,172 @@ def wl_moe_routed(F, inputs):
     cfg = {"workload": "moe_mxfp4_routed", "experts": 32, "tokens": 4096, "top_k": 4, "rows": int(d["offsets"][-1]),
            "rows_per_expert": [int(v) for v in d["counts"]], "N": 5760, "K": 2880, "output": "bf16",
            "input_sets_rotated": n}
-    return ops, cfg, "fp4 e2m1 codes (mxfp4); fp4 MFMA, f32 accumulate", None
+    return Workload(ops, cfg, "fp4 e2m1 codes (mxfp4); fp4 MFMA, f32 accumulate")
 
 
-WORKLOADS = {"w4a4_linear": wl_w4a4_linear, "moe": wl_moe, "training": wl_training, "rht": wl_rht,
+
+WORKLOADS = {"rht": wl_rht, "moe": wl_moe, "training": wl_training, "w4a4_linear": wl_w4a4_linear,
              "training_backward": wl_training_backward, "moe_routed": wl_moe_routed, "w4a4_fused": wl_w4a4_fused,
              "w4a4_unfused_chain": wl_w4a4_unfused_chain, "scale_search": wl_scale_search}
+# the configurations the default line carries beside the headline step
+EXTRA_WORKLOADS = ("moe", "training", "w4a4_linear")
+# the ones given a CPU baseline in the default line (the two speed targets)
+CPU_WORKLOADS = ("rht", "moe")
 
 
 # ---------------------------------------------------------------------------
-# CPU baseline: the oracle, untuned, single thread, bounded sample
+# CPU baseline: the oracle as it stands, on one core and on all host cores
 # ---------------------------------------------------------------------------
-def cpu_w4a4(d):
+def host_cores():
+    """Cores this process may run on, at most 16 (the machine's CPU share per GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def cpu_model():
+    try:
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def split(units, parts, step):
+    """units (a multiple of step) into `parts` ranges of whole steps."""
+    chunks = units // step
+    parts = max(1, min(parts, chunks))
+    bounds = [step * (chunks * i // parts) for i in range(parts + 1)]
+    return [(bounds[i], bounds[i + 1]) for i in range(parts) if bounds[i + 1] > bounds[i]]
+
+
+def cpu_quantize(s: QuantSample, units, workers, tmp):
+    """Seconds the oracle takes to quantize `units` of the sample, the units
+    split over `workers` concurrent processes (span of their oracle calls)."""
+    path = Path(tmp) / f"{abs(hash(s.name))}.npy"
+    if not path.exists():
+        np.save(path, s.x)
+    procs = []
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
+    for i, (a, b) in enumerate(split(units, workers, s.step)):
+        task = Path(tmp) / f"task_{i}.json"
+        task.write_text(json.dumps({"input": str(path), "fmt": s.fmt, "flags": s.flags, "signs": s.signs,
+                                    "seed": s.seed, "offset": s.offset, "axis": s.axis, "start": a, "stop": b}))
+        procs.append(subprocess.Popen([sys.executable, str(ROOT / "oracle" / "cpu_worker.py"), str(task)],
+                                      stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, env=env))
+    spans = []
+    for p in procs:
+        out, err = p.communicate()
+        if p.returncode != 0:
+            raise RuntimeError(f"cpu_worker failed: {err[-2000:]}")
+        spans.append(json.loads(out.strip().splitlines()[-1]))
+    return max(t["t1"] for t in spans) - min(t["t0"] for t in spans), len(procs)
+
+
+def cpu_gemm(g: GemmSample, m_s, n_s, threads):
+    """Oracle dequantize of m_s rows of A and n_s rows of B, then the
+    reference matmul (float64, the BLAS limited to `threads`); seconds
+    scaled to the whole GEMM."""
     from threadpoolctl import threadpool_limits
 
-    from block_scaled_fp4_amax_amd import inputs
     from oracle import oracle as O
-    a = inputs.bf16_bits(d["a"].cpu())
-    w = inputs.bf16_bits(d["w"].cpu())
-    M, K = a.shape
-    N = w.shape[0]
-    rows = 1024
-    with threadpool_limits(limits=1):
+    qa = O.quantize(np.ascontiguousarray(g.a[:m_s]), g.fmt, flags=g.fa, rht_signs=g.signs)
+    bsrc = np.ascontiguousarray(g.b[:, :n_s] if g.b_transposed else g.b[:n_s])
+    qb = O.quantize(bsrc, g.fmt, flags=g.fb, rht_signs=g.signs)
+    with threadpool_limits(limits=threads):
         t0 = time.perf_counter()
-        qa = O.quantize(a, O.NVFP4, flags=O.FOUR_OVER_SIX)
+        da = O.dequantize(g.fmt, qa["codes"], qa["scales"], qa["tensor_scale"])
+        db = O.dequantize(g.fmt, qb["codes"], qb["scales"], qb["tensor_scale"])
         t1 = time.perf_counter()
-        qw = O.quantize(w, O.NVFP4, flags=O.FOUR_OVER_SIX)
+        O.gemm_reference(da, db)
         t2 = time.perf_counter()
-        da = O.dequantize(O.NVFP4, qa["codes"][:rows], qa["scales"][:rows], qa["tensor_scale"])
-        dw = O.dequantize(O.NVFP4, qw["codes"], qw["scales"], qw["tensor_scale"])
-        O.gemm_reference(da, dw)
-        t3 = time.perf_counter()
-    t_step = (t1 - t0) + (t2 - t1) + (t3 - t2) * (M / rows)
-    return {"seconds_measured": t3 - t0, "step_seconds_extrapolated": t_step,
-            "sample": f"oracle NVFP4 4/6 quantize of all of A [{M},{K}] and W [{N},{K}] "
-                      f"(incl. tensor amax), dequantize + float64 matmul of {rows} of {M} output rows, "
-                      f"scaled by {M // rows} to the full GEMM",
-            "quantize_GBps": (quant_bytes(M * K, 2, 16, True) + quant_bytes(N * K, 2, 16, True)) / (t2 - t0) / 1e9,
-            "gemm_GFLOPs": 2.0 * rows * N * K / (t3 - t2) / 1e9}
+    full = g.groups * ((t1 - t0) * (g.M + g.N) / (m_s + n_s) + (t2 - t1) * (g.M * g.N) / (m_s * n_s))
+    return full, t2 - t0
+
+
+def cpu_baseline(wl: Workload, roof_s):
+    """Both legs of the CPU baseline of a workload's step."""
+    from oracle import oracle as O
+    O.lib()  # built once here, before any worker loads it
+    cores = host_cores()
+    legs = {}
+    with tempfile.TemporaryDirectory(prefix="fp4_cpu_") as tmp:
+        for leg, workers in (("one_core", 1), ("all_cores", cores)):
+            ops, total, measured, used = [], 0.0, 0.0, 1
+            for s in wl.cpu:
+                if isinstance(s, QuantSample):
+                    units = s.one if workers == 1 else s.all
+                    t, n = cpu_quantize(s, units, workers, tmp)
+                    full = t * s.full_units / units
+                    used = max(used, n)
+                    ops.append({"op": s.name, "sample": f"{units} of {s.full_units} "
+                                f"{'source columns' if s.axis else 'rows'}", "seconds": round(t, 3),
+                                "full_seconds": round(full, 3), "GBps": round(s.bytes_full / full / 1e9, 5)})
+                else:
+                    m_s, n_s = s.one if workers == 1 else s.all
+                    full, t = cpu_gemm(s, m_s, n_s, workers)
+                    used = max(used, workers)
+                    flops = 2.0 * s.groups * s.M * s.N * s.K
+                    ops.append({"op": s.name, "sample": f"{m_s} x {n_s} of {s.M} x {s.N} outputs"
+                                f"{f' (one of {s.groups} groups)' if s.groups > 1 else ''}, K {s.K}",
+                                "seconds": round(t, 3), "full_seconds": round(full, 3),
+                                "TFLOPs": round(flops / full / 1e12, 6)})
+                total += full
+                measured += t
+            legs[leg] = {"value": round(100.0 * roof_s / total, 6), "cores": used,
+                         "step_seconds": round(total, 3), "measured_seconds": round(measured, 3), "ops": ops}
+    a = legs["all_cores"]
+    return {"value": a["value"], "unit": "% of roofline (step)", "cores": a["cores"], "kind": "oracle",
+            "sample": "; ".join(f"{o['op']}: {o['sample']}" for o in a["ops"]) + "; each scaled to the full op",
+            "cpu_model": cpu_model(), "step_seconds": a["step_seconds"], "measured_seconds": a["measured_seconds"],
+            "ops": a["ops"], "one_core": legs["one_core"]}
+
+
+# ---------------------------------------------------------------------------
+# the worked example: codes, scales and MAE in every mode
+# ---------------------------------------------------------------------------
+def sha(a):
+    return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()[:16]
+
+
+def worked_example_record(F, inputs):
+    """The 4096-value example ("FP4" glossary, "Como funciona FP4") in the
+    whole-tensor, MXFP4, NVFP4 and NVFP4 four-over-six modes, on the GPU:
+    digests of the codes, scale bytes and tensor scale, and the MAE of the
+    dequantized tensor; beside them, as this configuration's CPU baseline,
+    the oracle's, and the page's printed MAE of its float-scale modes."""
+    from oracle import oracle as O
+    x = inputs.worked_example().reshape(1, 4096)
+    xd = x.cuda()
+    modes = {"whole_tensor": (F.FP4_NVFP4, F.FP4_TENSOR_SCALE), "mxfp4": (F.FP4_MXFP4, 0),
+             "nvfp4": (F.FP4_NVFP4, 0), "nvfp4_four_over_six": (F.FP4_NVFP4, F.FP4_FOUR_OVER_SIX)}
+    out = {"workload": "worked_example_4096", "input": "4096 fp32 N(0,1), seed 0, every 512th x20", "modes": {}}
+    xn = x.numpy().astype(np.float64)
+    for name, (fmt, fl) in modes.items():
+        q = F.quantize(xd, fmt, four_over_six=bool(fl & F.FP4_FOUR_OVER_SIX),
+                       tensor_scale=bool(fl & F.FP4_TENSOR_SCALE))
+        deq = F.dequantize(q).cpu().numpy().astype(np.float64)
+        codes, scales = q.codes.cpu().numpy(), q.scales.cpu().numpy()
+        ts = q.tensor_scale.cpu().numpy() if q.tensor_scale is not None else np.zeros(0, np.float32)
+        gpu = {"codes_sha256": sha(codes), "scales_sha256": sha(scales), "tensor_scale": [float(v) for v in ts],
+               "mae": float(np.abs(deq - xn).mean())}
+        r = O.quantize(x.numpy(), fmt, flags=fl)
+        od = O.dequantize(fmt, r["codes"], r["scales"], r["tensor_scale"]).astype(np.float64)
+        ots = np.array([r["tensor_scale"]], np.float32) if r["tensor_scale"] is not None else np.zeros(0, np.float32)
+        orc = {"codes_sha256": sha(r["codes"]), "scales_sha256": sha(r["scales"]),
+               "tensor_scale": [float(v) for v in ots], "mae": float(np.abs(od - xn).mean())}
+        out["modes"][name] = {"gpu": gpu, "oracle": orc,
+                              "bit_exact": bool(np.array_equal(codes, r["codes"]) and np.array_equal(scales, r["scales"])
+                                                and np.array_equal(ts.view(np.uint32), ots.view(np.uint32)))}
+    gold = json.loads((ROOT / "tests" / "golden" / "worked_example.json").read_text())
+    out["page_printed_mae_float_scale"] = {f"block_{k}": v for k, v in gold["mae"].items()}
+    out["oracle_float_scale_mae"] = {f"block_{b}": float(np.abs(O.float_scale_dequant(x.numpy()[0], b) - xn[0]).mean())
+                                     for b in (4096, 32, 16)}
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -613,12 +891,11 @@ def graph_step_ms(ops, steps, warmup):
     return t0.elapsed_time(t1) / steps
 
 
-def run(workload, steps, warmup, with_cpu):
-    import block_scaled_fp4_amax_amd as F
-    from block_scaled_fp4_amax_amd import inputs
-    F.lib()
-    torch.manual_seed(0)
-    ops, cfg, dtype, cpu_fn = WORKLOADS[workload](F, inputs)
+
+
+def time_ops(ops, steps, warmup):
+    """Eager timing: every op of every step between HIP events on its
+    stream; returns the per-op durations (ms) and the whole eager step."""
     torch.cuda.synchronize()
     for i in range(warmup):
         for op in ops:
@@ -636,43 +913,56 @@ def run(workload, steps, warmup, with_cpu):
             evs[i][j][1].record()
     t_end.record()
     torch.cuda.synchronize()
-    ms_step_eager = t_start.elapsed_time(t_end) / steps
-    ms_step = graph_step_ms(ops, steps, warmup)
-    kernels = []
-    roof_s = 0.0
-    for j, op in enumerate(ops):
-        d = [evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(steps)]
-        avg_ms = float(np.mean(d))
-        achieved = op.work / (avg_ms * 1e-3) / (1e9 if op.unit == "GB/s" else 1e12)
-        traffic = traffic_for(op.kernel, workload)
-        kernels.append({"op": op.name, "kernel": op.kernel, "bound": op.bound, "avg_ms": round(avg_ms, 5),
-                        "achieved": round(achieved, 2), "peak": op.peak, "unit": op.unit,
-                        "frac": round(achieved / op.peak, 4), "work_per_launch": op.work,
-                        "traffic": traffic})
-        roof_s += op.roofline_seconds()
+    per_op = [[evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(steps)] for j in range(len(ops))]
+    return per_op, t_start.elapsed_time(t_end) / steps
+
+
+def op_record(op, durations, workload):
+    avg_ms = float(np.mean(durations))
+    achieved = op.work / (avg_ms * 1e-3) / (1e9 if op.unit == "GB/s" else 1e12)
+    return {"op": op.name, "kernel": op.kernel, "bound": op.bound, "avg_ms": round(avg_ms, 5),
+            "achieved": round(achieved, 2), "peak": op.peak, "unit": op.unit, "frac": round(achieved / op.peak, 4),
+            "work_per_launch": op.work, "traffic": traffic_for(op.kernel, workload)}
+
+
+def run(workload, steps, warmup, with_cpu):
+    import block_scaled_fp4_amax_amd as F
+    from block_scaled_fp4_amax_amd import inputs
+    F.lib()
+    torch.manual_seed(0)
+    wl = WORKLOADS[workload](F, inputs)
+    per_op, ms_step_eager = time_ops(wl.ops, steps, warmup)
+    ms_step = graph_step_ms(wl.ops, steps, warmup)
+    kernels = [op_record(op, d, workload) for op, d in zip(wl.ops, per_op)]
+    roof_s = sum(op.roofline_seconds() for op in wl.ops)
+    probes = []
+    if wl.probes:
+        per_probe, _ = time_ops(wl.probes, steps, warmup)
+        probes = [op_record(op, d, workload) for op, d in zip(wl.probes, per_probe)]
     dom = max(kernels, key=lambda k: k["avg_ms"])
     value = 100.0 * roof_s / (ms_step * 1e-3)
     line = {"metric": METRIC, "value": round(value, 2), "unit": "% of roofline (step)", "n_gpus": 1,
             "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 5),
             "ms_per_step_eager": round(ms_step_eager, 5), "launch": "hip graph per step (one per input set)",
             "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": dtype,
-            "data": "synthetic (seeded generators; no dataset or trained weights)", "config": cfg,
+            "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+            "data": "synthetic (seeded generators; no dataset or trained weights)", "config": wl.cfg,
             "roofline": {"bound": dom["bound"], "achieved": dom["achieved"], "peak": dom["peak"],
                          "unit": dom["unit"], "frac": dom["frac"], "traffic": dom["traffic"],
                          "kernel": dom["kernel"]},
+            "step_roofline_ms": round(roof_s * 1e3, 5),
             "kernels": kernels}
-    if with_cpu and cpu_fn is not None:
-        c = cpu_fn()
-        line["cpu_baseline"] = {"value": round(100.0 * roof_s / c["step_seconds_extrapolated"], 6),
-                                "unit": "% of roofline (step)", "cores": 1, "kind": "oracle",
-                                "sample": c["sample"], "step_seconds": round(c["step_seconds_extrapolated"], 3),
-                                "quantize_GBps": round(c["quantize_GBps"], 4),
-                                "gemm_GFLOPs": round(c["gemm_GFLOPs"], 3),
-                                "host": f"{os.cpu_count()} logical CPUs visible"}
-    else:
-        line["cpu_baseline"] = None
+    if probes:
+        line["kernels_amax_supplied"] = probes
+    line["cpu_baseline"] = cpu_baseline(wl, roof_s) if with_cpu and wl.cpu else None
+    del wl
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     return line
+
+
+SUB_KEYS = ("config", "value", "ms_per_step", "ms_per_step_eager", "step_roofline_ms", "roofline", "kernels",
+            "kernels_amax_supplied", "cpu_baseline")
 
 
 def main():
@@ -680,7 +970,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="w4a4_linear", choices=[*WORKLOADS, "all"])
+    ap.add_argument("--workload", default="default", choices=["default", *WORKLOADS, "all"],
+                    help="default: the headline step with the other configurations in the same line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (HBM counter calibration)")
@@ -703,10 +994,23 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
         return
+    with_cpu = not args.no_cpu_baseline
+    if args.workload == "default":
+        import block_scaled_fp4_amax_amd as F
+        from block_scaled_fp4_amax_amd import inputs
+        line = run("rht", args.steps, args.warmup, with_cpu)
+        print(f"# headline step done: {line['ms_per_step']} ms", file=sys.stderr, flush=True)
+        line["workloads"] = {}
+        for nm in EXTRA_WORKLOADS:
+            sub = run(nm, args.steps, args.warmup, with_cpu and nm in CPU_WORKLOADS)
+            line["workloads"][sub["config"]["workload"]] = {k: sub[k] for k in SUB_KEYS if k in sub}
+            print(f"# {nm} step done: {sub['ms_per_step']} ms", file=sys.stderr, flush=True)
+        line["worked_example"] = worked_example_record(F, inputs)
+        print(json.dumps(line), flush=True)
+        return
     names = list(WORKLOADS) if args.workload == "all" else [args.workload]
     for nm in names:
-        line = run(nm, args.steps, args.warmup, with_cpu=not args.no_cpu_baseline)
-        print(json.dumps(line), flush=True)
+        print(json.dumps(run(nm, args.steps, args.warmup, with_cpu)), flush=True)
 
 
 if __name__ == "__main__":

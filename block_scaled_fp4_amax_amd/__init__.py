@@ -48,6 +48,7 @@ FP4_TRANSPOSE = 4
 FP4_STOCHASTIC = 8
 FP4_HADAMARD = 16
 FP4_SCALE_SEARCH = 32
+FP4_TENSOR_SCALE = 64
 
 EXPORTED_SYMBOLS = ("fp4_quantize_workspace", "fp4_quantize", "fp4_quantize_noalloc", "fp4_dequantize", "fp4_gemm",
                     "fp4_gemm_grouped", "fp4_gemm_quantize_output", "fp4_status_str")
@@ -249,9 +250,10 @@ def _check(status: int, where: str):
 
 
 def quantize(x, fmt="nvfp4", *, four_over_six=False, block2d=False, transpose=False, stochastic=False,
-             hadamard=False, scale_search=False, rht_signs=0, seed=0, offset=0, amax=None,
+             hadamard=False, scale_search=False, tensor_scale=False, rht_signs=0, seed=0, offset=0, amax=None,
              stream=None) -> Quantized:
-    """Quantize a [rows, cols] or [batch, rows, cols] bf16/fp32 device tensor."""
+    """Quantize a [rows, cols] or [batch, rows, cols] bf16/fp32 device tensor
+    (tensor_scale: the NVFP4 whole-tensor mode, FP4_TENSOR_SCALE)."""
     import torch
     fmt = _fmt(fmt)
     squeeze = x.dim() == 2
@@ -263,7 +265,8 @@ def quantize(x, fmt="nvfp4", *, four_over_six=False, block2d=False, transpose=Fa
     dt = {torch.bfloat16: FP4_BF16, torch.float32: FP4_F32}[x3.dtype]
     flags = ((FP4_FOUR_OVER_SIX if four_over_six else 0) | (FP4_BLOCK2D if block2d else 0)
              | (FP4_TRANSPOSE if transpose else 0) | (FP4_STOCHASTIC if stochastic else 0)
-             | (FP4_HADAMARD if hadamard else 0) | (FP4_SCALE_SEARCH if scale_search else 0))
+             | (FP4_HADAMARD if hadamard else 0) | (FP4_SCALE_SEARCH if scale_search else 0)
+             | (FP4_TENSOR_SCALE if tensor_scale else 0))
     amax_t = None
     if amax is not None:
         amax_t = torch.as_tensor(amax, dtype=torch.float32, device=x3.device).reshape(-1).contiguous()

@@ -17,7 +17,7 @@ static_assert(FP4_NOALLOC_SCRATCH_BYTES == kNoAllocScratchBytes, "the header sta
 namespace {
 
 constexpr uint32_t kKnownFlags =
-    FP4_FOUR_OVER_SIX | FP4_BLOCK2D | FP4_TRANSPOSE | FP4_STOCHASTIC | FP4_HADAMARD | FP4_SCALE_SEARCH;
+    FP4_FOUR_OVER_SIX | FP4_BLOCK2D | FP4_TRANSPOSE | FP4_STOCHASTIC | FP4_HADAMARD | FP4_SCALE_SEARCH | FP4_TENSOR_SCALE;
 constexpr int64_t kMaxGridYZ = 65535;
 constexpr int64_t kMaxGridX = 2147483647;
 // fp4_gemm_grouped: every tile scans the group offsets 64 at a time
@@ -83,7 +83,9 @@ fp4_status plan_quantize(int64_t batch, int64_t rows, int64_t cols, const fp4_qu
   if (o->flags & ~kKnownFlags) return FP4_ERR_INVALID;
   if (batch < 0 || rows < 0 || cols < 0) return FP4_ERR_INVALID;
   const bool nv = o->format == FP4_NVFP4;
-  if (!nv && (o->flags & (FP4_BLOCK2D | FP4_SCALE_SEARCH))) return FP4_ERR_UNSUPPORTED;
+  if (!nv && (o->flags & (FP4_BLOCK2D | FP4_SCALE_SEARCH | FP4_TENSOR_SCALE))) return FP4_ERR_UNSUPPORTED;
+  if ((o->flags & FP4_TENSOR_SCALE) && (o->flags & (FP4_FOUR_OVER_SIX | FP4_SCALE_SEARCH | FP4_BLOCK2D)))
+    return FP4_ERR_UNSUPPORTED;
   if ((o->flags & FP4_BLOCK2D) && (o->flags & FP4_HADAMARD) && (o->flags & FP4_TRANSPOSE)) return FP4_ERR_UNSUPPORTED;
   const bool tr = o->flags & FP4_TRANSPOSE;
   p->blk = nv ? 16 : 32;
@@ -388,7 +390,7 @@ fp4_status fp4_gemm_quantize_output(int32_t format, int64_t groups, int64_t M, i
   if (out_opts->format != FP4_MXFP4 && out_opts->format != FP4_NVFP4) return FP4_ERR_INVALID;
   if (out_opts->flags & ~kKnownFlags) return FP4_ERR_INVALID;
   const bool qnv = out_opts->format == FP4_NVFP4;
-  if (out_opts->flags & (FP4_BLOCK2D | FP4_TRANSPOSE)) return FP4_ERR_UNSUPPORTED;
+  if (out_opts->flags & (FP4_BLOCK2D | FP4_TRANSPOSE | FP4_TENSOR_SCALE)) return FP4_ERR_UNSUPPORTED;
   if (!qnv && (out_opts->flags & FP4_SCALE_SEARCH)) return FP4_ERR_UNSUPPORTED;
   if (groups < 0 || M < 0 || N < 0 || K < 0) return FP4_ERR_INVALID;
   const int64_t qblk = qnv ? 16 : 32;

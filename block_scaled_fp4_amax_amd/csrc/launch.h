@@ -14,6 +14,7 @@ enum Flags : uint32_t {
   kStochastic = 8u,
   kHadamard = 16u,
   kScaleSearch = 32u,
+  kTensorScale = 64u,
 };
 
 struct QuantArgs {

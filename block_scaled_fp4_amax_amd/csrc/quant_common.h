@@ -16,7 +16,9 @@
 //      [4, 8) or in [2, 4)), by the same squared error with the 4^e factor
 //      cancelled (e + 1 wins iff 4 S_{e+1} < S_e);
 //   2  NVFP4 scale search: every E4M3 code from the M = 6 candidate's to the
-//      M = 4 candidate's, smallest error wins, ties keep the smaller code.
+//      M = 4 candidate's, smallest error wins, ties keep the smaller code;
+//   3  NVFP4 whole-tensor scale: every block scale is E4M3 1.0 (code 0x38)
+//      and S_t = T / 6, so the tensor max maps to 6.
 #pragma once
 
 #include "fp4_device.h"
@@ -26,6 +28,7 @@ namespace fp4impl {
 using namespace fp4dev;
 
 constexpr float kInf = __builtin_huge_valf();
+constexpr uint32_t kUnitScaleCode = 0x38u;  // E4M3 1.0
 
 // One NVFP4 scale candidate: effective block scale eff = E4M3(code) * S_t and
 // its correctly rounded reciprocal. eff below the smallest normal makes the
@@ -190,6 +193,16 @@ __device__ __forceinline__ void quantize_unit(const float v[16], const NvConsts&
       w1 = e2m1_pack2_scaled<3>(w1, v[14], v[15], sc);
     }
   } else {
+    if constexpr (SEL == 3) {
+      const NvCand c = nv_code_candidate<TAB>(kUnitScaleCode, nc);
+      float q[16];
+#pragma unroll
+      for (int i = 0; i < 16; i++) q[i] = v[i] * c.r;
+      if constexpr (SR) sr16(q, L0, seed, offset, w0, w1);
+      else pack16(q, w0, w1);
+      sbyte = c.code;
+      return;
+    }
     if constexpr (B2D) {
       amax = __builtin_fmaxf(amax, xor_shfl<1>(amax));
       amax = __builtin_fmaxf(amax, xor_shfl<2>(amax));
@@ -264,12 +277,19 @@ __device__ __forceinline__ void quantize_unit(const float v[16], const NvConsts&
   }
 }
 
+// Divisor D of the tensor scale S_t = T / D for scale selection mode SEL:
+// 6 * 448 (plain), 4 * 448 (4/6 and the scale search: the M = 4 candidate of
+// the block holding T does not saturate E4M3), 6 (whole-tensor scale).
+template <int SEL>
+constexpr float tensor_divisor() {
+  return SEL == 0 ? 2688.0f : SEL == 3 ? 6.0f : 1792.0f;
+}
+
 // NVFP4 tensor scale for batch item b, computed identically by every
 // workgroup: T from amax_in or the max of the pre-pass partials; S_t = T / D
-// with D = 6 * 448 (4 * 448 under 4/6 and the scale search: FOS), replaced
-// by 1 when zero, denormal or not finite. The item's first workgroup (first)
-// stores S_t.
-template <bool FOS>
+// (tensor_divisor), replaced by 1 when zero, denormal or not finite. The
+// item's first workgroup (first) stores S_t.
+template <int SEL>
 __device__ __forceinline__ float tensor_scale_prologue(const QuantArgs& a, int64_t b, bool first) {
   __shared__ float red[4];
   float T;
@@ -297,7 +317,7 @@ __device__ __forceinline__ float tensor_scale_prologue(const QuantArgs& a, int64
     __syncthreads();
     T = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
   }
-  float St = T / (FOS ? 1792.0f : 2688.0f);
+  float St = T / tensor_divisor<SEL>();
   if (!(St >= kFltMin && St <= 3.40282347e38f)) St = 1.0f;
   if (first && threadIdx.x == 0) a.tensor_scale[b] = St;
   return St;
@@ -305,12 +325,12 @@ __device__ __forceinline__ float tensor_scale_prologue(const QuantArgs& a, int64
 
 // S_t (tensor_scale_prologue) and the workgroup's NvConsts; every thread of
 // the (256-thread) workgroup takes part.
-template <bool FOS>
+template <int SEL>
 __device__ __forceinline__ NvConsts nv_prologue(const QuantArgs& a, int64_t b, bool first) {
   __shared__ float rtab[128];
   __shared__ float kk[2];
   NvConsts nc;
-  nc.St = tensor_scale_prologue<FOS>(a, b, first);
+  nc.St = tensor_scale_prologue<SEL>(a, b, first);
   const int t = threadIdx.x;
   if (t < 128) {
     const float eff = e4m3_decode((uint32_t)t) * nc.St;

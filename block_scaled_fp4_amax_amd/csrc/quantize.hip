@@ -219,7 +219,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(QuantArgs a) {
   if (valid) raw.load(reinterpret_cast<const TIn*>(a.x) + b * a.bs_x + row * a.ld_x + cu * 16);
 
   NvConsts nc{};
-  if constexpr (NV) nc = nv_prologue<SEL != 0>(a, b, blockIdx.x == 0 && blockIdx.y == 0);  // every lane takes part
+  if constexpr (NV) nc = nv_prologue<SEL>(a, b, blockIdx.x == 0 && blockIdx.y == 0);  // every lane takes part
   if (!valid) return;
 
   float v[16];
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(QuantArgs a) {
   Patch16x8<TIn> t;
   if (valid) t.load(reinterpret_cast<const TIn*>(a.x) + b * a.bs_x + k0 * a.ld_x + n0, a.ld_x);
   NvConsts nc{};
-  if constexpr (NV) nc = nv_prologue<SEL != 0>(a, b, nb == 0 && kb == 0);  // while the loads are in flight
+  if constexpr (NV) nc = nv_prologue<SEL>(a, b, nb == 0 && kb == 0);  // while the loads are in flight
   if (valid) {
     const uint64_t Lrow = (uint64_t)b * (uint64_t)a.R;
     uint8_t* crow = cst + nl * kColsPitch + (kl >> 1);
@@ -483,7 +483,8 @@ static void launch_typed(const QuantArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(amax_finalize_kernel, dim3((unsigned)a.batch), dim3(256), 0, s, a);
     q.amax_in = q.partials + q.batch * q.nparts;
   }
-  if (q.flags & kScaleSearch) launch_nv_sel<TIn, 2>(q, s);
+  if (q.flags & kTensorScale) launch_sr_rht<TIn, true, 3, false>(q, s);  // one scale: no 2D
+  else if (q.flags & kScaleSearch) launch_nv_sel<TIn, 2>(q, s);
   else if (q.flags & kFourOverSix) launch_nv_sel<TIn, 1>(q, s);
   else launch_nv_sel<TIn, 0>(q, s);
 }

@@ -95,7 +95,14 @@ enum {
    * wins, ties keep the smaller code. Tensor scale as under 4/6 (D = 4 *
    * 448); takes precedence over FP4_FOUR_OVER_SIX. (The pages' theme of
    * choosing the scale by error, "Four Over Six", introduction.) */
-  FP4_SCALE_SEARCH = 32u
+  FP4_SCALE_SEARCH = 32u,
+  /* NVFP4 layout with one scale for the whole tensor: every block-scale byte
+   * is 0x38 (E4M3 1.0) and S_t = T / 6, so each value is quantized against
+   * T / 6 alone, the whole-tensor scaling of the worked example ("FP4",
+   * "Como funciona FP4": the block is the whole tensor, its max maps to 6).
+   * Dequantize and fp4_gemm read it as any NVFP4 tensor. Not with
+   * FP4_FOUR_OVER_SIX, FP4_SCALE_SEARCH or FP4_BLOCK2D (FP4_ERR_UNSUPPORTED). */
+  FP4_TENSOR_SCALE = 64u
 };
 
 typedef struct fp4_quant_opts {
@@ -143,8 +150,8 @@ size_t fp4_quantize_workspace(int64_t batch, int64_t rows, int64_t cols, const f
  *
  * NVFP4 tensor scale: T = max |x| over the batch item (after the Hadamard
  * transform, if on) or amax_in[b]; S_t = T / (6 * 448), or T / (4 * 448)
- * under FP4_FOUR_OVER_SIX or FP4_SCALE_SEARCH; S_t = 1 when that is zero,
- * denormal or not finite.
+ * under FP4_FOUR_OVER_SIX or FP4_SCALE_SEARCH, or T / 6 under
+ * FP4_TENSOR_SCALE; S_t = 1 when that is zero, denormal or not finite.
  */
 fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t batch, int64_t rows, int64_t cols,
                         int64_t ld_x, int64_t batch_stride_x, const fp4_quant_opts* opts,

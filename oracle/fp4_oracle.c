@@ -202,7 +202,8 @@ enum {
   OR_TRANSPOSE = 4u,
   OR_STOCHASTIC = 8u,
   OR_HADAMARD = 16u,
-  OR_SCALE_SEARCH = 32u
+  OR_SCALE_SEARCH = 32u,
+  OR_TENSOR_SCALE = 64u
 };
 
 static float load_elem(const void* x, int dtype, int64_t idx) {
@@ -257,7 +258,8 @@ float or_tensor_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64
  * M = 4 candidate of that block does not saturate. If S_t is zero, denormal or
  * not finite, S_t = 1 (the tensor then quantizes to zeros). */
 float or_nvfp4_tensor_scale(float amax, int four_over_six) {
-  float D = four_over_six ? 1792.0f : 2688.0f;
+  /* four_over_six = 2: the whole-tensor mode below, D = 6 */
+  float D = four_over_six == 2 ? 6.0f : (four_over_six ? 1792.0f : 2688.0f);
   float s = amax / D;
   if (!(s >= FLT_MIN) || !(s <= FLT_MAX)) s = 1.0f;
   return s;
@@ -364,7 +366,13 @@ int or_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld
   int fos = nv && (o->flags & OR_FOUR_OVER_SIX);
   int b2d = nv && (o->flags & OR_BLOCK2D);
   int sr = (o->flags & OR_STOCHASTIC) != 0;
-  if (!nv && (o->flags & (OR_BLOCK2D | OR_SCALE_SEARCH))) return -1;
+  /* Whole-tensor scale ([FP4] "Como funciona FP4": the worked example's
+   * first mode, one scale for the whole tensor that maps its max to 6): kept
+   * in the NVFP4 layout with every block's E4M3 scale at 1.0, and S_t = T / 6
+   * (a reading: the pages store no format for it). */
+  int whole = nv && (o->flags & OR_TENSOR_SCALE);
+  if (!nv && (o->flags & (OR_BLOCK2D | OR_SCALE_SEARCH | OR_TENSOR_SCALE))) return -1;
+  if (whole && (o->flags & (OR_FOUR_OVER_SIX | OR_SCALE_SEARCH | OR_BLOCK2D))) return -1;
   int64_t R, C;
   float* w = working_matrix(x, dtype, rows, cols, ld, o->flags, o->rht_signs, &R, &C);
   if (!w) return -1;
@@ -436,7 +444,7 @@ int or_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld
     for (int64_t i = 0; i < R * C; i++)
       if (fabsf(w[i]) > T) T = fabsf(w[i]);
   }
-  float S_t = or_nvfp4_tensor_scale(T, fos || search);
+  float S_t = or_nvfp4_tensor_scale(T, whole ? 2 : (fos || search));
   if (tensor_scale) *tensor_scale = S_t;
   if (amax_out) *amax_out = T;
 
@@ -452,7 +460,9 @@ int or_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld
 
       nv_cand c6 = nv_candidate(a, 6.0f, S_t);
       nv_cand chosen = c6;
-      if (search) {
+      if (whole) {
+        chosen = nv_code_candidate(0x38, S_t); /* E4M3 1.0: eff = S_t = T / 6 */
+      } else if (search) {
         /* The 4/6 choice widened to every E4M3 scale between the two: the
          * candidates are the codes from the M = 6 candidate's up to the
          * M = 4 candidate's, so the block max maps to each representable

@@ -50,7 +50,7 @@ LIB = HERE / "liboracle.so"
 
 MXFP4, NVFP4 = 0, 1
 F32, BF16 = 0, 1
-FOUR_OVER_SIX, BLOCK2D, TRANSPOSE, STOCHASTIC, HADAMARD, SCALE_SEARCH = 1, 2, 4, 8, 16, 32
+FOUR_OVER_SIX, BLOCK2D, TRANSPOSE, STOCHASTIC, HADAMARD, SCALE_SEARCH, TENSOR_SCALE = 1, 2, 4, 8, 16, 32, 64
 
 CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
 
@@ -176,8 +176,8 @@ def rht16(v, signs: int) -> np.ndarray:
     return a
 
 
-def nvfp4_tensor_scale(amax: float, four_over_six: bool) -> float:
-    return lib().or_nvfp4_tensor_scale(amax, int(bool(four_over_six)))
+def nvfp4_tensor_scale(amax: float, four_over_six: bool, whole_tensor: bool = False) -> float:
+    return lib().or_nvfp4_tensor_scale(amax, 2 if whole_tensor else int(bool(four_over_six)))
 
 
 # --- tensors ----------------------------------------------------------------

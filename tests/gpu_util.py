@@ -5,7 +5,7 @@ import torch
 
 from block_scaled_fp4_amax_amd import inputs
 
-FLAG_NAMES = {1: "fos", 2: "b2d", 4: "tr", 8: "sr", 16: "rht", 32: "search"}
+FLAG_NAMES = {1: "fos", 2: "b2d", 4: "tr", 8: "sr", 16: "rht", 32: "search", 64: "tensor"}
 
 
 def flag_str(flags):
@@ -40,7 +40,7 @@ def oracle_quantize(O, x: torch.Tensor, fmt, flags=0, signs=0, seed=0, offset=0,
 def gpu_quantize(F, x_dev: torch.Tensor, fmt, flags=0, signs=0, seed=0, offset=0, amax=None):
     q = F.quantize(x_dev, fmt, four_over_six=bool(flags & 1), block2d=bool(flags & 2), transpose=bool(flags & 4),
                    stochastic=bool(flags & 8), hadamard=bool(flags & 16), scale_search=bool(flags & 32),
-                   rht_signs=signs, seed=seed, offset=offset, amax=amax)
+                   tensor_scale=bool(flags & 64), rht_signs=signs, seed=seed, offset=offset, amax=amax)
     torch.cuda.synchronize()
     codes = q.codes.cpu().numpy()
     scales = q.scales.cpu().numpy()

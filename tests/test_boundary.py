@@ -58,12 +58,16 @@ def test_quantize_option_errors(fp4):
     bad.size = 8
     assert q(fp4, bad) == fp4.FP4_ERR_INVALID
     assert q(fp4, fp4.make_opts(7)) == fp4.FP4_ERR_INVALID
-    assert q(fp4, fp4.make_opts(fp4.FP4_NVFP4, flags=64)) == fp4.FP4_ERR_INVALID
     assert q(fp4, fp4.make_opts(fp4.FP4_MXFP4, flags=fp4.FP4_SCALE_SEARCH)) == fp4.FP4_ERR_UNSUPPORTED
     assert q(fp4, fp4.make_opts(fp4.FP4_MXFP4, flags=fp4.FP4_BLOCK2D)) == fp4.FP4_ERR_UNSUPPORTED
     f = fp4.FP4_BLOCK2D | fp4.FP4_HADAMARD | fp4.FP4_TRANSPOSE
     assert q(fp4, fp4.make_opts(fp4.FP4_NVFP4, flags=f)) == fp4.FP4_ERR_UNSUPPORTED
     assert q(fp4, o, dt=5) == fp4.FP4_ERR_INVALID
+    ts = fp4.FP4_TENSOR_SCALE
+    assert q(fp4, fp4.make_opts(fp4.FP4_MXFP4, flags=ts)) == fp4.FP4_ERR_UNSUPPORTED
+    for other in (fp4.FP4_FOUR_OVER_SIX, fp4.FP4_SCALE_SEARCH, fp4.FP4_BLOCK2D):
+        assert q(fp4, fp4.make_opts(fp4.FP4_NVFP4, flags=ts | other)) == fp4.FP4_ERR_UNSUPPORTED
+    assert q(fp4, fp4.make_opts(fp4.FP4_NVFP4, flags=128)) == fp4.FP4_ERR_INVALID
 
 
 def test_quantize_shape_errors(fp4):
@@ -237,7 +241,8 @@ def test_gemm_quantize_output_errors(fp4):
     for f in (fp4.FP4_BLOCK2D, fp4.FP4_TRANSPOSE):
         assert gq(fp4, fp4.make_opts(fp4.FP4_NVFP4, flags=f, amax_in=FAKE)) == fp4.FP4_ERR_UNSUPPORTED
     assert gq(fp4, fp4.make_opts(fp4.FP4_MXFP4, flags=fp4.FP4_SCALE_SEARCH)) == fp4.FP4_ERR_UNSUPPORTED
-    assert gq(fp4, fp4.make_opts(fp4.FP4_NVFP4, flags=64, amax_in=FAKE)) == fp4.FP4_ERR_INVALID
+    assert gq(fp4, fp4.make_opts(fp4.FP4_NVFP4, flags=128, amax_in=FAKE)) == fp4.FP4_ERR_INVALID
+    assert gq(fp4, fp4.make_opts(fp4.FP4_NVFP4, flags=fp4.FP4_TENSOR_SCALE, amax_in=FAKE)) == fp4.FP4_ERR_UNSUPPORTED
     assert gq(fp4, mx, fmt=3) == fp4.FP4_ERR_INVALID                               # operand format
     assert gq(fp4, mx, M=0) == fp4.FP4_OK
 

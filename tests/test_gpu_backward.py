@@ -113,9 +113,11 @@ def test_full_dgrad(oracle, full_inputs):
     rows, cols = sample(m, rng), sample(k, rng)
     qg, dg = operand(oracle, d["grad"], FOS | SR, G_OFFSET, rows=rows)
     qwt, dwt = operand(oracle, d["w"], FOS | B2D | TR, rows=cols)
-    dx = F.gemm(qg, qwt, torch.bfloat16)
-    torch.cuda.synchronize()
-    check_product(oracle, dx, dg, dwt, torch.bfloat16, "dgrad 8192^3", rows, cols)
+    for out in (torch.bfloat16, torch.float32):
+        dx = F.gemm(qg, qwt, out)
+        torch.cuda.synchronize()
+        check_product(oracle, dx, dg, dwt, out, f"dgrad 8192^3 {out}", rows, cols)
+        del dx
 
 
 def test_full_wgrad(oracle, full_inputs):
@@ -127,6 +129,8 @@ def test_full_wgrad(oracle, full_inputs):
     rows, cols = sample(n, rng), sample(k, rng)
     qgt, dgt = operand(oracle, d["grad"], FOS | SR | TR, GT_OFFSET, rows=rows)
     qxt, dxt = operand(oracle, d["x"], FOS | TR, rows=cols)
-    dw = F.gemm(qgt, qxt, torch.bfloat16)
-    torch.cuda.synchronize()
-    check_product(oracle, dw, dgt, dxt, torch.bfloat16, "wgrad 8192^3", rows, cols)
+    for out in (torch.bfloat16, torch.float32):
+        dw = F.gemm(qgt, qxt, out)
+        torch.cuda.synchronize()
+        check_product(oracle, dw, dgt, dxt, out, f"wgrad 8192^3 {out}", rows, cols)
+        del dw

@@ -104,7 +104,8 @@ def test_router_offsets_computed_on_device(oracle):
 
 def test_full_moe_routed(oracle):
     """The benchmark's shape: 32 experts, 4096 tokens routed top-4 (16384
-    rows), K 2880, N 5760, MXFP4, bf16 out; sampled rows and columns."""
+    rows), K 2880, N 5760, MXFP4, bf16 and fp32 out; sampled rows and
+    columns."""
     d = inputs.moe_routed()
     print(f"[grouped-full] counts={d['counts'].tolist()}", flush=True)
     rng = np.random.default_rng(3)
@@ -114,7 +115,8 @@ def test_full_moe_routed(oracle):
     qa, da = oracle_operand(oracle, d["x"], MX, 0)
     qb, db = oracle_operand(oracle, d["w"], MX, TR, rows=cols)
     a = F.Quantized(MX, qa.codes[0], qa.scales[0], None)
-    c = F.gemm_grouped(a, qb, d["offsets"].cuda(), torch.bfloat16)
-    torch.cuda.synchronize()
     da = da[0]
-    check_groups(oracle, c, da, db, d["offsets"], torch.bfloat16, "moe routed", rows=rows, cols=cols)
+    for out in (torch.bfloat16, torch.float32):
+        c = F.gemm_grouped(a, qb, d["offsets"].cuda(), out)
+        torch.cuda.synchronize()
+        check_groups(oracle, c, da, db, d["offsets"], out, f"moe routed {out}", rows=rows, cols=cols)

@@ -12,12 +12,13 @@ from gpu_util import (assert_codes_equal, flag_str, gpu_quantize, mixed_matrix, 
 pytestmark = pytest.mark.gpu
 
 MX, NV = 0, 1
-FOS, B2D, TR, SR, RHT, SEARCH = 1, 2, 4, 8, 16, 32
+FOS, B2D, TR, SR, RHT, SEARCH, TS = 1, 2, 4, 8, 16, 32, 64
 
 
 def valid_combos():
     """Every flag set the API accepts: MXFP4 without 2D or the scale search;
-    NVFP4 without 2D + Hadamard + transpose; the search in place of 4/6."""
+    NVFP4 without 2D + Hadamard + transpose; the search in place of 4/6; the
+    whole-tensor scale without 4/6, the search or 2D."""
     out = []
     for f in range(32):
         if f & B2D == 0:
@@ -26,6 +27,8 @@ def valid_combos():
             out.append((NV, f))
             if f & FOS == 0:
                 out.append((NV, f | SEARCH))
+        if not f & (FOS | B2D):
+            out.append((NV, f | TS))
     return out
 
 
@@ -99,7 +102,7 @@ def test_padded_input_pitch(fp4, oracle, fmt, flags):
 
 def test_worked_example_all_modes(fp4, oracle):
     x = inputs.worked_example().reshape(1, 4096)
-    for fmt, flags in [(MX, 0), (NV, 0), (NV, FOS)]:
+    for fmt, flags in [(MX, 0), (NV, 0), (NV, FOS), (NV, TS)]:
         q = check(fp4, oracle, x, fmt, flags, what="worked-example")
         deq = fp4.dequantize(q).cpu().numpy()
         r = oracle.quantize(x.numpy(), fmt, flags=flags)

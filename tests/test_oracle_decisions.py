@@ -262,3 +262,18 @@ def test_mxfp4_exponent_pair_is_the_exact_argmin(oracle):
     got = unpack(q["codes"]).reshape(-1, 32).astype(np.int64)
     np.testing.assert_array_equal(got & 7, want)
     np.testing.assert_array_equal(got >> 3, np.signbit(blocks).astype(np.int64))
+
+
+def test_whole_tensor_scale_codes_are_nearest(oracle):
+    """Whole-tensor scale (every block scale 1.0, S_t = T / 6): S_t is the
+    correctly rounded T / 6 and every code the nearest E2M1 value of x / S_t,
+    outside the float32 rounding band, on 10^5 blocks."""
+    rng = np.random.default_rng(43)
+    x = make_input(rng, 4000, 400, 1, 16, lo=-2, hi=2)
+    q = oracle.quantize(x, NV, flags=64)
+    St = np.float32(q["tensor_scale"])
+    assert correctly_rounded_f32(St, Fraction(float(np.abs(x).max())) / 6)
+    assert (q["scales"] == 0x38).all()
+    blocks = as_blocks(x, 1)
+    chosen = np.full(len(blocks), 0x38, np.int64)
+    assert check_codes(blocks, as_blocks(unpack(q["codes"]), 1).astype(np.int64), chosen, St) < 1e-3

@@ -94,6 +94,25 @@ def test_worked_example_mae(oracle):
         assert round(mae, gold["printed_decimals"]) == want, (block, mae)
 
 
+def test_whole_tensor_mode_gives_the_pages_mae(oracle):
+    """The NVFP4 layout with every block scale at 1.0 and S_t = T / 6 is the
+    worked example's whole-tensor scaling: its dequantized tensor equals the
+    float-scale mode's with one block of 4096, element for element, and its
+    MAE is the printed whole-tensor value; S_t is the correctly rounded T / 6."""
+    from fractions import Fraction
+    gold = json.loads((HERE / "golden" / "worked_example.json").read_text())
+    x = inputs.worked_example().numpy().reshape(1, 4096)
+    q = oracle.quantize(x, oracle.NVFP4, flags=oracle.TENSOR_SCALE)
+    assert (q["scales"] == 0x38).all()
+    T = Fraction(float(np.abs(x).max()))
+    st = np.float32(q["tensor_scale"])
+    for nb in (np.nextafter(st, np.float32(np.inf)), np.nextafter(st, np.float32(0))):
+        assert abs(Fraction(float(st)) - T / 6) <= abs(Fraction(float(nb)) - T / 6)
+    d = oracle.dequantize(oracle.NVFP4, q["codes"], q["scales"], q["tensor_scale"])
+    np.testing.assert_array_equal(d[0], oracle.float_scale_dequant(x, 4096))
+    assert round(float(np.abs(d.astype(np.float64) - x).mean()), gold["printed_decimals"]) == gold["mae"]["4096"]
+
+
 def test_worked_example_generator_is_the_pages_seeding():
     torch.manual_seed(0)
     x = torch.randn(4096)
