@@ -104,7 +104,7 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const uint8_t* base, uint32_t bytes
 // inline assembly so that the compiler, which cannot match the copies in
 // flight to the stage slots, adds no vmcnt waits of its own before LDS reads:
 // every wait on these copies is explicit below. The instruction has no output
-// register; m0 is not otherwise used by this kernel.
+// register; m0, which it writes, is declared clobbered.
 __device__ __forceinline__ void b2l16(const i32x4& rsrc, uint32_t voff, uint32_t lds) {
   asm volatile(
       "s_mov_b32 m0, %2\n\t"
@@ -112,7 +112,7 @@ __device__ __forceinline__ void b2l16(const i32x4& rsrc, uint32_t voff, uint32_t
       "buffer_load_dwordx4 %0, %1, 0 offen lds"
       :
       : "v"(voff), "s"(rsrc), "s"(lds)
-      : "memory");
+      : "memory", "m0");
 }
 // Scalar (wave-uniform) fp32 load, completed inside the statement. A vector
 // load here would make the compiler wait for every copy in flight before

@@ -67,60 +67,98 @@ int amax_partials(int64_t src_rows, int64_t src_cols, uint32_t flags) {
   return (int)p;
 }
 
+// Position (r, c) of a unit in a grid of per_row units per row, advanced by
+// a fixed number of units with an add and a compare instead of a division.
+struct UnitPos {
+  int64_t r, c;
+  __device__ __forceinline__ void init(int64_t u, int64_t per_row) {
+    r = u / per_row;
+    c = u - r * per_row;
+  }
+  __device__ __forceinline__ void advance(int64_t dq, int64_t dr, int64_t per_row) {
+    r += dq;
+    c += dr;
+    if (c >= per_row) {
+      c -= per_row;
+      r++;
+    }
+  }
+};
+
+// Grid-stride over the units of one batch item, NU units per lane per step
+// (units u, u + stride, ..., u + (NU - 1) stride), so that every lane has
+// NU units' loads in flight before it reduces any of them.
 template <typename TIn, int MODE>
 __global__ __launch_bounds__(256) void amax_kernel(QuantArgs a) {
   const int64_t b = blockIdx.y;
   const TIn* x = reinterpret_cast<const TIn*>(a.x) + b * a.bs_x;
   const int64_t rows = a.src_rows, cols = a.src_cols;
-  int64_t per_row, units;
-  if (MODE == kAmaxPlain) { per_row = cols / 8; units = rows * per_row; }
-  else if (MODE == kAmaxRhtRows) { per_row = cols / 16; units = rows * per_row; }
-  else { per_row = cols / 8; units = (rows / 16) * per_row; }
-  float m = 0.0f;
+  // plain: 8 values of a row; RHT rows: one 16-value slice of a row; RHT
+  // columns: 16 rows x 8 columns (eight slices down the columns)
+  const int64_t per_row = MODE == kAmaxRhtRows ? cols / 16 : cols / 8;
+  const int64_t unit_rows = MODE == kAmaxRhtCols ? rows / 16 : rows;
+  constexpr int NU = MODE == kAmaxRhtCols ? 1 : (MODE == kAmaxRhtRows ? 4 : (sizeof(TIn) == 2 ? 8 : 4));
   const int64_t stride = (int64_t)gridDim.x * 256;
-  if constexpr (MODE == kAmaxPlain) {
-    // four 16-byte loads in flight per lane
-    for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < units; u += 4 * stride) {
-      float v[4][8];
+  UnitPos pos[NU];
+  pos[0].init((int64_t)blockIdx.x * 256 + threadIdx.x, per_row);
+  const int64_t sq = stride / per_row, sr = stride - sq * per_row;
 #pragma unroll
-      for (int k = 0; k < 4; k++) {
-        const int64_t uk = u + k * stride;
-        if (uk < units) {
-          const int64_t r = uk / per_row, c = uk - r * per_row;
-          load8<TIn>(x + r * a.ld_x + c * 8, v[k]);
+  for (int k = 1; k < NU; k++) {
+    pos[k] = pos[k - 1];
+    pos[k].advance(sq, sr, per_row);
+  }
+  const int64_t step = (int64_t)NU * stride;
+  const int64_t dq = step / per_row, dr = step - dq * per_row;
+  float m = 0.0f;
+  // units run in order, so every unit of a step lies past pos[0]
+  while (pos[0].r < unit_rows) {
+    if constexpr (MODE == kAmaxPlain) {
+      float v[NU][8];
+#pragma unroll
+      for (int k = 0; k < NU; k++) {
+        if (pos[k].r < unit_rows) {
+          load8<TIn>(x + pos[k].r * a.ld_x + pos[k].c * 8, v[k]);
         } else {
 #pragma unroll
           for (int i = 0; i < 8; i++) v[k][i] = 0.0f;
         }
       }
 #pragma unroll
-      for (int k = 0; k < 4; k++)
+      for (int k = 0; k < NU; k++)
 #pragma unroll
         for (int i = 0; i < 8; i++) m = __builtin_fmaxf(m, __builtin_fabsf(v[k][i]));
-    }
-  } else {
-    for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < units; u += stride) {
-      const int64_t r = u / per_row, c = u - r * per_row;
-      if constexpr (MODE == kAmaxRhtRows) {
-        float v[16];
-        load8<TIn>(x + r * a.ld_x + c * 16, v);
-        load8<TIn>(x + r * a.ld_x + c * 16 + 8, v + 8);
-        rht16(v, a.signs);
-        m = __builtin_fmaxf(m, max_abs16(v));
-      } else {
-        float t[16][8];
+    } else if constexpr (MODE == kAmaxRhtRows) {
+      float v[NU][16];
 #pragma unroll
-        for (int i = 0; i < 16; i++) load8<TIn>(x + (r * 16 + i) * a.ld_x + c * 8, t[i]);
+      for (int k = 0; k < NU; k++) {
+        if (pos[k].r < unit_rows) {
+          load8<TIn>(x + pos[k].r * a.ld_x + pos[k].c * 16, v[k]);
+          load8<TIn>(x + pos[k].r * a.ld_x + pos[k].c * 16 + 8, v[k] + 8);
+        } else {
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
-          float v[16];
-#pragma unroll
-          for (int i = 0; i < 16; i++) v[i] = t[i][j];
-          rht16(v, a.signs);
-          m = __builtin_fmaxf(m, max_abs16(v));
+          for (int i = 0; i < 16; i++) v[k][i] = 0.0f;
         }
       }
+#pragma unroll
+      for (int k = 0; k < NU; k++) {
+        rht16(v[k], a.signs);
+        m = __builtin_fmaxf(m, max_abs16(v[k]));
+      }
+    } else {
+      float t[16][8];
+#pragma unroll
+      for (int i = 0; i < 16; i++) load8<TIn>(x + (pos[0].r * 16 + i) * a.ld_x + pos[0].c * 8, t[i]);
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; i++) v[i] = t[i][j];
+        rht16(v, a.signs);
+        m = __builtin_fmaxf(m, max_abs16(v));
+      }
     }
+#pragma unroll
+    for (int k = 0; k < NU; k++) pos[k].advance(dq, dr, per_row);
   }
   m = __builtin_fmaxf(m, xor_shfl<32>(m));
   m = __builtin_fmaxf(m, xor_shfl<16>(m));
