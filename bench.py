@@ -126,6 +126,19 @@ class QuantCall:
         return self.F.Quantized(self.fmt, self.codes, self.scales, self.ts if self.nv else None)
 
 
+def gemm_kernel_label(nv, G, M, N, K, out_kind, routed=False):
+    """The gemm_fp4_kernel instantiation that fp4_gemm launches, by the tile
+    rule of launch_gemm in csrc/gemm.hip: 256-wide tiles when they still give
+    every compute unit a tile (for NVFP4 only from K = 2048 and with a plain
+    output), else 128-wide. The label only keys the kernel in profiles."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    mt = (M + 255) // 256 * (1 if routed else G)
+    wide = (N + 255) // 256 * mt >= cus
+    bn = 256 if wide and out_kind < 2 and (not nv or K >= 2048) else 128
+    b = lambda v: "true" if v else "false"
+    return f"gemm_fp4_kernel<{b(nv)}, {bn}, 4, {out_kind}, {b(routed)}>"
+
+
 class GemmCall:
     def __init__(self, F, qa, qb, out_dtype=torch.bfloat16):
         self.F, self.lib = F, F.lib()
@@ -152,6 +165,10 @@ class GemmCall:
 
     def flops(self):
         return 2.0 * self.G * self.M * self.N * self.K
+
+    def kernel(self):
+        return gemm_kernel_label(self.a.fmt == self.F.FP4_NVFP4, self.G, self.M, self.N, self.K,
+                                 1 if self.ct == self.F.FP4_BF16 else 0)
 
 
 class GemmQuantizeOutputCall:
@@ -336,7 +353,7 @@ def wl_w4a4_linear(F, inputs):
               PEAK_HBM_GBS, qa, "GB/s"),
            Op("quantize W nvfp4 4/6 (amax pre-pass + quantize)", "amax_kernel+quant_rows_kernel", "hbm", qw.bytes(),
               PEAK_HBM_GBS, qw, "GB/s"),
-           Op("gemm nvfp4 (exact fp16 dequant + fp16 MFMA)", "gemm_fp4_kernel<true, 128, 4, 1, false>", "mfma",
+           Op("gemm nvfp4 (exact fp16 dequant + fp16 MFMA)", gm.kernel(), "mfma",
               gm.flops(), PEAK_TFLOPS["f16"], gm, "TFLOP/s")]
     probes = [kernel_only(F, "quantize A nvfp4 4/6", "quant_rows_kernel", xa, F.FP4_NVFP4, fos, probe_amax(d["a"])),
               kernel_only(F, "quantize W nvfp4 4/6", "quant_rows_kernel", xw, F.FP4_NVFP4, fos, probe_amax(d["w"]))]
@@ -360,7 +377,7 @@ def wl_moe(F, inputs):
               PEAK_HBM_GBS, qw, "GB/s"),
            Op("quantize X mxfp4 32x[512x2880]", "quant_rows_kernel", "hbm", qx.bytes(),
               PEAK_HBM_GBS, qx, "GB/s"),
-           Op("grouped gemm mxfp4 (scaled FP4 MFMA)", "gemm_fp4_kernel<false, 256, 4, 1, false>", "mfma",
+           Op("grouped gemm mxfp4 (scaled FP4 MFMA)", gm.kernel(), "mfma",
               gm.flops(), PEAK_TFLOPS["fp4"], gm, "TFLOP/s")]
     cfg = {"workload": "moe_mxfp4_grouped_32x512x5760x2880", "experts": 32, "M": 512, "N": 5760, "K": 2880,
            "output": "bf16", "input_sets_rotated": n}
@@ -418,7 +435,7 @@ def wl_rht(F, inputs):
     gm = GemmCall(F, qx, qw, torch.bfloat16)
     ops = [Op("quantize X nvfp4 4/6 RHT", "quant_rows_kernel", "hbm", qx.bytes(), PEAK_HBM_GBS, qx, "GB/s", lane=1),
            Op("quantize W^T nvfp4 4/6 RHT", "quant_cols_kernel", "hbm", qw.bytes(), PEAK_HBM_GBS, qw, "GB/s", lane=2),
-           Op("gemm nvfp4 (exact fp16 dequant + fp16 MFMA)", "gemm_fp4_kernel<true, 128, 4, 1, false>", "mfma",
+           Op("gemm nvfp4 (exact fp16 dequant + fp16 MFMA)", gm.kernel(), "mfma",
               gm.flops(), PEAK_TFLOPS["f16"], gm, "TFLOP/s")]
     probes = [kernel_only(F, "quantize X nvfp4 4/6 RHT", "quant_rows_kernel", xs, F.FP4_NVFP4, f,
                           probe_amax(d["x"], True, d["signs"]), signs=d["signs"]),
@@ -457,12 +474,12 @@ def wl_training_backward(F, inputs):
     ops = [Op("quantize dY nvfp4 4/6 stochastic", "quant_rows_kernel", "hbm", qg.bytes(),
               PEAK_HBM_GBS, qg, "GB/s", lane=1),
            Op("quantize W^T nvfp4 2D 4/6", "quant_cols_kernel", "hbm", qwt.bytes(), PEAK_HBM_GBS, qwt, "GB/s", lane=2),
-           Op("dgrad gemm nvfp4 dX = dY W", "gemm_fp4_kernel<true, 128, 4, 1, false>", "mfma", gd.flops(),
+           Op("dgrad gemm nvfp4 dX = dY W", gd.kernel(), "mfma", gd.flops(),
               PEAK_TFLOPS["f16"], gd, "TFLOP/s"),
            Op("quantize dY^T nvfp4 4/6 stochastic", "quant_cols_kernel", "hbm", qgt.bytes(), PEAK_HBM_GBS, qgt,
               "GB/s", lane=1),
            Op("quantize X^T nvfp4 4/6", "quant_cols_kernel", "hbm", qxt.bytes(), PEAK_HBM_GBS, qxt, "GB/s", lane=2),
-           Op("wgrad gemm nvfp4 dW = dY^T X", "gemm_fp4_kernel<true, 128, 4, 1, false>", "mfma", gw.flops(),
+           Op("wgrad gemm nvfp4 dW = dY^T X", gw.kernel(), "mfma", gw.flops(),
               PEAK_TFLOPS["f16"], gw, "TFLOP/s")]
     cfg = {"workload": "training_backward_nvfp4_8192", "M": 8192, "N": 8192, "K": 8192,
            "gradient": "8192x8192 bf16 Laplace(0,1e-3)", "weight": "8192x8192 bf16 N(0,0.02)",
@@ -514,7 +531,7 @@ def wl_w4a4_unfused_chain(F, inputs):
               PEAK_HBM_GBS, qa, "GB/s"),
            Op("quantize W nvfp4 4/6 (amax pre-pass + quantize)", "amax_kernel+quant_rows_kernel", "hbm", qw.bytes(),
               PEAK_HBM_GBS, qw, "GB/s"),
-           Op("gemm nvfp4 (exact fp16 dequant + fp16 MFMA)", "gemm_fp4_kernel<true, 128, 4, 1, false>", "mfma",
+           Op("gemm nvfp4 (exact fp16 dequant + fp16 MFMA)", gm.kernel(), "mfma",
               gm.flops(), PEAK_TFLOPS["f16"], gm, "TFLOP/s"),
            Op("quantize C nvfp4 4/6 (amax supplied)", "quant_rows_kernel", "hbm", qc.bytes(), PEAK_HBM_GBS, qc,
               "GB/s")]

@@ -22,8 +22,8 @@
 // for A and B, which leaves the sum unchanged.
 //
 // Tiling: a workgroup (4 waves, 2 x 2) owns a 256 x BN tile of C (BN = 256
-// for MXFP4 unless fewer tiles than compute units would result, else 128;
-// NVFP4 always 128); each wave owns 128 x BN/2 as 32 x 32 MFMA tiles. The
+// unless fewer tiles than compute units would result, or, for NVFP4, K is
+// short; else 128); each wave owns 128 x BN/2 as 32 x 32 MFMA tiles. The
 // grid is persistent (one workgroup per CU) and walks tiles in an order that
 // keeps operand panels within one XCD's L2.
 //
@@ -104,7 +104,10 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const uint8_t* base, uint32_t bytes
 // inline assembly so that the compiler, which cannot match the copies in
 // flight to the stage slots, adds no vmcnt waits of its own before LDS reads:
 // every wait on these copies is explicit below. The instruction has no output
-// register; m0, which it writes, is declared clobbered.
+// register. It writes m0, which cannot be named as clobbered: the compiler
+// reserves m0 (it rejects it on a clobber list) and sets it itself right
+// before each instruction of its own that reads it, never holding a value in
+// it across other code; in this kernel nothing but these copies reads m0.
 __device__ __forceinline__ void b2l16(const i32x4& rsrc, uint32_t voff, uint32_t lds) {
   asm volatile(
       "s_mov_b32 m0, %2\n\t"
@@ -112,7 +115,7 @@ __device__ __forceinline__ void b2l16(const i32x4& rsrc, uint32_t voff, uint32_t
       "buffer_load_dwordx4 %0, %1, 0 offen lds"
       :
       : "v"(voff), "s"(rsrc), "s"(lds)
-      : "memory", "m0");
+      : "memory");
 }
 // Scalar (wave-uniform) fp32 load, completed inside the statement. A vector
 // load here would make the compiler wait for every copy in flight before
@@ -884,15 +887,19 @@ static void launch_tiles(const GemmArgs& g, hipStream_t s) {
 // workload shape (fewer MFMAs per fragment read, more dequant per MFMA for
 // NVFP4), so one wave per SIMD it is.
 constexpr int kWavesMx = 4, kWavesNv = 4;
+// shortest K at which the 256-wide NVFP4 tile is the faster one
+constexpr int64_t kNvWideMinK = 2048;
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   // 256-wide tiles when they still give every compute unit a tile
   const int64_t t256 = ((g.N + 255) / 256) * (g.offs ? (g.M + kBM - 1) / kBM : m_tiles(g));
   const bool wide = t256 >= device_cu_count();
   if (g.nvfp4) {
-    // NVFP4 keeps the 256 x 128 tile: its fp16 dequant temporaries do not
-    // fit beside 256 accumulators
-    launch_tiles<true, 128, kWavesNv>(g, s);
+    // NVFP4: the 256-wide tile dequantizes 0.5 instead of 0.75 fragments per
+    // MFMA, but it spills in the tile epilogue (256 accumulators beside the
+    // fp16 dequant state), which long K amortizes
+    if (wide && !g.qc && g.K >= kNvWideMinK) launch_tiles<true, 256, kWavesNv>(g, s);
+    else launch_tiles<true, 128, kWavesNv>(g, s);
   } else {
     // a quantized output keeps the 128-wide tile: beside 256 accumulators
     // the quantizer's temporaries would spill

@@ -171,3 +171,26 @@ def test_full_rht_gemm(oracle):
     d = inputs.rht_activation(device="cuda")
     full_case(oracle, d["x"], d["w"], NV, FOS | RHT, FOS | RHT | TR, signs=d["signs"],
               what="16384x12288x4096 nvfp4 rht")
+
+
+def test_nvfp4_wide_tile_ragged(oracle):
+    """The 256-wide NVFP4 tile (enough tiles for every compute unit and a long
+    K): 4100 x 3900 x 2112 leaves a partial last M tile (4 rows) and N tile
+    (60 columns), and K = 33 half-stages ends on a half stage. Sampled outputs
+    include the first and last rows and columns of every partial tile."""
+    d = inputs.w4a4_linear(m=4100, n=3900, k=2112, device="cuda")
+    a, b = d["a"].unsqueeze(0), d["w"].unsqueeze(0)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([rng.choice(4100, 40, replace=False), [0, 255, 256, 4095, 4096, 4099]]))
+    cols = np.unique(np.concatenate([rng.choice(3900, 40, replace=False), [0, 255, 256, 3839, 3840, 3899]]))
+    qa, da = oracle_operand(oracle, a.cpu(), NV, FOS, rows=rows)
+    qb, db = oracle_operand(oracle, b.cpu(), NV, FOS, rows=cols)
+    ref = oracle.gemm_reference(da[0], db[0])
+    absab = np.abs(da[0]).astype(np.float64) @ np.abs(db[0]).astype(np.float64).T
+    for out_dtype in (torch.bfloat16, torch.float32):
+        print(f"[gemm-wide] 4100x3900x2112 nvfp4 -> {out_dtype}", flush=True)
+        c = F.gemm(qa, qb, out_dtype)
+        torch.cuda.synchronize()
+        assert tuple(c.shape) == (1, 4100, 3900), c.shape
+        got = c[0][torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()]
+        check_close(got, ref, absab, da.shape[-1], out_dtype, f"wide nvfp4 {out_dtype}")
