@@ -911,26 +911,32 @@ def graph_step_ms(ops, steps, warmup):
 
 
 def time_ops(ops, steps, warmup):
-    """Eager timing: every op of every step between HIP events on its
-    stream; returns the per-op durations (ms) and the whole eager step."""
+    """Eager timing. Each op alone: `steps` back-to-back launches (rotating
+    input sets) between two HIP events on its stream, so that the queue stays
+    ahead of the device and host launch latency does not enter an op's time;
+    then the whole eager step (every op in order, `steps` times). Returns the
+    per-op average durations (ms, one value per op) and the eager step (ms)."""
     torch.cuda.synchronize()
     for i in range(warmup):
         for op in ops:
             op.launch(i)
     torch.cuda.synchronize()
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ops]
-           for _ in range(steps)]
+    per_op = []
+    for op in ops:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            op.launch(i)
+        e1.record()
+        torch.cuda.synchronize()
+        per_op.append([e0.elapsed_time(e1) / steps])
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t_start.record()
     for i in range(steps):
-        for j, op in enumerate(ops):
-            evs[i][j][0].record()
+        for op in ops:
             op.launch(i)
-            evs[i][j][1].record()
     t_end.record()
     torch.cuda.synchronize()
-    per_op = [[evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(steps)] for j in range(len(ops))]
     return per_op, t_start.elapsed_time(t_end) / steps
 
 
