@@ -531,6 +531,8 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_fp4_kernel(GemmArgs g) {
     voffs[j] = q < 4 ? (uint32_t)(64 * q + lane) * (uint32_t)g.lda_s
                      : (uint32_t)((64 * (q - 4) + lane) & (BN - 1)) * (uint32_t)g.ldb_s;
   }
+  const uint32_t(&voff_k)[T::kLW] = voff;
+  const uint32_t(&voffs_k)[T::kLCW] = voffs;
   i32x4 ra, rb, rsa, rsb;
   auto set_sources = [&](int64_t grp_, int64_t m0_, int64_t mend_, int64_t n0_) {
     const int64_t rows_a = mend_ - m0_ < kBM ? mend_ - m0_ : kBM;
@@ -580,6 +582,23 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_fp4_kernel(GemmArgs g) {
   const int offb1 = T::kABytes + (wn * T::kWN + r32) * kRowBytes + ((2 + h) ^ rot) * 16;
   const int offsa = (wm * 128 + r32) * 16;
   const int offsb = T::kSABytes + (wn * T::kWN + r32) * 16;
+  // LDS byte addresses of the lane's scale words in chunk 0, held opaque to
+  // the compiler: every scale read is then this base plus an immediate under
+  // 64 KB (ds_read's offset field), instead of one register per (chunk, row
+  // block, stage) address past 64 KB
+  uint32_t sbase_a = (uint32_t)(T::kChunk0 + offsa), sbase_b = (uint32_t)(T::kChunk0 + offsb);
+  asm volatile("" : "+v"(sbase_a), "+v"(sbase_b));
+  // The same for the fragment reads, whose slots reach past 64 KB: a low
+  // base (the lane's address in slot 0) and a high one (64 KB above it) per
+  // operand and half-stage; frag_at picks, at compile time, the one that
+  // leaves the immediate under 64 KB.
+  uint32_t fa0_lo = (uint32_t)offa0, fa1_lo = (uint32_t)offa1, fb0_lo = (uint32_t)offb0, fb1_lo = (uint32_t)offb1;
+  uint32_t fa0_hi = fa0_lo + 65536u, fa1_hi = fa1_lo + 65536u, fb0_hi = fb0_lo + 65536u, fb1_hi = fb1_lo + 65536u;
+  asm volatile("" : "+v"(fa0_lo), "+v"(fa1_lo), "+v"(fb0_lo), "+v"(fb1_lo));
+  asm volatile("" : "+v"(fa0_hi), "+v"(fa1_hi), "+v"(fb0_hi), "+v"(fb1_hi));
+  auto frag_at = [&](uint32_t lo, uint32_t hi, int imm) -> const uint4* {
+    return reinterpret_cast<const uint4*>(imm < 65536 ? lds + lo + imm : lds + hi + (imm - 65536));
+  };
   uint4 ca0[4], ca1[4], cb0[NJ], cb1[NJ];
   // scale words of a stage, double-buffered by stage parity. MXFP4: one
   // dword per row = the E8M0 bytes of (kb, h) at byte 2 kb + h. NVFP4: two
@@ -588,30 +607,31 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_fp4_kernel(GemmArgs g) {
 
 #define G_READ(SLOT, KB, CA, CB)                                                        \
   do {                                                                                  \
+    const int so_ = (int)((SLOT) - lds);                                                \
     _Pragma("unroll") for (int i = 0; i < 4; i++)                                       \
-      CA[i] = *reinterpret_cast<const uint4*>((SLOT) + ((KB) ? offa1 : offa0) + i * 32 * kRowBytes); \
+      CA[i] = *frag_at((KB) ? fa1_lo : fa0_lo, (KB) ? fa1_hi : fa0_hi, so_ + i * 32 * kRowBytes); \
     _Pragma("unroll") for (int j = 0; j < NJ; j++)                                      \
-      CB[j] = *reinterpret_cast<const uint4*>((SLOT) + ((KB) ? offb1 : offb0) + j * 32 * kRowBytes); \
+      CB[j] = *frag_at((KB) ? fb1_lo : fb0_lo, (KB) ? fb1_hi : fb0_hi, so_ + j * 32 * kRowBytes); \
   } while (0)
 
 #define G_READ_SCALES(CHUNK, U, SA, SB)                                                 \
   do {                                                                                  \
     _Pragma("unroll") for (int i = 0; i < 4; i++) {                                     \
       if constexpr (NV) {                                                               \
-        const uint2 v_ = *reinterpret_cast<const uint2*>((CHUNK) + offsa + i * 512 + ((U) % CS) * 8); \
+        const uint2 v_ = *reinterpret_cast<const uint2*>(lds + sbase_a + ((CHUNK) - lds - T::kChunk0) + i * 512 + ((U) % CS) * 8); \
         SA[i][0] = v_.x;                                                                \
         SA[i][NV ? 1 : 0] = v_.y;                                                       \
       } else {                                                                          \
-        SA[i][0] = *reinterpret_cast<const uint32_t*>((CHUNK) + offsa + i * 512 + ((U) % CS) * 4); \
+        SA[i][0] = *reinterpret_cast<const uint32_t*>(lds + sbase_a + ((CHUNK) - lds - T::kChunk0) + i * 512 + ((U) % CS) * 4); \
       }                                                                                 \
     }                                                                                   \
     _Pragma("unroll") for (int j = 0; j < NJ; j++) {                                    \
       if constexpr (NV) {                                                               \
-        const uint2 v_ = *reinterpret_cast<const uint2*>((CHUNK) + offsb + j * 512 + ((U) % CS) * 8); \
+        const uint2 v_ = *reinterpret_cast<const uint2*>(lds + sbase_b + ((CHUNK) - lds - T::kChunk0) + j * 512 + ((U) % CS) * 8); \
         SB[j][0] = v_.x;                                                                \
         SB[j][NV ? 1 : 0] = v_.y;                                                       \
       } else {                                                                          \
-        SB[j][0] = *reinterpret_cast<const uint32_t*>((CHUNK) + offsb + j * 512 + ((U) % CS) * 4); \
+        SB[j][0] = *reinterpret_cast<const uint32_t*>(lds + sbase_b + ((CHUNK) - lds - T::kChunk0) + j * 512 + ((U) % CS) * 4); \
       }                                                                                 \
     }                                                                                   \
   } while (0)
@@ -760,6 +780,20 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_fp4_kernel(GemmArgs g) {
   constexpr int kAfter0 = 3 * T::kLW + (1 % CS == 0 ? T::kLCW : 0) + (2 % CS == 0 ? T::kLCW : 0) +
                           (3 % CS == 0 ? T::kLCW : 0);
   auto issue_first_stages = [&]() {
+    // copies of the lane offsets the compiler cannot see through (shadowing
+    // the kernel's): the first stages' offsets are then added here, per tile,
+    // rather than formed once before the tile loop and kept (spilled) across it
+    uint32_t voff[T::kLW], voffs[T::kLCW];
+#pragma unroll
+    for (int j = 0; j < T::kLW; j++) {
+      voff[j] = voff_k[j];
+      asm volatile("" : "+v"(voff[j]));
+    }
+#pragma unroll
+    for (int j = 0; j < T::kLCW; j++) {
+      voffs[j] = voffs_k[j];
+      asm volatile("" : "+v"(voffs[j]));
+    }
     G_ISSUE(L, L + T::kChunk0, 0, true);
     G_ISSUE(L + T::kSlot, L + T::kChunk0 + ((1 / CS) % 2) * T::kChunk, 1, 1 % CS == 0);
     G_ISSUE(L + 2 * T::kSlot, L + T::kChunk0 + ((2 / CS) % 2) * T::kChunk, 2, 2 % CS == 0);
@@ -815,20 +849,26 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_fp4_kernel(GemmArgs g) {
       constexpr int kNR = 2 * RR / WAVES;  // rows each wave stores per round
       auto region = [&](int v) { return lds + (v / T::kWPS) * T::kSlot + (v % T::kWPS) * kReg; };
       const int sm = (int)(wl & 1), sh = (int)(wl >> 1);
+      // the lane index as a value the compiler cannot see through, so that
+      // the epilogue's many LDS and global addresses are formed here, once
+      // per tile, rather than before the tile loop and kept (spilled) across
+      // the K loop
+      int lane_e = lane;
+      asm volatile("" : "+v"(lane_e));
 #pragma unroll
       for (int round = 0; round < 128 / RR; round++) {
-        stage_wave_rows<T::kWN, RR>(acc, alpha, region(w), round, lane);
+        stage_wave_rows<T::kWN, RR>(acc, alpha, region(w), round, lane_e);
         wait_lgkm0();
         lds_barrier();
         // wave s: rows (s >> 1) * kNR + [0, kNR) of the blocks of the waves with wm = s & 1
         if constexpr (OUT == kOutF32 || OUT == kOutBF16) {
           store_staged_rows<T::kWN, WAVES / 2, kNR, OUT == kOutBF16>(g, region(sm),
                                                                     (int)(region(sm + 2) - region(sm)), sh * kNR,
-                                                                    cgrp, m0 + sm * 128 + round * RR, mend, n0, lane);
+                                                                    cgrp, m0 + sm * 128 + round * RR, mend, n0, lane_e);
         } else {
           store_staged_rows_q<T::kWN, WAVES / 2, kNR, OUT == kOutNV>(g, region(sm),
                                                                     (int)(region(sm + 2) - region(sm)), sh * kNR,
-                                                                    cgrp, m0 + sm * 128 + round * RR, mend, n0, lane,
+                                                                    cgrp, m0 + sm * 128 + round * RR, mend, n0, lane_e,
                                                                     nc_out);
         }
         wait_lgkm0();
