@@ -129,12 +129,12 @@ class QuantCall:
 def gemm_kernel_label(nv, G, M, N, K, out_kind, routed=False):
     """The gemm_fp4_kernel instantiation that fp4_gemm launches, by the tile
     rule of launch_gemm in csrc/gemm.hip: 256-wide tiles when they still give
-    every compute unit a tile (for NVFP4 only from K = 2048 and with a plain
+    every compute unit a tile (for NVFP4 only from K = 1024 and with a plain
     output), else 128-wide. The label only keys the kernel in profiles."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     mt = (M + 255) // 256 * (1 if routed else G)
     wide = (N + 255) // 256 * mt >= cus
-    bn = 256 if wide and out_kind < 2 and (not nv or K >= 2048) else 128
+    bn = 256 if wide and out_kind < 2 and (not nv or K >= 1024) else 128
     b = lambda v: "true" if v else "false"
     return f"gemm_fp4_kernel<{b(nv)}, {bn}, 4, {out_kind}, {b(routed)}>"
 

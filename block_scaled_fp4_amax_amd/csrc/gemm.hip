@@ -928,7 +928,7 @@ static void launch_tiles(const GemmArgs& g, hipStream_t s) {
 // NVFP4), so one wave per SIMD it is.
 constexpr int kWavesMx = 4, kWavesNv = 4;
 // shortest K at which the 256-wide NVFP4 tile is the faster one
-constexpr int64_t kNvWideMinK = 2048;
+constexpr int64_t kNvWideMinK = 1024;
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   // 256-wide tiles when they still give every compute unit a tile
