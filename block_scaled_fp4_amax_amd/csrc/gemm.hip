@@ -484,6 +484,10 @@ template <bool NV, int BN, int WAVES, int OUT, bool VAR>
 __global__ __launch_bounds__(WAVES * 64, 1) void gemm_fp4_kernel(GemmArgs g) {
   using T = Tile<NV, BN, WAVES>;
   constexpr int NJ = T::kNJ;
+  // Only the 256-wide NVFP4 tile runs short of registers around its K loop;
+  // it alone forms its per-tile addresses anew each tile (below) instead of
+  // keeping them live, which costs VALU work the other forms do not need.
+  constexpr bool kOpaqueTile = NV && BN == 256;
   constexpr int CS = T::kCS;
   __shared__ __attribute__((aligned(16))) uint8_t lds[T::kLds];
 
@@ -787,12 +791,12 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_fp4_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < T::kLW; j++) {
       voff[j] = voff_k[j];
-      asm volatile("" : "+v"(voff[j]));
+      if constexpr (kOpaqueTile) asm volatile("" : "+v"(voff[j]));
     }
 #pragma unroll
     for (int j = 0; j < T::kLCW; j++) {
       voffs[j] = voffs_k[j];
-      asm volatile("" : "+v"(voffs[j]));
+      if constexpr (kOpaqueTile) asm volatile("" : "+v"(voffs[j]));
     }
     G_ISSUE(L, L + T::kChunk0, 0, true);
     G_ISSUE(L + T::kSlot, L + T::kChunk0 + ((1 / CS) % 2) * T::kChunk, 1, 1 % CS == 0);
@@ -854,7 +858,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_fp4_kernel(GemmArgs g) {
       // per tile, rather than before the tile loop and kept (spilled) across
       // the K loop
       int lane_e = lane;
-      asm volatile("" : "+v"(lane_e));
+      if constexpr (kOpaqueTile) asm volatile("" : "+v"(lane_e));
 #pragma unroll
       for (int round = 0; round < 128 / RR; round++) {
         stage_wave_rows<T::kWN, RR>(acc, alpha, region(w), round, lane_e);
