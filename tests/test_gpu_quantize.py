@@ -63,6 +63,35 @@ def test_batched(fp4, oracle, fmt, flags):
     check(fp4, oracle, x, fmt, flags, what="batch3")
 
 
+# The amax pre-pass walks the item's units (8 values of a row; a 16-value RHT
+# slice; 16 rows x 8 columns under transposed RHT) with an incremental
+# (row, column) position: shapes whose rows hold one or two units, so that a
+# step of the grid stride crosses many rows, a single row, ragged counts and a
+# batch. S_t compares the amax bit for bit.
+def amax_walk_cases():
+    """(shape, flags) pairs valid for NVFP4: the block direction (columns, or
+    rows when transposed) a multiple of 16, the other one of 8 when
+    transposed."""
+    out = []
+    for shape in [(4099, 16), (1, 4096), (37, 48), (3, 2, 2048), (2064, 24), (16, 8), (48, 4104)]:
+        for flags in (0, RHT, TR, TR | RHT):
+            rows, cols = shape[-2], shape[-1]
+            R, C = (cols, rows) if flags & TR else (rows, cols)
+            if C % 16 == 0 and (not flags & TR or R % 8 == 0):
+                out.append((shape, flags))
+    return out
+
+
+@pytest.mark.parametrize("shape,flags", amax_walk_cases(),
+                         ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else flag_str(v))
+def test_amax_prepass_unit_walk(fp4, oracle, shape, flags):
+    rows, cols = shape[-2], shape[-1]
+    x = mixed_matrix(rows, cols, seed=rows + cols + flags)
+    if len(shape) == 3:
+        x = torch.stack([x * (10.0 ** k) for k in range(shape[0])])
+    check(fp4, oracle, x, NV, flags, what="amax-walk")
+
+
 @pytest.mark.parametrize("fmt,flags", [(MX, 0), (NV, FOS), (NV, FOS | RHT), (NV, FOS | TR), (NV, FOS | TR | RHT),
                                        (NV, B2D | FOS)])
 def test_padded_input_pitch(fp4, oracle, fmt, flags):
