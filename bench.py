@@ -104,6 +104,7 @@ class QuantCall:
         self.dt = F.FP4_BF16 if x.dtype == torch.bfloat16 else F.FP4_F32
         self.nv = fmt == F.FP4_NVFP4
         self.fmt = fmt
+        self.flags = flags
         self.stream = torch.cuda.current_stream().cuda_stream
         self.lib = F.lib()
         self.opts_ref = ctypes.byref(self.opts)
@@ -124,6 +125,29 @@ class QuantCall:
 
     def quantized(self):
         return self.F.Quantized(self.fmt, self.codes, self.scales, self.ts if self.nv else None)
+
+    def kernel(self):
+        """The quantizer instantiation fp4_quantize launches for this call, by
+        the dispatch of csrc/quantize.hip (quant_rows_kernel or, transposed,
+        quant_cols_kernel<input, NVFP4, scale selection, 2D, SR, RHT>), after
+        the amax pre-pass when NVFP4 runs without a supplied amax. The label
+        only keys the kernel in profiles."""
+        F, f = self.F, self.flags
+        b = lambda v: "true" if v else "false"
+        if not self.nv:
+            sel = 1 if f & F.FP4_FOUR_OVER_SIX else 0
+        elif f & F.FP4_TENSOR_SCALE:
+            sel = 3
+        elif f & F.FP4_SCALE_SEARCH:
+            sel = 2
+        else:
+            sel = 1 if f & F.FP4_FOUR_OVER_SIX else 0
+        b2d = self.nv and sel != 3 and bool(f & F.FP4_BLOCK2D)
+        name = "quant_cols_kernel" if f & F.FP4_TRANSPOSE else "quant_rows_kernel"
+        tin = "unsigned short" if self.dt == F.FP4_BF16 else "float"
+        k = (f"{name}<{tin}, {b(self.nv)}, {sel}, {b(b2d)}, {b(f & F.FP4_STOCHASTIC)}, "
+             f"{b(f & F.FP4_HADAMARD)}>")
+        return "amax_kernel+" + k if self.nv and self.amax is None else k
 
 
 def gemm_kernel_label(nv, G, M, N, K, out_kind, routed=False):
@@ -336,9 +360,9 @@ def bits(t):
     return t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
 
 
-def kernel_only(F, name, kernel, xs, fmt, flags, amax, signs=0, seed=0, offset=0):
+def kernel_only(F, name, xs, fmt, flags, amax, signs=0, seed=0, offset=0):
     q = QuantCall(F, xs, fmt, flags, signs=signs, seed=seed, offset=offset, amax=amax)
-    return Op(name + " (kernel only, amax supplied)", kernel, "hbm", q.bytes(), PEAK_HBM_GBS, q, "GB/s")
+    return Op(name + " (kernel only, amax supplied)", q.kernel(), "hbm", q.bytes(), PEAK_HBM_GBS, q, "GB/s")
 
 
 def wl_w4a4_linear(F, inputs):
@@ -349,14 +373,14 @@ def wl_w4a4_linear(F, inputs):
     qa = QuantCall(F, xa, F.FP4_NVFP4, fos)
     qw = QuantCall(F, xw, F.FP4_NVFP4, fos)
     gm = GemmCall(F, qa, qw, torch.bfloat16)
-    ops = [Op("quantize A nvfp4 4/6 (amax pre-pass + quantize)", "amax_kernel+quant_rows_kernel", "hbm", qa.bytes(),
+    ops = [Op("quantize A nvfp4 4/6 (amax pre-pass + quantize)", qa.kernel(), "hbm", qa.bytes(),
               PEAK_HBM_GBS, qa, "GB/s"),
-           Op("quantize W nvfp4 4/6 (amax pre-pass + quantize)", "amax_kernel+quant_rows_kernel", "hbm", qw.bytes(),
+           Op("quantize W nvfp4 4/6 (amax pre-pass + quantize)", qw.kernel(), "hbm", qw.bytes(),
               PEAK_HBM_GBS, qw, "GB/s"),
            Op("gemm nvfp4 (exact fp16 dequant + fp16 MFMA)", gm.kernel(), "mfma",
               gm.flops(), PEAK_TFLOPS["f16"], gm, "TFLOP/s")]
-    probes = [kernel_only(F, "quantize A nvfp4 4/6", "quant_rows_kernel", xa, F.FP4_NVFP4, fos, probe_amax(d["a"])),
-              kernel_only(F, "quantize W nvfp4 4/6", "quant_rows_kernel", xw, F.FP4_NVFP4, fos, probe_amax(d["w"]))]
+    probes = [kernel_only(F, "quantize A nvfp4 4/6", xa, F.FP4_NVFP4, fos, probe_amax(d["a"])),
+              kernel_only(F, "quantize W nvfp4 4/6", xw, F.FP4_NVFP4, fos, probe_amax(d["w"]))]
     cfg = {"workload": "w4a4_linear_nvfp4_four_over_six", "M": 2048, "N": 4096, "K": 4096,
            "activations": "2048x4096 bf16 N(0,1), 1% columns x30", "weight": "4096x4096 bf16 N(0,0.02)",
            "output": "bf16", "input_sets_rotated": n}
@@ -373,9 +397,9 @@ def wl_moe(F, inputs):
     qw = QuantCall(F, copies(d["w"], n), F.FP4_MXFP4, F.FP4_TRANSPOSE)
     qx = QuantCall(F, copies(d["x"], n), F.FP4_MXFP4, 0)
     gm = GemmCall(F, qx, qw, torch.bfloat16)
-    ops = [Op("quantize W^T mxfp4 32x[2880x5760]", "quant_cols_kernel", "hbm", qw.bytes(),
+    ops = [Op("quantize W^T mxfp4 32x[2880x5760]", qw.kernel(), "hbm", qw.bytes(),
               PEAK_HBM_GBS, qw, "GB/s"),
-           Op("quantize X mxfp4 32x[512x2880]", "quant_rows_kernel", "hbm", qx.bytes(),
+           Op("quantize X mxfp4 32x[512x2880]", qx.kernel(), "hbm", qx.bytes(),
               PEAK_HBM_GBS, qx, "GB/s"),
            Op("grouped gemm mxfp4 (scaled FP4 MFMA)", gm.kernel(), "mfma",
               gm.flops(), PEAK_TFLOPS["fp4"], gm, "TFLOP/s")]
@@ -404,15 +428,15 @@ def wl_training(F, inputs):
     q1 = QuantCall(F, ws, F.FP4_NVFP4, f)
     q2 = QuantCall(F, ws2, F.FP4_NVFP4, f | F.FP4_TRANSPOSE)
     q3 = QuantCall(F, gs, F.FP4_NVFP4, fg, seed=d["sr_seed"])
-    ops = [Op("quantize W nvfp4 2D 4/6", "quant_rows_kernel", "hbm", q1.bytes(), PEAK_HBM_GBS, q1, "GB/s", lane=1),
-           Op("quantize W^T nvfp4 2D 4/6", "quant_cols_kernel", "hbm", q2.bytes(), PEAK_HBM_GBS, q2, "GB/s", lane=2),
-           Op("quantize G nvfp4 4/6 stochastic", "quant_rows_kernel", "hbm", q3.bytes(),
+    ops = [Op("quantize W nvfp4 2D 4/6", q1.kernel(), "hbm", q1.bytes(), PEAK_HBM_GBS, q1, "GB/s", lane=1),
+           Op("quantize W^T nvfp4 2D 4/6", q2.kernel(), "hbm", q2.bytes(), PEAK_HBM_GBS, q2, "GB/s", lane=2),
+           Op("quantize G nvfp4 4/6 stochastic", q3.kernel(), "hbm", q3.bytes(),
               PEAK_HBM_GBS, q3, "GB/s", lane=3)]
     aw, ag = probe_amax(d["w"]), probe_amax(d["grad"])
-    probes = [kernel_only(F, "quantize W nvfp4 2D 4/6", "quant_rows_kernel", ws, F.FP4_NVFP4, f, aw),
-              kernel_only(F, "quantize W^T nvfp4 2D 4/6", "quant_cols_kernel", ws2, F.FP4_NVFP4, f | F.FP4_TRANSPOSE,
+    probes = [kernel_only(F, "quantize W nvfp4 2D 4/6", ws, F.FP4_NVFP4, f, aw),
+              kernel_only(F, "quantize W^T nvfp4 2D 4/6", ws2, F.FP4_NVFP4, f | F.FP4_TRANSPOSE,
                           aw),
-              kernel_only(F, "quantize G nvfp4 4/6 stochastic", "quant_rows_kernel", gs, F.FP4_NVFP4, fg, ag,
+              kernel_only(F, "quantize G nvfp4 4/6 stochastic", gs, F.FP4_NVFP4, fg, ag,
                           seed=d["sr_seed"])]
     cfg = {"workload": "training_quantize_nvfp4_8192x8192", "shape": [8192, 8192], "input_sets_rotated": n}
     w, g = bits(d["w"][:, :2048].contiguous()), bits(d["grad"][:1024])
@@ -433,13 +457,13 @@ def wl_rht(F, inputs):
     qx = QuantCall(F, xs, F.FP4_NVFP4, f, signs=d["signs"])
     qw = QuantCall(F, wsets, F.FP4_NVFP4, f | F.FP4_TRANSPOSE, signs=d["signs"])
     gm = GemmCall(F, qx, qw, torch.bfloat16)
-    ops = [Op("quantize X nvfp4 4/6 RHT", "quant_rows_kernel", "hbm", qx.bytes(), PEAK_HBM_GBS, qx, "GB/s", lane=1),
-           Op("quantize W^T nvfp4 4/6 RHT", "quant_cols_kernel", "hbm", qw.bytes(), PEAK_HBM_GBS, qw, "GB/s", lane=2),
+    ops = [Op("quantize X nvfp4 4/6 RHT", qx.kernel(), "hbm", qx.bytes(), PEAK_HBM_GBS, qx, "GB/s", lane=1),
+           Op("quantize W^T nvfp4 4/6 RHT", qw.kernel(), "hbm", qw.bytes(), PEAK_HBM_GBS, qw, "GB/s", lane=2),
            Op("gemm nvfp4 (exact fp16 dequant + fp16 MFMA)", gm.kernel(), "mfma",
               gm.flops(), PEAK_TFLOPS["f16"], gm, "TFLOP/s")]
-    probes = [kernel_only(F, "quantize X nvfp4 4/6 RHT", "quant_rows_kernel", xs, F.FP4_NVFP4, f,
+    probes = [kernel_only(F, "quantize X nvfp4 4/6 RHT", xs, F.FP4_NVFP4, f,
                           probe_amax(d["x"], True, d["signs"]), signs=d["signs"]),
-              kernel_only(F, "quantize W^T nvfp4 4/6 RHT", "quant_cols_kernel", wsets, F.FP4_NVFP4,
+              kernel_only(F, "quantize W^T nvfp4 4/6 RHT", wsets, F.FP4_NVFP4,
                           f | F.FP4_TRANSPOSE, probe_amax(d["w"], True, d["signs"], along_columns=True),
                           signs=d["signs"])]
     cfg = {"workload": "rht_activation_nvfp4_16384x12288x4096", "M": 16384, "N": 12288, "K": 4096,
@@ -471,14 +495,14 @@ def wl_training_backward(F, inputs):
     qgt = QuantCall(F, gs2, F.FP4_NVFP4, fos | sr | tr, seed=d["sr_seed"], offset=1 << 40)
     qxt = QuantCall(F, xs, F.FP4_NVFP4, fos | tr)
     gw = GemmCall(F, qgt, qxt, torch.bfloat16)
-    ops = [Op("quantize dY nvfp4 4/6 stochastic", "quant_rows_kernel", "hbm", qg.bytes(),
+    ops = [Op("quantize dY nvfp4 4/6 stochastic", qg.kernel(), "hbm", qg.bytes(),
               PEAK_HBM_GBS, qg, "GB/s", lane=1),
-           Op("quantize W^T nvfp4 2D 4/6", "quant_cols_kernel", "hbm", qwt.bytes(), PEAK_HBM_GBS, qwt, "GB/s", lane=2),
+           Op("quantize W^T nvfp4 2D 4/6", qwt.kernel(), "hbm", qwt.bytes(), PEAK_HBM_GBS, qwt, "GB/s", lane=2),
            Op("dgrad gemm nvfp4 dX = dY W", gd.kernel(), "mfma", gd.flops(),
               PEAK_TFLOPS["f16"], gd, "TFLOP/s"),
-           Op("quantize dY^T nvfp4 4/6 stochastic", "quant_cols_kernel", "hbm", qgt.bytes(), PEAK_HBM_GBS, qgt,
+           Op("quantize dY^T nvfp4 4/6 stochastic", qgt.kernel(), "hbm", qgt.bytes(), PEAK_HBM_GBS, qgt,
               "GB/s", lane=1),
-           Op("quantize X^T nvfp4 4/6", "quant_cols_kernel", "hbm", qxt.bytes(), PEAK_HBM_GBS, qxt, "GB/s", lane=2),
+           Op("quantize X^T nvfp4 4/6", qxt.kernel(), "hbm", qxt.bytes(), PEAK_HBM_GBS, qxt, "GB/s", lane=2),
            Op("wgrad gemm nvfp4 dW = dY^T X", gw.kernel(), "mfma", gw.flops(),
               PEAK_TFLOPS["f16"], gw, "TFLOP/s")]
     cfg = {"workload": "training_backward_nvfp4_8192", "M": 8192, "N": 8192, "K": 8192,
@@ -501,9 +525,9 @@ def wl_w4a4_fused(F, inputs):
     amax = probe.c.abs().amax().reshape(1)
     del probe
     gq = GemmQuantizeOutputCall(F, qa, qw, amax)
-    ops = [Op("quantize A nvfp4 4/6 (amax pre-pass + quantize)", "amax_kernel+quant_rows_kernel", "hbm", qa.bytes(),
+    ops = [Op("quantize A nvfp4 4/6 (amax pre-pass + quantize)", qa.kernel(), "hbm", qa.bytes(),
               PEAK_HBM_GBS, qa, "GB/s"),
-           Op("quantize W nvfp4 4/6 (amax pre-pass + quantize)", "amax_kernel+quant_rows_kernel", "hbm", qw.bytes(),
+           Op("quantize W nvfp4 4/6 (amax pre-pass + quantize)", qw.kernel(), "hbm", qw.bytes(),
               PEAK_HBM_GBS, qw, "GB/s"),
            Op("gemm nvfp4, output quantized to nvfp4 4/6 in the epilogue", "gemm_fp4_kernel<true, 128, 4, 3, false>",
               "mfma", gq.flops(), PEAK_TFLOPS["f16"], gq, "TFLOP/s")]
@@ -527,13 +551,13 @@ def wl_w4a4_unfused_chain(F, inputs):
     gm(0)
     amax = gm.c.float().abs().amax().reshape(1)
     qc = QuantCall(F, [gm.c], F.FP4_NVFP4, F.FP4_FOUR_OVER_SIX, amax=amax)
-    ops = [Op("quantize A nvfp4 4/6 (amax pre-pass + quantize)", "amax_kernel+quant_rows_kernel", "hbm", qa.bytes(),
+    ops = [Op("quantize A nvfp4 4/6 (amax pre-pass + quantize)", qa.kernel(), "hbm", qa.bytes(),
               PEAK_HBM_GBS, qa, "GB/s"),
-           Op("quantize W nvfp4 4/6 (amax pre-pass + quantize)", "amax_kernel+quant_rows_kernel", "hbm", qw.bytes(),
+           Op("quantize W nvfp4 4/6 (amax pre-pass + quantize)", qw.kernel(), "hbm", qw.bytes(),
               PEAK_HBM_GBS, qw, "GB/s"),
            Op("gemm nvfp4 (exact fp16 dequant + fp16 MFMA)", gm.kernel(), "mfma",
               gm.flops(), PEAK_TFLOPS["f16"], gm, "TFLOP/s"),
-           Op("quantize C nvfp4 4/6 (amax supplied)", "quant_rows_kernel", "hbm", qc.bytes(), PEAK_HBM_GBS, qc,
+           Op("quantize C nvfp4 4/6 (amax supplied)", qc.kernel(), "hbm", qc.bytes(), PEAK_HBM_GBS, qc,
               "GB/s")]
     cfg = {"workload": "w4a4_linear_nvfp4_unfused_output_quantize", "M": 2048, "N": 4096, "K": 4096,
            "activations": "2048x4096 bf16 N(0,1), 1% columns x30", "weight": "4096x4096 bf16 N(0,0.02)",
@@ -551,11 +575,11 @@ def wl_scale_search(F, inputs):
     qs = QuantCall(F, copies(d["w"], n), F.FP4_NVFP4, F.FP4_SCALE_SEARCH)
     q2 = QuantCall(F, copies(d["w"], n), F.FP4_NVFP4, F.FP4_SCALE_SEARCH | F.FP4_BLOCK2D)
     qm = QuantCall(F, copies(d["w"], n), F.FP4_MXFP4, F.FP4_FOUR_OVER_SIX)
-    ops = [Op("quantize W nvfp4 scale search (amax pre-pass + quantize)", "amax_kernel+quant_rows_kernel", "hbm",
+    ops = [Op("quantize W nvfp4 scale search (amax pre-pass + quantize)", qs.kernel(), "hbm",
               qs.bytes(), PEAK_HBM_GBS, qs, "GB/s", lane=1),
-           Op("quantize W nvfp4 2D scale search (amax pre-pass + quantize)", "amax_kernel+quant_rows_kernel", "hbm",
+           Op("quantize W nvfp4 2D scale search (amax pre-pass + quantize)", q2.kernel(), "hbm",
               q2.bytes(), PEAK_HBM_GBS, q2, "GB/s", lane=2),
-           Op("quantize W mxfp4 4/6 exponent pair", "quant_rows_kernel", "hbm", qm.bytes(),
+           Op("quantize W mxfp4 4/6 exponent pair", qm.kernel(), "hbm", qm.bytes(),
               PEAK_HBM_GBS, qm, "GB/s", lane=3)]
     cfg = {"workload": "scale_search_8192", "shape": [8192, 8192], "weight": "8192x8192 bf16 N(0,0.02)",
            "input_sets_rotated": n}
@@ -572,9 +596,9 @@ def wl_moe_routed(F, inputs):
     qw = QuantCall(F, copies(d["w"], n), F.FP4_MXFP4, F.FP4_TRANSPOSE)
     qx = QuantCall(F, copies(d["x"], n), F.FP4_MXFP4, 0)
     gm = GroupedGemmCall(F, qx, qw, d["offsets"], torch.bfloat16)
-    ops = [Op("quantize W^T mxfp4 32x[2880x5760]", "quant_cols_kernel", "hbm", qw.bytes(),
+    ops = [Op("quantize W^T mxfp4 32x[2880x5760]", qw.kernel(), "hbm", qw.bytes(),
               PEAK_HBM_GBS, qw, "GB/s"),
-           Op("quantize routed X mxfp4 [16384x2880]", "quant_rows_kernel", "hbm", qx.bytes(), PEAK_HBM_GBS, qx,
+           Op("quantize routed X mxfp4 [16384x2880]", qx.kernel(), "hbm", qx.bytes(), PEAK_HBM_GBS, qx,
               "GB/s"),
            Op("grouped gemm mxfp4, router row counts", "gemm_fp4_kernel<false, 256, 4, 1, true>", "mfma",
               gm.flops(), PEAK_TFLOPS["fp4"], gm, "TFLOP/s")]
