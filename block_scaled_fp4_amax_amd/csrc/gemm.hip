@@ -518,25 +518,31 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_fp4_kernel(GemmArgs g) {
   // offsets are fixed for the kernel; a tile sets four buffer resources whose
   // size ends at its last valid row, and a stage adds its K offset.
   const uint32_t lda = (uint32_t)g.lda, ldb = (uint32_t)g.ldb;
-  const uint32_t piece = (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) * 16);
-  uint32_t voff[T::kLW];
+  // The lane offsets of lane ln (scale-chunk block q = w + WAVES j, j <
+  // kLCW: A rows 64 q + lane for q < 4, else B rows (64 (q - 4) + lane)
+  // mod BN). Under kOpaqueTile each tile forms them anew from an opaque
+  // copy of the lane index, so that none is kept (spilled) across the
+  // epilogue; elsewhere the compiler keeps one set for the kernel.
+  auto lane_offsets = [&](int ln, uint32_t (&vo)[T::kLW], uint32_t (&vs)[T::kLCW]) {
+    const uint32_t piece = (uint32_t)(((ln & 3) ^ ((ln >> 4) & 3)) * 16);
 #pragma unroll
-  for (int j = 0; j < T::kLW; j++) {
-    const int q = w + WAVES * j;
-    voff[j] = j < T::kLWA ? (uint32_t)(16 * q + (lane >> 2)) * lda + piece
-                          : (uint32_t)(16 * (q - 16) + (lane >> 2)) * ldb + piece;
-  }
-  // scale-chunk block q = w + WAVES j (j < kLCW): A rows 64 q + lane for
-  // q < 4, else B rows (64 (q - 4) + lane) mod BN
-  uint32_t voffs[T::kLCW];
+    for (int j = 0; j < T::kLW; j++) {
+      const int q = w + WAVES * j;
+      vo[j] = j < T::kLWA ? (uint32_t)(16 * q + (ln >> 2)) * lda + piece
+                          : (uint32_t)(16 * (q - 16) + (ln >> 2)) * ldb + piece;
+    }
 #pragma unroll
-  for (int j = 0; j < T::kLCW; j++) {
-    const int q = w + WAVES * j;
-    voffs[j] = q < 4 ? (uint32_t)(64 * q + lane) * (uint32_t)g.lda_s
-                     : (uint32_t)((64 * (q - 4) + lane) & (BN - 1)) * (uint32_t)g.ldb_s;
-  }
-  const uint32_t(&voff_k)[T::kLW] = voff;
-  const uint32_t(&voffs_k)[T::kLCW] = voffs;
+    for (int j = 0; j < T::kLCW; j++) {
+      const int q = w + WAVES * j;
+      vs[j] = q < 4 ? (uint32_t)(64 * q + ln) * (uint32_t)g.lda_s
+                    : (uint32_t)((64 * (q - 4) + ln) & (BN - 1)) * (uint32_t)g.ldb_s;
+    }
+  };
+  auto tile_lane = [&]() {
+    int ln = lane;
+    if constexpr (kOpaqueTile) asm volatile("" : "+v"(ln));
+    return ln;
+  };
   i32x4 ra, rb, rsa, rsb;
   auto set_sources = [&](int64_t grp_, int64_t m0_, int64_t mend_, int64_t n0_) {
     const int64_t rows_a = mend_ - m0_ < kBM ? mend_ - m0_ : kBM;
@@ -577,29 +583,37 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_fp4_kernel(GemmArgs g) {
 
   f32x16 acc[4][NJ];
 
-  // Fragment addresses: A rows wm*128 + i*32 + r32, B rows wn*kWN + j*32 +
-  // r32; the lane's 16-byte K piece of half-stage kb is 2 kb + h, rotated.
-  const int rot = (r32 >> 2) & 3;
-  const int offa0 = (wm * 128 + r32) * kRowBytes + ((0 + h) ^ rot) * 16;
-  const int offa1 = (wm * 128 + r32) * kRowBytes + ((2 + h) ^ rot) * 16;
-  const int offb0 = T::kABytes + (wn * T::kWN + r32) * kRowBytes + ((0 + h) ^ rot) * 16;
-  const int offb1 = T::kABytes + (wn * T::kWN + r32) * kRowBytes + ((2 + h) ^ rot) * 16;
-  const int offsa = (wm * 128 + r32) * 16;
-  const int offsb = T::kSABytes + (wn * T::kWN + r32) * 16;
-  // LDS byte addresses of the lane's scale words in chunk 0, held opaque to
-  // the compiler: every scale read is then this base plus an immediate under
-  // 64 KB (ds_read's offset field), instead of one register per (chunk, row
-  // block, stage) address past 64 KB
-  uint32_t sbase_a = (uint32_t)(T::kChunk0 + offsa), sbase_b = (uint32_t)(T::kChunk0 + offsb);
-  asm volatile("" : "+v"(sbase_a), "+v"(sbase_b));
-  // The same for the fragment reads, whose slots reach past 64 KB: a low
-  // base (the lane's address in slot 0) and a high one (64 KB above it) per
-  // operand and half-stage; frag_at picks, at compile time, the one that
-  // leaves the immediate under 64 KB.
-  uint32_t fa0_lo = (uint32_t)offa0, fa1_lo = (uint32_t)offa1, fb0_lo = (uint32_t)offb0, fb1_lo = (uint32_t)offb1;
-  uint32_t fa0_hi = fa0_lo + 65536u, fa1_hi = fa1_lo + 65536u, fb0_hi = fb0_lo + 65536u, fb1_hi = fb1_lo + 65536u;
-  asm volatile("" : "+v"(fa0_lo), "+v"(fa1_lo), "+v"(fb0_lo), "+v"(fb1_lo));
-  asm volatile("" : "+v"(fa0_hi), "+v"(fa1_hi), "+v"(fb0_hi), "+v"(fb1_hi));
+  // LDS read bases of lane ln. Fragments: A rows wm*128 + i*32 + r32, B
+  // rows wn*kWN + j*32 + r32; the lane's 16-byte K piece of half-stage kb is
+  // 2 kb + h, rotated. The bases are held opaque to the compiler, so that
+  // every read is a base plus an immediate under 64 KB (ds_read's offset
+  // field) instead of one register per (slot, row block, stage) address past
+  // 64 KB: the scale words' base in chunk 0, and per operand and half-stage
+  // a low fragment base (slot 0) and a high one (64 KB above it); frag_at
+  // picks, at compile time, the one that leaves the immediate under 64 KB.
+  // Under kOpaqueTile each tile forms them anew (from tile_lane()).
+  struct LdsBases {
+    uint32_t sa, sb, a0_lo, a1_lo, b0_lo, b1_lo, a0_hi, a1_hi, b0_hi, b1_hi;
+  };
+  auto lds_bases = [&](int ln) {
+    const int r = ln & 31, hh = ln >> 5, rot = (r >> 2) & 3;
+    LdsBases o;
+    o.a0_lo = (uint32_t)((wm * 128 + r) * kRowBytes + ((0 + hh) ^ rot) * 16);
+    o.a1_lo = (uint32_t)((wm * 128 + r) * kRowBytes + ((2 + hh) ^ rot) * 16);
+    o.b0_lo = (uint32_t)(T::kABytes + (wn * T::kWN + r) * kRowBytes + ((0 + hh) ^ rot) * 16);
+    o.b1_lo = (uint32_t)(T::kABytes + (wn * T::kWN + r) * kRowBytes + ((2 + hh) ^ rot) * 16);
+    o.sa = (uint32_t)(T::kChunk0 + (wm * 128 + r) * 16);
+    o.sb = (uint32_t)(T::kChunk0 + T::kSABytes + (wn * T::kWN + r) * 16);
+    o.a0_hi = o.a0_lo + 65536u;
+    o.a1_hi = o.a1_lo + 65536u;
+    o.b0_hi = o.b0_lo + 65536u;
+    o.b1_hi = o.b1_lo + 65536u;
+    asm volatile("" : "+v"(o.sa), "+v"(o.sb));
+    asm volatile("" : "+v"(o.a0_lo), "+v"(o.a1_lo), "+v"(o.b0_lo), "+v"(o.b1_lo));
+    asm volatile("" : "+v"(o.a0_hi), "+v"(o.a1_hi), "+v"(o.b0_hi), "+v"(o.b1_hi));
+    return o;
+  };
+  const LdsBases bases_k = lds_bases(lane);
   auto frag_at = [&](uint32_t lo, uint32_t hi, int imm) -> const uint4* {
     return reinterpret_cast<const uint4*>(imm < 65536 ? lds + lo + imm : lds + hi + (imm - 65536));
   };
@@ -613,29 +627,29 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_fp4_kernel(GemmArgs g) {
   do {                                                                                  \
     const int so_ = (int)((SLOT) - lds);                                                \
     _Pragma("unroll") for (int i = 0; i < 4; i++)                                       \
-      CA[i] = *frag_at((KB) ? fa1_lo : fa0_lo, (KB) ? fa1_hi : fa0_hi, so_ + i * 32 * kRowBytes); \
+      CA[i] = *frag_at((KB) ? lb.a1_lo : lb.a0_lo, (KB) ? lb.a1_hi : lb.a0_hi, so_ + i * 32 * kRowBytes); \
     _Pragma("unroll") for (int j = 0; j < NJ; j++)                                      \
-      CB[j] = *frag_at((KB) ? fb1_lo : fb0_lo, (KB) ? fb1_hi : fb0_hi, so_ + j * 32 * kRowBytes); \
+      CB[j] = *frag_at((KB) ? lb.b1_lo : lb.b0_lo, (KB) ? lb.b1_hi : lb.b0_hi, so_ + j * 32 * kRowBytes); \
   } while (0)
 
 #define G_READ_SCALES(CHUNK, U, SA, SB)                                                 \
   do {                                                                                  \
     _Pragma("unroll") for (int i = 0; i < 4; i++) {                                     \
       if constexpr (NV) {                                                               \
-        const uint2 v_ = *reinterpret_cast<const uint2*>(lds + sbase_a + ((CHUNK) - lds - T::kChunk0) + i * 512 + ((U) % CS) * 8); \
+        const uint2 v_ = *reinterpret_cast<const uint2*>(lds + lb.sa + ((CHUNK) - lds - T::kChunk0) + i * 512 + ((U) % CS) * 8); \
         SA[i][0] = v_.x;                                                                \
         SA[i][NV ? 1 : 0] = v_.y;                                                       \
       } else {                                                                          \
-        SA[i][0] = *reinterpret_cast<const uint32_t*>(lds + sbase_a + ((CHUNK) - lds - T::kChunk0) + i * 512 + ((U) % CS) * 4); \
+        SA[i][0] = *reinterpret_cast<const uint32_t*>(lds + lb.sa + ((CHUNK) - lds - T::kChunk0) + i * 512 + ((U) % CS) * 4); \
       }                                                                                 \
     }                                                                                   \
     _Pragma("unroll") for (int j = 0; j < NJ; j++) {                                    \
       if constexpr (NV) {                                                               \
-        const uint2 v_ = *reinterpret_cast<const uint2*>(lds + sbase_b + ((CHUNK) - lds - T::kChunk0) + j * 512 + ((U) % CS) * 8); \
+        const uint2 v_ = *reinterpret_cast<const uint2*>(lds + lb.sb + ((CHUNK) - lds - T::kChunk0) + j * 512 + ((U) % CS) * 8); \
         SB[j][0] = v_.x;                                                                \
         SB[j][NV ? 1 : 0] = v_.y;                                                       \
       } else {                                                                          \
-        SB[j][0] = *reinterpret_cast<const uint32_t*>(lds + sbase_b + ((CHUNK) - lds - T::kChunk0) + j * 512 + ((U) % CS) * 4); \
+        SB[j][0] = *reinterpret_cast<const uint32_t*>(lds + lb.sb + ((CHUNK) - lds - T::kChunk0) + j * 512 + ((U) % CS) * 4); \
       }                                                                                 \
     }                                                                                   \
   } while (0)
@@ -784,20 +798,8 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_fp4_kernel(GemmArgs g) {
   constexpr int kAfter0 = 3 * T::kLW + (1 % CS == 0 ? T::kLCW : 0) + (2 % CS == 0 ? T::kLCW : 0) +
                           (3 % CS == 0 ? T::kLCW : 0);
   auto issue_first_stages = [&]() {
-    // copies of the lane offsets the compiler cannot see through (shadowing
-    // the kernel's): the first stages' offsets are then added here, per tile,
-    // rather than formed once before the tile loop and kept (spilled) across it
     uint32_t voff[T::kLW], voffs[T::kLCW];
-#pragma unroll
-    for (int j = 0; j < T::kLW; j++) {
-      voff[j] = voff_k[j];
-      if constexpr (kOpaqueTile) asm volatile("" : "+v"(voff[j]));
-    }
-#pragma unroll
-    for (int j = 0; j < T::kLCW; j++) {
-      voffs[j] = voffs_k[j];
-      if constexpr (kOpaqueTile) asm volatile("" : "+v"(voffs[j]));
-    }
+    lane_offsets(tile_lane(), voff, voffs);
     G_ISSUE(L, L + T::kChunk0, 0, true);
     G_ISSUE(L + T::kSlot, L + T::kChunk0 + ((1 / CS) % 2) * T::kChunk, 1, 1 % CS == 0);
     G_ISSUE(L + 2 * T::kSlot, L + T::kChunk0 + ((2 / CS) % 2) * T::kChunk, 2, 2 % CS == 0);
@@ -807,6 +809,11 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_fp4_kernel(GemmArgs g) {
   issue_first_stages();
   for (int64_t jt = 0;; jt++) {
     const int64_t m0 = pos.m0, mend = pos.mend, n0 = pos.n0, cgrp = pos.grp;
+    // the K loop's copy offsets (used by G_COPY) and LDS read bases (used by
+    // G_READ, G_READ_SCALES)
+    uint32_t voff[T::kLW], voffs[T::kLCW];
+    lane_offsets(tile_lane(), voff, voffs);
+    const LdsBases lb = kOpaqueTile ? lds_bases(tile_lane()) : bases_k;
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
