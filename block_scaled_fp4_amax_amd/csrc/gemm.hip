@@ -374,6 +374,13 @@ __device__ __forceinline__ void stage_wave_rows(const f32x16 (&acc)[4][WN / 32],
 // (MXFP4 or NVFP4 codes and scales).
 enum OutKind { kOutF32 = 0, kOutBF16 = 1, kOutMX = 2, kOutNV = 3 };
 
+// C is written once and never read back by the kernel: non-temporal stores
+// keep its lines from displacing in L2 the operand panels that the tiles in
+// flight still read.
+__device__ __forceinline__ void store_c16(uint8_t* p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
 template <int WN, int NWN, int NR, bool OUT_BF16>
 __device__ __forceinline__ void store_staged_rows(const GemmArgs& g, const uint8_t* reg0, int reg_stride, int row0,
                                                   int64_t grp, int64_t m_base, int64_t m_end, int64_t n0, int lane) {
@@ -399,10 +406,10 @@ __device__ __forceinline__ void store_staged_rows(const GemmArgs& g, const uint8
           uint32_t o[4];
 #pragma unroll
           for (int e = 0; e < 4; e++) o[e] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)vv[2 * e], (__bf16)vv[2 * e + 1]});
-          *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+          store_c16(dst, u32x4{o[0], o[1], o[2], o[3]});
         } else {
-          reinterpret_cast<float4*>(dst)[0] = v0;
-          reinterpret_cast<float4*>(dst)[1] = v1;
+          store_c16(dst, __builtin_bit_cast(u32x4, f32x4{v0.x, v0.y, v0.z, v0.w}));
+          store_c16(dst + 16, __builtin_bit_cast(u32x4, f32x4{v1.x, v1.y, v1.z, v1.w}));
         }
       } else {
         // row end or unaligned C: element by element
@@ -473,7 +480,7 @@ __device__ __forceinline__ void store_staged_rows_q(const GemmArgs& g, const uin
     }
 #undef G_QUNIT
     if (m < m_end && n < g.N) {
-      *reinterpret_cast<uint2*>(g.qc + grp * g.qc_gs + m * g.ldqc + n / 2) = make_uint2(w0, w1);
+      __builtin_nontemporal_store(u32x2{w0, w1}, reinterpret_cast<u32x2*>(g.qc + grp * g.qc_gs + m * g.ldqc + n / 2));
       if constexpr (QNV) g.qs[grp * g.qs_gs + m * g.ldqs + n / 16] = (uint8_t)sbyte;
       else if ((u & 1) == 0) g.qs[grp * g.qs_gs + m * g.ldqs + n / 32] = (uint8_t)sbyte;
     }
