@@ -96,9 +96,12 @@ fp4_status plan_quantize(int64_t batch, int64_t rows, int64_t cols, const fp4_qu
   if ((o->flags & FP4_BLOCK2D) && (p->R % 16 != 0)) return FP4_ERR_INVALID;
   if (batch > kMaxGridYZ) return FP4_ERR_UNSUPPORTED;
   if (tr) {
-    // transposed kernel: one workgroup per 256 source rows x 128 source
-    // columns, in a one-dimensional grid padded to whole XCD lanes
-    if (((batch * ((cols + 127) / 128) + 7) / 8) * 8 * ((rows + 255) / 256) > kMaxGridX) return FP4_ERR_UNSUPPORTED;
+    // transposed kernel: one workgroup per 256 source rows x 64 source
+    // columns (128 with 16 x 16 tiles), in a one-dimensional grid padded to
+    // whole XCD lanes
+    const int64_t wcols = (o->flags & FP4_BLOCK2D) ? 128 : 64;
+    if (((batch * ((cols + wcols - 1) / wcols) + 7) / 8) * 8 * ((rows + 255) / 256) > kMaxGridX)
+      return FP4_ERR_UNSUPPORTED;
   } else if (o->flags & FP4_BLOCK2D) {
     if (p->R / 16 > kMaxGridYZ || ((p->C / 16) + 15) / 16 > kMaxGridX) return FP4_ERR_UNSUPPORTED;
   } else {

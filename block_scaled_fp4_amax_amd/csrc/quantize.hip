@@ -7,11 +7,12 @@
 //                      block, half an MXFP4 block (lane pair), or one row of a
 //                      16x16 tile (16 lanes).
 //   quant_cols_kernel  transposed input: blocks run down the columns of X.
-//                      One lane owns a 16-row x 8-column patch (sixteen
-//                      16-byte row loads) = eight blocks, one per source
-//                      column; an MXFP4 block is a vertical lane pair, a
-//                      16x16 tile a horizontal one. Output goes through LDS
-//                      so each output row is written as whole lines.
+//                      One lane owns a 16-row x 4-column patch (sixteen
+//                      8-byte row loads of bf16), or 16 x 8 for 16x16
+//                      tiles: one block per source column; an MXFP4 block
+//                      is a vertical lane pair, a 16x16 tile a horizontal
+//                      one. Output goes through LDS so each output row is
+//                      written as whole lines.
 //
 // The method is stated in quant_common.h.
 #include <mutex>
@@ -280,25 +281,41 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(QuantArgs a) {
 // ------------------------------------------------------------------------
 // Transposed quantization (output = Q(X^T))
 // ------------------------------------------------------------------------
-// A workgroup takes 256 source rows (k) x 128 source columns (n). Lane
-// (wave w, g = lane / 2, h = lane % 2) owns the 16 x 8 patch at
-// k = 64 w + 32 (g / 16) + 16 h, n = 8 (g % 16): sixteen 16-byte row loads.
-// Its eight 16-value blocks (one per source column) land in an LDS image of
-// the workgroup's output, 128 rows of 128 code bytes plus their scale bytes,
-// which the workgroup then stores with consecutive lanes along each output
-// row, so every output row gets one whole 128-byte line per workgroup.
-constexpr int kColsK = 256, kColsN = 128;
+// A workgroup takes 256 source rows (k) x 16 PW source columns (n). Lane
+// (wave w, g = lane / 2, h = lane % 2) owns the 16 x PW patch at
+// k = 64 w + 32 (g / 16) + 16 h, n = PW (g % 16): sixteen row loads of PW
+// values. Its PW 16-value blocks (one per source column) land in an LDS
+// image of the workgroup's output, 16 PW rows of 128 code bytes plus their
+// scale bytes, which the workgroup then stores with consecutive lanes along
+// each output row, so every output row gets one whole 128-byte line per
+// workgroup. PW = 8 for 16 x 16 tiles, whose tile error adds a lane's 8
+// columns to its horizontal partner's; else PW = 4, which halves the
+// registers a lane holds its patch in and doubles the workgroups.
+constexpr int kColsK = 256;
 constexpr int kColsPitch = kColsK / 2 + 8;  // staged code row, padded (bytes)
 constexpr int kColsScales = kColsK / 16;    // staged scale bytes per row (NVFP4; MXFP4 uses half)
+constexpr int cols_pw(bool b2d) { return b2d ? 8 : 4; }
+constexpr int cols_n(int pw) { return 16 * pw; }  // source columns per workgroup
 
-template <typename TIn>
-struct Patch16x8;
+template <typename TIn, int PW>
+struct Patch16;
 template <>
-struct Patch16x8<uint16_t> {
+struct Patch16<uint16_t, 8> {
   uint4 r[16];
   __device__ __forceinline__ void load(const uint16_t* p, int64_t ld) {
 #pragma unroll
     for (int i = 0; i < 16; i++) r[i] = *reinterpret_cast<const uint4*>(p + i * ld);
+  }
+  // Hides the loaded words from the compiler's view, so that a pass over
+  // the patch converts them anew instead of keeping an earlier pass's fp32
+  // values live (128 registers) across the passes.
+  __device__ __forceinline__ void opaque() {
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      u32x4 v = {r[i].x, r[i].y, r[i].z, r[i].w};
+      asm volatile("" : "+v"(v));
+      r[i] = make_uint4(v.x, v.y, v.z, v.w);
+    }
   }
   __device__ __forceinline__ float get(int i, int j) const {
     const uint32_t w = (j >> 1) == 0 ? r[i].x : (j >> 1) == 1 ? r[i].y : (j >> 1) == 2 ? r[i].z : r[i].w;
@@ -306,7 +323,19 @@ struct Patch16x8<uint16_t> {
   }
 };
 template <>
-struct Patch16x8<float> {
+struct Patch16<uint16_t, 4> {
+  uint2 r[16];
+  __device__ __forceinline__ void load(const uint16_t* p, int64_t ld) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) r[i] = *reinterpret_cast<const uint2*>(p + i * ld);
+  }
+  __device__ __forceinline__ float get(int i, int j) const {
+    const uint32_t w = (j >> 1) == 0 ? r[i].x : r[i].y;
+    return (j & 1) ? bf16_hi(w) : bf16_lo(w);
+  }
+};
+template <>
+struct Patch16<float, 8> {
   float4 r[16][2];
   __device__ __forceinline__ void load(const float* p, int64_t ld) {
 #pragma unroll
@@ -319,13 +348,27 @@ struct Patch16x8<float> {
     const float4& f = r[i][j >> 2];
     return (j & 3) == 0 ? f.x : (j & 3) == 1 ? f.y : (j & 3) == 2 ? f.z : f.w;
   }
+  __device__ __forceinline__ void opaque() {}  // fp32 values are used as loaded
+};
+template <>
+struct Patch16<float, 4> {
+  float4 r[16];
+  __device__ __forceinline__ void load(const float* p, int64_t ld) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) r[i] = *reinterpret_cast<const float4*>(p + i * ld);
+  }
+  __device__ __forceinline__ float get(int i, int j) const {
+    const float4& f = r[i];
+    return (j & 3) == 0 ? f.x : (j & 3) == 1 ? f.y : (j & 3) == 2 ? f.z : f.w;
+  }
 };
 
 template <typename TIn, bool NV, int SEL, bool B2D, bool SR, bool RHT>
 __global__ __launch_bounds__(256) void quant_cols_kernel(QuantArgs a) {
+  constexpr int PW = cols_pw(B2D), kColsN = cols_n(PW);
   __shared__ __attribute__((aligned(16))) uint8_t cst[kColsN * kColsPitch];
   __shared__ __attribute__((aligned(16))) uint8_t sst[kColsN * kColsScales];
-  // Workgroup order: a column strip (batch item, 128 source columns) is
+  // Workgroup order: a column strip (batch item, kColsN source columns) is
   // walked down K by consecutive workgroups of one XCD (workgroup ids go
   // round-robin to the 8 XCDs, each with its own L2). An output row's 128-byte
   // segments straddle cache lines whenever its pitch is not a multiple of 128;
@@ -338,7 +381,7 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(QuantArgs a) {
   const int64_t b = strip / ncb;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane & 1, g = lane >> 1;
-  const int nl = (g & 15) * 8;                         // patch columns, workgroup-relative
+  const int nl = (g & 15) * PW;                        // patch columns, workgroup-relative
   const int kl = wave * 64 + (g >> 4) * 32 + h * 16;   // patch rows, workgroup-relative
   const int64_t nb = (strip - b * ncb) * kColsN, kb = (i_x % nkb) * kColsK;
   const int64_t n0 = nb + nl, k0 = kb + kl;
@@ -346,7 +389,7 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(QuantArgs a) {
   // tile) are valid together: rows come in whole blocks, columns in whole
   // tiles.
   const bool valid = n0 < a.src_cols && k0 < a.src_rows;
-  Patch16x8<TIn> t;
+  Patch16<TIn, PW> t;
   if (valid) t.load(reinterpret_cast<const TIn*>(a.x) + b * a.bs_x + k0 * a.ld_x + n0, a.ld_x);
   NvConsts nc{};
   if constexpr (NV) nc = nv_prologue<SEL>(a, b, nb == 0 && kb == 0);  // while the loads are in flight
@@ -361,42 +404,56 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(QuantArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; i++)
 #pragma unroll
-        for (int j = 0; j < 8; j++) amax = __builtin_fmaxf(amax, __builtin_fabsf(t.get(i, j)));
+        for (int j = 0; j < PW; j++) amax = __builtin_fmaxf(amax, __builtin_fabsf(t.get(i, j)));
       amax = __builtin_fmaxf(amax, xor_shfl<2>(amax));
       NvCand c = nv_candidate(amax, nc.k6, nc);
       // a candidate's error sum: per source row, the FMA chain over this
       // lane's 8 columns plus the partner's over the other 8, then a
       // pairwise tree over the 16 source rows
+      // (the tree is formed as the row sums arrive: level[d] holds the
+      // pending left operand of depth d, so few sums are live at once)
       auto tile_sum = [&](const NvCand& cc) {
-        float p[16];
+        float level[4];
 #pragma unroll
         for (int i = 0; i < 16; i++) {
           float qq[8];
 #pragma unroll
-          for (int j = 0; j < 8; j++) qq[j] = t.get(i, j) * cc.r;
+          for (int j = 0; j < PW; j++) qq[j] = t.get(i, j) * cc.r;
           uint32_t ww = e2m1_pack2<0>(0u, qq[0], qq[1]);
           ww = e2m1_pack2<1>(ww, qq[2], qq[3]);
           ww = e2m1_pack2<2>(ww, qq[4], qq[5]);
           ww = e2m1_pack2<3>(ww, qq[6], qq[7]);
-          p[i] = sq_chain8(qq, ww);
-          p[i] = p[i] + xor_shfl<2>(p[i]);
+          float x = sq_chain8(qq, ww);
+          x = x + xor_shfl<2>(x);
+          // rows i - 2^d + 1 .. i close a subtree of depth d + 1 when bit d
+          // of i is set: add its left half, held since, on the left
+#pragma unroll
+          for (int d = 0; d < 4; d++) {
+            if (!((i >> d) & 1)) {
+              level[d] = x;
+              break;
+            }
+            x = level[d] + x;
+          }
+          if (i == 15) level[0] = x;
         }
-#pragma unroll
-        for (int width = 1; width < 16; width <<= 1)
-#pragma unroll
-          for (int i = 0; i < 16; i += 2 * width) p[i] = p[i] + p[i + width];
-        return p[0];
+        return level[0];
       };
       if constexpr (SEL == 1) {
         NvCand c4 = nv_candidate(amax, nc.k4, nc);
-        const float s6 = tile_sum(c), s4 = tile_sum(c4);
+        t.opaque();
+        const float s6 = tile_sum(c);
+        t.opaque();
+        const float s4 = tile_sum(c4);
         if (cand_error(c4, s4) < cand_error(c, s6)) c = c4;
       } else if constexpr (SEL == 2) {
         // the lane pair shares amax, hence the loop bounds
+        t.opaque();
         float best = cand_error(c, tile_sum(c));
         const uint32_t hi = nv_candidate(amax, nc.k4, nc).code;
         for (uint32_t code = c.code + 1; code <= hi; code++) {
           const NvCand cc = nv_code_candidate(code, nc);
+          t.opaque();
           const float err = cand_error(cc, tile_sum(cc));
           if (err < best) {
             best = err;
@@ -404,8 +461,9 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(QuantArgs a) {
           }
         }
       }
+      t.opaque();
 #pragma unroll
-      for (int j = 0; j < 8; j++) {
+      for (int j = 0; j < PW; j++) {
         float q[16];
 #pragma unroll
         for (int i = 0; i < 16; i++) q[i] = t.get(i, j) * c.r;
@@ -419,7 +477,7 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(QuantArgs a) {
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; j++) {
+      for (int j = 0; j < PW; j++) {
         float v[16];
 #pragma unroll
         for (int i = 0; i < 16; i++) v[i] = t.get(i, j);
@@ -466,6 +524,7 @@ static void launch_one(const QuantArgs& a, hipStream_t s) {
       return;  // rejected by the API
     } else {
       // 8 XCD lanes of ceil(strips / 8) column strips, each strip nkb workgroups
+      constexpr int kColsN = cols_n(cols_pw(B2D));
       const int64_t strips = a.batch * ((a.src_cols + kColsN - 1) / kColsN);
       const int64_t nkb = (a.src_rows + kColsK - 1) / kColsK;
       dim3 grid((unsigned)(8 * ((strips + 7) / 8) * nkb));
