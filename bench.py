@@ -614,8 +614,8 @@ WORKLOADS = {"rht": wl_rht, "moe": wl_moe, "training": wl_training, "w4a4_linear
              "w4a4_unfused_chain": wl_w4a4_unfused_chain, "scale_search": wl_scale_search}
 # the configurations the default line carries beside the headline step
 EXTRA_WORKLOADS = ("moe", "training", "w4a4_linear")
-# the ones given a CPU baseline in the default line (the two speed targets)
-CPU_WORKLOADS = ("rht", "moe")
+# the ones given a CPU baseline in the default line: every configuration it carries
+CPU_WORKLOADS = ("rht", "moe", "training", "w4a4_linear")
 
 
 # ---------------------------------------------------------------------------
