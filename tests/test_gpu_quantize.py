@@ -92,6 +92,18 @@ def test_amax_prepass_unit_walk(fp4, oracle, shape, flags):
     check(fp4, oracle, x, NV, flags, what="amax-walk")
 
 
+# Transposed quantization takes 64 source columns per workgroup (16 lanes of
+# 4 columns; 128 columns of 8 with 2D tiles): source widths of 8, 24, 200 and
+# 4104 columns leave the last strip holding 8, 24, 8 and 8 columns, with
+# source heights of one MXFP4 block to a ragged K tail.
+@pytest.mark.parametrize("shape", [(64, 8), (96, 24), (288, 200), (32, 4104)], ids=lambda v: "x".join(map(str, v)))
+@pytest.mark.parametrize("fmt,flags", [(MX, TR), (MX, TR | FOS | SR), (NV, TR | FOS), (NV, TR | SR | FOS),
+                                       (NV, TR | SEARCH), (NV, TR | TS), (NV, TR | FOS | RHT)], ids=lambda v: str(v))
+def test_transposed_strip_edges(fp4, oracle, fmt, flags, shape):
+    x = mixed_matrix(*shape, seed=shape[0] + shape[1] + flags)
+    check(fp4, oracle, x, fmt, flags, what="strip-edge")
+
+
 @pytest.mark.parametrize("fmt,flags", [(MX, 0), (NV, FOS), (NV, FOS | RHT), (NV, FOS | TR), (NV, FOS | TR | RHT),
                                        (NV, B2D | FOS)])
 def test_padded_input_pitch(fp4, oracle, fmt, flags):
