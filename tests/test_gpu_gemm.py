@@ -129,9 +129,9 @@ def test_rht_cancels_in_the_product(oracle):
 # full sizes (the benchmark's launch configurations), sampled outputs
 # ---------------------------------------------------------------------------
 def full_case(O, a, b, fmt, fa, fb, signs=0, what=""):
-    """The product at full size, written as bf16 and as fp32 (the north
-    star's 1e-3 relative Frobenius bound applies to the fp32 output, here on
-    48 x 48 sampled outputs of up to three groups)."""
+    """The product at full size, written as bf16 and as fp32 (the 1e-3
+    relative Frobenius bound applies to the fp32 output, here on 48 x 48
+    sampled outputs of up to three groups)."""
     print(f"[gemm-full] {what} A{tuple(a.shape)} B{tuple(b.shape)}", flush=True)
     a3 = a.unsqueeze(0) if a.dim() == 2 else a
     b3 = b.unsqueeze(0) if b.dim() == 2 else b
