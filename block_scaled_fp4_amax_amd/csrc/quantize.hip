@@ -425,8 +425,10 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(QuantArgs a) {
           ww = e2m1_pack2<3>(ww, qq[6], qq[7]);
           float x = sq_chain8(qq, ww);
           x = x + xor_shfl<2>(x);
-          // rows i - 2^d + 1 .. i close a subtree of depth d + 1 when bit d
-          // of i is set: add its left half, held since, on the left
+          // While bit d of i is set, x completes the right half of a subtree
+          // whose left half's sum waits in level[d]: add it on the left and
+          // go up a level. At the first clear bit, x waits there itself. At
+          // i = 15 every bit is set and x is the whole tile's sum.
 #pragma unroll
           for (int d = 0; d < 4; d++) {
             if (!((i >> d) & 1)) {
