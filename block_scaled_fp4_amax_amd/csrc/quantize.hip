@@ -297,6 +297,13 @@ constexpr int kColsScales = kColsK / 16;    // staged scale bytes per row (NVFP4
 constexpr int cols_pw(bool b2d) { return b2d ? 8 : 4; }
 constexpr int cols_n(int pw) { return 16 * pw; }  // source columns per workgroup
 
+// The patch rows are read once and the staged code lines written once, so
+// both go through the caches non-temporally: the streamed input then does
+// not displace the lines that the workgroups of one XCD are still filling.
+__device__ __forceinline__ float4 nt_load_f4(const float* p) {
+  const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
 template <typename TIn, int PW>
 struct Patch16;
 template <>
@@ -304,7 +311,10 @@ struct Patch16<uint16_t, 8> {
   uint4 r[16];
   __device__ __forceinline__ void load(const uint16_t* p, int64_t ld) {
 #pragma unroll
-    for (int i = 0; i < 16; i++) r[i] = *reinterpret_cast<const uint4*>(p + i * ld);
+    for (int i = 0; i < 16; i++) {
+      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + i * ld));
+      r[i] = make_uint4(v.x, v.y, v.z, v.w);
+    }
   }
   // Hides the loaded words from the compiler's view, so that a pass over
   // the patch converts them anew instead of keeping an earlier pass's fp32
@@ -327,7 +337,10 @@ struct Patch16<uint16_t, 4> {
   uint2 r[16];
   __device__ __forceinline__ void load(const uint16_t* p, int64_t ld) {
 #pragma unroll
-    for (int i = 0; i < 16; i++) r[i] = *reinterpret_cast<const uint2*>(p + i * ld);
+    for (int i = 0; i < 16; i++) {
+      const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p + i * ld));
+      r[i] = make_uint2(v.x, v.y);
+    }
   }
   __device__ __forceinline__ float get(int i, int j) const {
     const uint32_t w = (j >> 1) == 0 ? r[i].x : r[i].y;
@@ -340,8 +353,8 @@ struct Patch16<float, 8> {
   __device__ __forceinline__ void load(const float* p, int64_t ld) {
 #pragma unroll
     for (int i = 0; i < 16; i++) {
-      r[i][0] = reinterpret_cast<const float4*>(p + i * ld)[0];
-      r[i][1] = reinterpret_cast<const float4*>(p + i * ld)[1];
+      r[i][0] = nt_load_f4(p + i * ld);
+      r[i][1] = nt_load_f4(p + i * ld + 4);
     }
   }
   __device__ __forceinline__ float get(int i, int j) const {
@@ -355,7 +368,7 @@ struct Patch16<float, 4> {
   float4 r[16];
   __device__ __forceinline__ void load(const float* p, int64_t ld) {
 #pragma unroll
-    for (int i = 0; i < 16; i++) r[i] = *reinterpret_cast<const float4*>(p + i * ld);
+    for (int i = 0; i < 16; i++) r[i] = nt_load_f4(p + i * ld);
   }
   __device__ __forceinline__ float get(int i, int j) const {
     const float4& f = r[i];
@@ -504,7 +517,8 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(QuantArgs a) {
   for (int i = 0; i < (kColsN * kColsK / 2) / (8 * 256); i++) {
     const int c = threadIdx.x + 256 * i, r = c >> 4, cb = (c & 15) * 8;
     if (r < nrows && cb < kbytes)
-      *reinterpret_cast<uint2*>(cout + r * a.ld_c + cb) = *reinterpret_cast<const uint2*>(cst + r * kColsPitch + cb);
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x2*>(cst + r * kColsPitch + cb),
+                                  reinterpret_cast<u32x2*>(cout + r * a.ld_c + cb));
   }
   constexpr int kSPer = NV ? kColsScales : kColsScales / 2;  // scale bytes per row per workgroup
   const int svalid = NV ? kbytes / 8 : kbytes / 16;
