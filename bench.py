@@ -130,8 +130,10 @@ class QuantCall:
         """The quantizer instantiation fp4_quantize launches for this call, by
         the dispatch of csrc/quantize.hip (quant_rows_kernel or, transposed,
         quant_cols_kernel<input, NVFP4, scale selection, 2D, SR, RHT>), after
-        the amax pre-pass when NVFP4 runs without a supplied amax. The label
-        only keys the kernel in profiles."""
+        the amax pre-pass (amax_kernel<input, plain / RHT rows / RHT columns>,
+        then amax_finalize_kernel) when NVFP4 runs without a supplied amax;
+        the kernels of one call are joined by '+'. The label only keys the
+        kernels in profiles."""
         F, f = self.F, self.flags
         b = lambda v: "true" if v else "false"
         if not self.nv:
@@ -147,7 +149,10 @@ class QuantCall:
         tin = "unsigned short" if self.dt == F.FP4_BF16 else "float"
         k = (f"{name}<{tin}, {b(self.nv)}, {sel}, {b(b2d)}, {b(f & F.FP4_STOCHASTIC)}, "
              f"{b(f & F.FP4_HADAMARD)}>")
-        return "amax_kernel+" + k if self.nv and self.amax is None else k
+        if not (self.nv and self.amax is None):
+            return k
+        mode = 0 if not f & F.FP4_HADAMARD else (2 if f & F.FP4_TRANSPOSE else 1)
+        return f"amax_kernel<{tin}, {mode}>+amax_finalize_kernel+{k}"
 
 
 def gemm_kernel_label(nv, G, M, N, K, out_kind, routed=False):
@@ -781,6 +786,12 @@ KERNEL_SOURCES = {  # device sources each kernel family is built from
 }
 
 
+def own_kernel(label):
+    """True for a kernel built from this library's device sources."""
+    return label.split("<")[0] in ("amax_kernel", "amax_finalize_kernel", "quant_rows_kernel", "quant_cols_kernel",
+                                   "gemm_fp4_kernel", "dequant_kernel")
+
+
 def kernel_family(label):
     if label.startswith("gemm"):
         return "gemm"
@@ -811,21 +822,35 @@ def kernel_label(rocprof_name):
     return n.split("::")[-1] if "<" not in n else n[n.rfind("::", 0, n.index("<")) + 2:]
 
 
-def traffic_for(op_kernel, workload):
-    """HBM bytes per launch of one kernel, from the committed rocprofv3
-    counter summary, if it was taken on the current kernel sources; else
-    None (also for ops made of several kernels)."""
-    p = ROOT / "profiles" / "hbm_traffic.json"
-    if not p.exists() or "+" in op_kernel:
+def traffic_for(op_kernel, workload, table=None):
+    """HBM bytes per launch of one op, from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources; else None. An op
+    of several kernels ('a+b+c') sums its kernels' entries. The counters are
+    kept per kernel instantiation, averaged over its dispatches in the
+    workload (ops of different sizes can share one), so a figure is only
+    reported where those dispatches read nearly the same bytes (the spreads
+    of the op's kernels add up to under 5 % of its total): the averages then
+    are this op's own figures. table: the summary's contents (default: read
+    from profiles/hbm_traffic.json)."""
+    t = table
+    if t is None:
+        p = ROOT / "profiles" / "hbm_traffic.json"
+        if not p.exists():
+            return None
+        try:
+            t = json.loads(p.read_text())
+        except ValueError:
+            return None
+    total = spread = 0
+    for k in op_kernel.split("+"):
+        e = t.get("workloads", {}).get(workload, {}).get(k)
+        if not e or e.get("source_digest") != source_digest(k):
+            return None
+        total += e["bytes_per_launch"]
+        spread += e.get("fetch_spread_bytes", total)
+    if spread > 0.05 * total:
         return None
-    try:
-        t = json.loads(p.read_text())
-    except ValueError:
-        return None
-    e = t.get("workloads", {}).get(workload, {}).get(op_kernel)
-    if not e or e.get("source_digest") != source_digest(op_kernel):
-        return None
-    return e.get("bytes_per_launch")
+    return total
 
 
 def read_pmc(dirpath, counter):
@@ -865,7 +890,9 @@ def ingest_pmc(base, copy_bytes, commands):
             fb = float(np.mean(fe[k])) * 1024.0 * f_fetch
             wb = float(np.mean(wr[k])) * 1024.0 * f_write
             ent[k] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "bytes_per_launch": round(fb + wb),
-                      "dispatches": len(fe[k]), "source_digest": source_digest(k) if "<" in k else None}
+                      "dispatches": len(fe[k]),
+                      "fetch_spread_bytes": round((max(fe[k]) - min(fe[k])) * 1024.0 * f_fetch),
+                      "source_digest": source_digest(k) if own_kernel(k) else None}
         out["workloads"][wdir.name] = ent
     dst = ROOT / "profiles" / "hbm_traffic.json"
     dst.parent.mkdir(exist_ok=True)
