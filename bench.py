@@ -885,14 +885,14 @@ def ingest_pmc(base, copy_bytes, commands):
         fe, wr = read_pmc(wdir / "fetch", "FETCH_SIZE"), read_pmc(wdir / "write", "WRITE_SIZE")
         ent = {}
         for k in fe:
-            if k not in wr:
+            if k not in wr or not own_kernel(k):  # this library's kernels only
                 continue
             fb = float(np.mean(fe[k])) * 1024.0 * f_fetch
             wb = float(np.mean(wr[k])) * 1024.0 * f_write
             ent[k] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "bytes_per_launch": round(fb + wb),
                       "dispatches": len(fe[k]),
                       "fetch_spread_bytes": round((max(fe[k]) - min(fe[k])) * 1024.0 * f_fetch),
-                      "source_digest": source_digest(k) if own_kernel(k) else None}
+                      "source_digest": source_digest(k)}
         out["workloads"][wdir.name] = ent
     dst = ROOT / "profiles" / "hbm_traffic.json"
     dst.parent.mkdir(exist_ok=True)
