@@ -183,7 +183,16 @@ __global__ __launch_bounds__(256) void amax_finalize_kernel(QuantArgs a) {
   const int64_t b = blockIdx.x;
   const float* p = a.partials + b * a.nparts;
   float m = 0.0f;
-  for (int i = threadIdx.x; i < a.nparts; i += 256) m = __builtin_fmaxf(m, p[i]);
+  if ((a.nparts & 3) == 0) {
+    // 16-byte loads (the workspace is 16-byte aligned): up to 1024 partials
+    // in one load per lane instead of a chain of dependent ones
+    for (int i = 4 * threadIdx.x; i < a.nparts; i += 4 * 256) {
+      const float4 q = *reinterpret_cast<const float4*>(p + i);
+      m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fmaxf(q.x, q.y), __builtin_fmaxf(q.z, q.w)));
+    }
+  } else {
+    for (int i = threadIdx.x; i < a.nparts; i += 256) m = __builtin_fmaxf(m, p[i]);
+  }
   m = __builtin_fmaxf(m, xor_shfl<32>(m));
   m = __builtin_fmaxf(m, xor_shfl<16>(m));
   m = __builtin_fmaxf(m, xor_shfl<8>(m));
