@@ -98,7 +98,8 @@ __global__ __launch_bounds__(256) void amax_kernel(QuantArgs a) {
   // columns: 16 rows x 8 columns (eight slices down the columns)
   const int64_t per_row = MODE == kAmaxRhtRows ? cols / 16 : cols / 8;
   const int64_t unit_rows = MODE == kAmaxRhtCols ? rows / 16 : rows;
-  constexpr int NU = MODE == kAmaxRhtCols ? 1 : (MODE == kAmaxRhtRows ? 4 : (sizeof(TIn) == 2 ? 8 : 4));
+  // (for bf16, 4 units per lane measured faster than 8 and much faster than 16)
+  constexpr int NU = MODE == kAmaxRhtCols ? 1 : 4;
   const int64_t stride = (int64_t)gridDim.x * 256;
   UnitPos pos[NU];
   pos[0].init((int64_t)blockIdx.x * 256 + threadIdx.x, per_row);
