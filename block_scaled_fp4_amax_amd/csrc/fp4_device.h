@@ -113,17 +113,20 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1
 // points per binade, so (a - lo) / (hi - lo) * 2^16 is the mantissa's low 22
 // bits / 2^6; in [0.5, 1) it is the mantissa / 2^7; below 0.5 it is a * 2^17,
 // exact in fp32. Each test is the exact comparison of the definition.
+// For a >= 1 the encoding's bits 22 and up are 2 * (binade + 127) plus the
+// half-binade bit, which is the round-down code + 252; adding
+// 2^22 - 1 - r * 2^6 carries into bit 22 exactly when the low 22 bits exceed
+// r * 2^6, so the sum's bits 22 and up give the rounded code + 252. From
+// a = 6 on that code is 7 or more (at most 260), so a min saturates it.
 __device__ __forceinline__ uint32_t e2m1_sr(float q, uint32_t r16) {
   const uint32_t bits = __builtin_bit_cast(uint32_t, q);
   const uint32_t sign = (bits >> 28) & 8u;
   const uint32_t ab = bits & 0x7fffffffu;
   const uint32_t mant = ab & 0x7fffffu;
-  const uint32_t e = (ab >> 23) - 127u;  // binade (used where a >= 1)
-  const uint32_t c_hi = 2u + 2u * e + (mant >> 22) + ((r16 << 6) < (mant & 0x3fffffu));
+  const uint32_t c_hi = ((ab + (0x3fffffu - (r16 << 6))) >> 22) - 252u;
   const uint32_t c_mid = 1u + ((r16 << 7) < mant);
   const uint32_t c_lo = (float)r16 < __builtin_fabsf(q) * 131072.0f;
-  uint32_t m = ab >= 0x3f800000u ? c_hi : (ab >= 0x3f000000u ? c_mid : c_lo);
-  m = ab >= 0x40c00000u ? 7u : m;
+  const uint32_t m = ab >= 0x3f800000u ? (c_hi < 7u ? c_hi : 7u) : (ab >= 0x3f000000u ? c_mid : c_lo);
   return sign | m;
 }
 
