@@ -198,6 +198,38 @@ def test_edge_values(fp4, oracle, kind):
         check(fp4, oracle, x, fmt, flags, what=kind)
 
 
+def sr_edge_matrix(rows, seed):
+    """fp32 MXFP4 blocks holding 7.5, so that their max lies in [4, 8), the
+    E8M0 scale is 1 and every value reaches the stochastic rounding
+    unscaled: the E2M1 grid
+    points, their fp32 neighbours, the midpoints and their neighbours, values
+    about 0.5, denormals and values past 6 that saturate, in both signs. Each
+    value meets many draws across the rows."""
+    f = np.float32
+    pts = [0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    vals = []
+    for g in pts:
+        g = f(g)
+        vals += [g, np.nextafter(g, f(0)), np.nextafter(g, f(np.inf))]
+    vals += [f(2.0 ** -17), f(3 * 2.0 ** -18), f(1e-30), f(1.4e-45), f(0.49999997), f(6.5), f(7.99), f(0.0)]
+    vals = np.array(vals, dtype=np.float32)
+    rng = np.random.default_rng(seed)
+    x = vals[rng.integers(0, len(vals), size=(rows, 128))]
+    x *= np.where(rng.random((rows, 128)) < 0.5, -1.0, 1.0).astype(np.float32)
+    x[:, ::32] = 7.5  # puts each 32-value block's max in [4, 8)
+    return torch.from_numpy(x)
+
+
+def test_sr_rounding_edges(fp4, oracle):
+    """Stochastic rounding where the round-up decision is closest: every code
+    bit-exact against the oracle, as-is and transposed (the transposed blocks
+    run down the columns, so their max is whatever a column holds: the scale
+    is 1 where that lies in [4, 8), else a power of two)."""
+    x = sr_edge_matrix(512, seed=11)
+    check(fp4, oracle, x, MX, SR, seed=99, offset=3, what="sr-edges")
+    check(fp4, oracle, x, MX, SR | TR, seed=7, offset=0, what="sr-edges-T")
+
+
 def test_empty_is_noop(fp4):
     x = torch.zeros(0, 64, dtype=torch.bfloat16, device="cuda")
     q = fp4.quantize(x, "nvfp4")
